@@ -1,0 +1,221 @@
+"""Throughput of the product-key memory forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload memplus_16m_bf16]
+
+A step is one whole forward (projection, qk-norm, scoring + per-half top-k,
+combine + softmax, weighted EmbeddingBag over the value table, Memory+ gate) over
+one batch of synthetic tokens whose inputs are already resident in HBM.  Prints one
+JSON line with tokens/s, the roofline of the dominant kernel (the value gather,
+HBM-bound) measured with HIP events on the forward's stream, and the oracle's
+throughput on the host cores over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
+FP32_MFMA_PEAK_TFLOPS = 157.3
+METRIC = "PKM fwd tokens/s + value-gather GB/s (% of HBM peak) at 16M keys, 1 MI355X"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gather_memplus_16m_bf16_counters.json")
+GATHER_SRC = os.path.join(ROOT, "sparse_key_value_amd", "csrc", "gather.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gather_bytes(cfg, T):
+    """Algorithmic bytes one gather launch must move: value rows + (idx, w) + y (fp32)."""
+    rows = T * cfg.H * cfg.k * cfg.d_v * cfg.elem_bytes
+    sel = T * cfg.H * cfg.k * 8
+    y = T * cfg.d_v * 4 if cfg.memory_plus else T * cfg.d_v * cfg.elem_bytes
+    return rows, rows + sel + y
+
+
+def flops(cfg, T):
+    proj = 2 * T * cfg.d_model * cfg.H * cfg.d_q
+    score = 2 * T * cfg.H * 2 * cfg.n_sub * cfg.d_h
+    gate = 4 * T * cfg.d_model * cfg.d_v if cfg.memory_plus else 0
+    return proj, score, gate
+
+
+def counter_traffic():
+    """HBM bytes per gather launch from the committed rocprofv3 counter runs, if the kernel is unchanged."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+        sha = hashlib.sha256(open(GATHER_SRC, "rb").read()).hexdigest()
+        if rec.get("gather_source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, cfg, target_s, max_tokens=None):
+    """Time the oracle on the first S tokens of the same workload on the host cores."""
+    import numpy as np
+    import torch
+
+    from oracle import pkm as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max([p["num_threads"] for p in blas] or [1])
+    except Exception:
+        cores = 1
+    # the oracle reads value rows from a host copy of the table (uint16 bf16 bits / float32)
+    table_bytes = cfg.N * cfg.d_v * cfg.elem_bytes
+    avail = 0
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemAvailable:"):
+                avail = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    note = ""
+    if avail > table_bytes + (24 << 30):
+        log(f"copying the {table_bytes / 2**30:.0f} GiB value table to host memory for the oracle")
+        t0 = time.perf_counter()
+        host = np.empty((cfg.N, cfg.d_v), dtype=np.uint16 if cfg.dtype == "bf16" else np.float32)
+        ht = torch.from_numpy(host.view(np.int16) if cfg.dtype == "bf16" else host)
+        dv = wl.values.view(torch.int16) if cfg.dtype == "bf16" else wl.values
+        step = max(1, (1 << 30) // (cfg.d_v * cfg.elem_bytes))
+        for r0 in range(0, cfg.N, step):
+            ht[r0:r0 + step].copy_(dv[r0:r0 + step])
+        log(f"host table ready in {time.perf_counter() - t0:.1f} s")
+        rows_of = O.rows_from_table(host, cfg.dtype)
+    else:
+        from synth import inputs as S
+        note = "; host RAM too small for the table: rows regenerated on the host, inside the timing"
+        rows_of = lambda r: O.to_f64(S.value_rows(wl.seed, r, cfg.d_v, cfg.dtype), cfg.dtype)
+
+    def run(n):
+        inp = {k: (v[:n] if k == "x" else v) for k, v in wl.inp.items()}
+        t0 = time.perf_counter()
+        O.forward(inp, cfg, rows_of)
+        return time.perf_counter() - t0
+
+    run(4)
+    per_tok = run(16) / 16
+    n = int(max(16, min(max_tokens or wl.T, target_s / max(per_tok, 1e-9))))
+    log(f"oracle: {per_tok * 1e3:.1f} ms/token estimated, timing {n} tokens")
+    dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {cfg.name}, float64 NumPy oracle, {dt:.1f} s" + note}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="memplus_16m_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the forward has no multi-GPU path "
+              "in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import CONFIGS
+    from synth import device as SD
+    from tests.gpu_util import Workload
+
+    cfg = CONFIGS[a.workload]
+    T = cfg.T
+    log(f"workload {cfg.name}: T={T}, N={cfg.N}, d_v={cfg.d_v}, {cfg.dtype}; filling the value table")
+    wl = Workload(cfg, seed=a.seed)
+    h = wl.pkm.handle
+    x = wl.dev["x"]
+    out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # streaming-read ceiling over the value table itself (one pass, after a warm pass)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    SD.stream_read(wl.values, sink)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    SD.stream_read(wl.values, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    tbytes = wl.values.numel() * wl.values.element_size()
+    stream_gbps = tbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    log(f"streaming read of the table: {stream_gbps:.0f} GB/s")
+
+    for _ in range(a.warmup):
+        P.pkm_forward(h, x, T, out, stream=stream)
+    P.pkm_enable_stage_timing(h, a.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        P.pkm_forward(h, x, T, out, stream=stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / a.steps * 1e3
+    tok_s = T * a.steps / elapsed
+
+    stages = {n: sum(P.pkm_stage_times(h, n, a.steps)) / a.steps for n in P.STAGES}
+    g_ms = stages["gather"]
+    rows_b, alg_b = gather_bytes(cfg, T)
+    achieved = alg_b / (g_ms * 1e-3) / 1e9
+    proj, score, gate = flops(cfg, T)
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12 if ms > 0 else None
+    peak_t = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(wl, cfg, a.cpu_seconds)
+
+    traffic = counter_traffic()
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs and weights; value table generated on the GPU)",
+        "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
+                   "n_sub": cfg.n_sub, "n_keys": cfg.N, "d_value": cfg.d_v, "k": cfg.k, "qk_norm": cfg.qk_norm,
+                   "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30},
+        "roofline": {"bound": "hbm", "kernel": "gather (weighted EmbeddingBag)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": g_ms},
+        "gather_value_GBps": rows_b / (g_ms * 1e-3) / 1e9,
+        "gather_value_frac_hbm": rows_b / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "stream_read_GBps": stream_gbps,
+        "gather_frac_of_stream_read": achieved / stream_gbps,
+        "stages_ms": stages,
+        "score_TFLOPs": tf(score, stages["score"]),
+        "score_mfma_frac": (tf(score, stages["score"]) or 0) / peak_t,
+        "project_TFLOPs": tf(proj, stages["project"]),
+        "gate_TFLOPs": tf(gate, stages["gate1"] + stages["gate2"]) if gate else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,61 @@
+"""Product-key memory forward for AMD Instinct MI355X (gfx950).
+
+The forward ("Memory Layers at Scale": a product-key memory layer in place of an
+FFN) runs entirely in the HIP kernels of ``libpkm.so`` behind the C ABI of
+``include/pkm.h``; this package only marshals arguments (``_lib``) and manages
+device memory with PyTorch (``ProductKeyMemory``).
+"""
+
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, PKM_BF16, PKM_EHIP, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_F32, PKM_OK, STAGES,
+    PkmError, make_config, pkm_config, pkm_copy_normalized_subkeys, pkm_create, pkm_debug_ptrs, pkm_destroy,
+    pkm_embedding_bag, pkm_enable_stage_timing, pkm_forward, pkm_forward_debug, pkm_last_error, pkm_select,
+    pkm_stage_times, pkm_workspace_size,
+)
+
+
+class ProductKeyMemory:
+    """Owns a handle and its workspace (a torch uint8 tensor on the current device).
+
+    Tensors (torch, on the GPU, row-major, dtype matching ``dtype``):
+      W_q [d_model, H*d_q], subkeys [H, 2, n_sub, d_q/2], values [n_sub^2, d_value],
+      W1 [d_model, d_value] and W2 [d_value, d_model] when ``memory_plus``.
+    ``values`` is borrowed: keep it alive and unchanged while this object is used.
+    """
+
+    def __init__(self, *, d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
+                 W_q, subkeys, values, W1=None, W2=None, norm_eps=1e-6, stream=None):
+        import torch
+
+        self.cfg = make_config(d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
+                               norm_eps)
+        self.ws_bytes = pkm_workspace_size(self.cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=values.device)
+        self._keep = (W_q, subkeys, values, W1, W2)
+        self.handle = pkm_create(self.cfg, W_q, subkeys, values, W1, W2, self.workspace, self.ws_bytes, stream)
+
+    @property
+    def out_width(self) -> int:
+        return self.cfg.d_model if self.cfg.memory_plus else self.cfg.d_value
+
+    def forward(self, x, out=None, idx_out=None, w_out=None, stream=None):
+        import torch
+
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.out_width), dtype=x.dtype, device=x.device)
+        pkm_forward(self.handle, x, T, out, idx_out, w_out, stream)
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            pkm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

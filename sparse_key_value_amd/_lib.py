@@ -1,0 +1,154 @@
+"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h``).
+
+Argument marshalling only: every function has the name of the C entry point it
+calls, takes torch tensors (or raw device addresses as ints, or None for NULL)
+and passes their data pointers and the current HIP stream.  No computation of
+the forward happens in Python.  If the library has not been built this module
+raises at import time; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkm.so")
+
+PKM_OK, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_EHIP = 0, -1, -2, -3, -4
+PKM_F32, PKM_BF16 = 0, 1
+STAGES = ["project", "qnorm", "score", "combine", "gather", "gate1", "gate2", "total"]
+STAGE_ID = {n: i for i, n in enumerate(STAGES)}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_key_value_amd.build` "
+                      "(the product-key memory path has no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class pkm_config(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_query", ctypes.c_int32),
+        ("n_sub", ctypes.c_int32), ("k", ctypes.c_int32), ("d_value", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("memory_plus", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float), ("max_tokens", ctypes.c_int64),
+    ]
+
+
+class pkm_debug_ptrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("qhat", "half_idx", "half_score", "idx", "score", "w", "y")]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_sig = {
+    "pkm_workspace_size": (_sz, [ctypes.POINTER(pkm_config)]),
+    "pkm_create": (ctypes.c_int, [ctypes.POINTER(pkm_config), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "pkm_forward": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "pkm_forward_debug": (ctypes.c_int, [_vp, _vp, _i64, _vp, ctypes.POINTER(pkm_debug_ptrs), _vp]),
+    "pkm_select": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pkm_copy_normalized_subkeys": (ctypes.c_int, [_vp, _vp, _vp]),
+    "pkm_embedding_bag": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp]),
+    "pkm_enable_stage_timing": (ctypes.c_int, [_vp, _i32]),
+    "pkm_stage_times": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_float), _i32]),
+    "pkm_destroy": (ctypes.c_int, [_vp]),
+    "pkm_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+EXPORTED = tuple(_sig)
+
+
+class PkmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where} failed with code {code}: {pkm_last_error()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise PkmError(rc, where)
+    return rc
+
+
+def make_config(d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
+                norm_eps=1e-6) -> pkm_config:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    return pkm_config(int(d_model), int(n_heads), int(d_query), int(n_sub), int(k), int(d_value), int(dt),
+                      int(bool(qk_norm)), int(bool(memory_plus)), float(norm_eps), int(max_tokens))
+
+
+def pkm_last_error() -> str:
+    return _lib.pkm_last_error().decode()
+
+
+def pkm_workspace_size(cfg: pkm_config) -> int:
+    n = _lib.pkm_workspace_size(ctypes.byref(cfg))
+    if n == 0:
+        raise PkmError(PKM_EINVAL, "pkm_workspace_size")
+    return n
+
+
+def pkm_create(cfg: pkm_config, W_q, subkeys, values, W1, W2, workspace, ws_bytes=None, stream=None) -> int:
+    h = ctypes.c_void_p()
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pkm_create(ctypes.byref(cfg), _ptr(W_q), _ptr(subkeys), _ptr(values), _ptr(W1), _ptr(W2),
+                           _ptr(workspace), ws_bytes, _stream(stream), ctypes.byref(h)), "pkm_create")
+    return h.value
+
+
+def pkm_forward(h: int, x, T: int, out, idx_out=None, w_out=None, stream=None) -> None:
+    _check(_lib.pkm_forward(h, _ptr(x), T, _ptr(out), _ptr(idx_out), _ptr(w_out), _stream(stream)), "pkm_forward")
+
+
+def pkm_forward_debug(h: int, x, T: int, out, dbg: dict | None = None, stream=None) -> None:
+    d = pkm_debug_ptrs(*[_ptr((dbg or {}).get(n)) for n, _ in pkm_debug_ptrs._fields_])
+    _check(_lib.pkm_forward_debug(h, _ptr(x), T, _ptr(out), ctypes.byref(d), _stream(stream)), "pkm_forward_debug")
+
+
+def pkm_select(h: int, qhat, T: int, half_idx=None, half_score=None, idx=None, score=None, w=None, stream=None) -> None:
+    _check(_lib.pkm_select(h, _ptr(qhat), T, _ptr(half_idx), _ptr(half_score), _ptr(idx), _ptr(score), _ptr(w),
+                           _stream(stream)), "pkm_select")
+
+
+def pkm_copy_normalized_subkeys(h: int, dst, stream=None) -> None:
+    _check(_lib.pkm_copy_normalized_subkeys(h, _ptr(dst), _stream(stream)), "pkm_copy_normalized_subkeys")
+
+
+def pkm_embedding_bag(table, n_rows: int, dim: int, dtype, idx, w, n_bags: int, bag_size: int, y, stream=None) -> None:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    _check(_lib.pkm_embedding_bag(_ptr(table), n_rows, dim, dt, _ptr(idx), _ptr(w), n_bags, bag_size, _ptr(y),
+                                  _stream(stream)), "pkm_embedding_bag")
+
+
+def pkm_enable_stage_timing(h: int, max_records: int) -> None:
+    _check(_lib.pkm_enable_stage_timing(h, max_records), "pkm_enable_stage_timing")
+
+
+def pkm_stage_times(h: int, stage, n: int) -> list[float]:
+    sid = STAGE_ID.get(stage, stage)
+    buf = (ctypes.c_float * max(1, n))()
+    got = _check(_lib.pkm_stage_times(h, sid, buf, n), "pkm_stage_times")
+    return [buf[i] for i in range(got)]
+
+
+def pkm_destroy(h: int) -> None:
+    _check(_lib.pkm_destroy(h), "pkm_destroy")

@@ -1,0 +1,129 @@
+// Weighted EmbeddingBag gather-reduce over the value table.
+//
+// y[b, :] = sum over j of w[b, j] * table[idx[b, j], :]   ("Memory Layers at Scale"
+// digest, parallel EmbeddingBag: the memory read is an EmbeddingBag and is bound by
+// memory bandwidth, not FLOPs).  In the forward a bag is one token's H*k selected
+// rows with their softmax weights (core idea: weighted sum of the top-k values).
+//
+// Design for gfx950: every lane owns one 16-byte column slice of a row, so one row
+// read by a group of lanes is one fully coalesced burst; a bag's indices and weights
+// are wave-uniform and come through the scalar cache; UNROLL rows are put in flight
+// before any is consumed (the table is far larger than the caches, so the loads are
+// nontemporal); accumulation is fp32 in a fixed order, with no atomics, so results
+// are bitwise reproducible.
+#include "kernels.hpp"
+
+namespace pkm {
+
+template <int EB>
+struct VecTraits;
+template <>
+struct VecTraits<2> {  // bf16: 8 elements per 16 bytes
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void fma(float* acc, u32x4 v, float w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = __builtin_fmaf(w, bf16_lo(v[e]), acc[2 * e]);
+      acc[2 * e + 1] = __builtin_fmaf(w, bf16_hi(v[e]), acc[2 * e + 1]);
+    }
+  }
+};
+template <>
+struct VecTraits<4> {  // fp32: 4 elements per 16 bytes
+  static constexpr int E = 4;
+  __device__ static __forceinline__ void fma(float* acc, u32x4 v, float w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, __uint_as_float(v[e]), acc[e]);
+  }
+};
+
+// Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bag blockIdx.x*BPB+g and
+// the 16-byte column slices [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of its rows.
+template <int EB, int UNROLL, bool UNIFORM>
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, int64_t n_rows,
+                                                     int row_vecs, int tpr, int bags_per_block,
+                                                     const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                     int64_t n_bags, int bag, void* __restrict__ y, int y_f32) {
+  using VT = VecTraits<EB>;
+  constexpr int E = VT::E;
+  int g = threadIdx.x / tpr;
+  if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
+  const int col = blockIdx.y * tpr + (threadIdx.x - g * tpr);  // 16-byte slice index in the row
+  const int64_t b = (int64_t)blockIdx.x * bags_per_block + g;
+  if (g >= bags_per_block || b >= n_bags || col >= row_vecs) return;
+  const int32_t* bi = idx + b * bag;
+  const float* bw = w + b * bag;
+  const size_t row_bytes = (size_t)row_vecs * 16;
+  const uint8_t* base = table + (size_t)col * 16;
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+
+  int j = 0;
+  for (; j + UNROLL <= bag; j += UNROLL) {
+    u32x4 v[UNROLL];
+    float wt[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      int32_t r = bi[j + u];
+      bool ok = (uint64_t)(int64_t)r < (uint64_t)n_rows;
+      wt[u] = ok ? bw[j + u] : 0.f;
+      r = ok ? r : 0;
+      v[u] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)r * row_bytes));
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) VT::fma(acc, v[u], wt[u]);
+  }
+  for (; j < bag; ++j) {
+    int32_t r = bi[j];
+    bool ok = (uint64_t)(int64_t)r < (uint64_t)n_rows;
+    float wt = ok ? bw[j] : 0.f;
+    r = ok ? r : 0;
+    u32x4 v = __builtin_nontemporal_load((const u32x4*)(base + (size_t)r * row_bytes));
+    VT::fma(acc, v, wt);
+  }
+
+  const int64_t dim = (int64_t)row_vecs * E;
+  const int64_t o = b * dim + (int64_t)col * E;
+  if (y_f32) {
+    float* yo = (float*)y + o;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) *(f32x4*)(yo + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  } else if (EB == 2) {
+    uint16_t* yo = (uint16_t*)y + o;
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pk[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
+    *(u32x4*)yo = pk;
+  } else {
+    float* yo = (float*)y + o;
+    *(f32x4*)yo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  }
+}
+
+hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
+                         const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s) {
+  if (n_bags == 0) return hipSuccess;
+  const int eb = dtype == DT_BF16 ? 2 : 4;
+  const int row_vecs = (int)((int64_t)dim * eb / 16);
+  const int tpr = row_vecs < 256 ? row_vecs : 256;
+  const int bpb = 256 / tpr;
+  const int threads = bpb * tpr;
+  dim3 grid((unsigned)((n_bags + bpb - 1) / bpb), (unsigned)((row_vecs + tpr - 1) / tpr));
+  const int y_f32 = (!y_dtype_is_table || dtype == DT_F32) ? 1 : 0;
+  const bool uniform = (tpr % 64) == 0;
+#define PKM_GATHER(EBV, UNI)                                                                                  \
+  gather_kernel<EBV, 8, UNI><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, w, \
+                                                       n_bags, bag, y, y_f32)
+  if (eb == 2) {
+    if (uniform) PKM_GATHER(2, true); else PKM_GATHER(2, false);
+  } else {
+    if (uniform) PKM_GATHER(4, true); else PKM_GATHER(4, false);
+  }
+#undef PKM_GATHER
+  return hipGetLastError();
+}
+
+}  // namespace pkm

@@ -1,0 +1,182 @@
+// Dense GEMMs of the forward: the query projection q = x W_q, and the two Memory+
+// products ("Memory Layers at Scale" digest, Memory+ block: out = (y * silu(x W1)) W2),
+// with the gate y * silu(.) fused into the epilogue of x W1.
+//
+// C[M, N] = A[M, K] * Bt[N, K]^T: both operands are K-contiguous (the weights are
+// transposed once at create), fp32 accumulation.
+//  * bf16: matrix cores, v_mfma_f32_32x32x16_bf16.  Block tile 128 x 128 x 64, four
+//    waves in a 2 x 2 arrangement, each wave 64 x 64 (2 x 2 MFMA tiles).  Tiles are
+//    staged through padded LDS rows; the next K-tile is prefetched into registers
+//    while the current one is multiplied.
+//  * fp32: a plain SIMT tile (64 x 64 x 16, 4 x 4 per thread) for the fp32 workloads.
+#include "kernels.hpp"
+
+namespace pkm {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): 144 bytes
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
+                                                        void* __restrict__ C, const float* __restrict__ aux, int64_t M,
+                                                        int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+
+  // global -> register prefetch: each tile is 128 rows x 8 units of 16 bytes; 4 units per thread
+  u32x4 pa[4], pb[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + i * 256;
+      const int r = u >> 3, cu = u & 7;
+      const int kc = k0 + cu * 8;
+      const int64_t gm = m0 + r;
+      const int gn = n0 + r;
+      pa[i] = (gm < M && kc < K) ? *(const u32x4*)(A + gm * K + kc) : u32x4{0, 0, 0, 0};
+      pb[i] = (gn < N && kc < K) ? *(const u32x4*)(Bt + (int64_t)gn * K + kc) : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + i * 256;
+      const int r = u >> 3, cu = u & 7;
+      *(u32x4*)(As + r * LDK + cu * 8) = pa[i];
+      *(u32x4*)(Bs + r * LDK + cu * 8) = pb[i];
+    }
+    __syncthreads();
+    if (k0 + BK < K) fetch(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *(const bf16x8*)(As + (wm * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+        bfr[i] = *(const bf16x8*)(Bs + (wn * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: lane holds column n = .. + lane % 32 and 16 rows of each 32 x 32 tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m >= M) continue;
+        const float v = acc[i][j][r];
+        const int64_t o = m * N + n;
+        if (EPI == EPI_STORE_F32) {
+          ((float*)C)[o] = v;
+        } else if (EPI == EPI_STORE_DT) {
+          ((uint16_t*)C)[o] = f32_to_bf16(v);
+        } else {
+          ((uint16_t*)C)[o] = f32_to_bf16(aux[o] * silu_f32(v));
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ Bt,
+                                                       float* __restrict__ C, const float* __restrict__ aux, int64_t M,
+                                                       int N, int K) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    // 64 rows x 16 k of each operand: 1024 elements, 4 per thread
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * 256;
+      const int r = e >> 4, kc = e & 15;
+      const int64_t gm = m0 + r;
+      const int gn = n0 + r;
+      As[kc][r] = (gm < M && k0 + kc < K) ? A[gm * K + k0 + kc] : 0.f;
+      Bs[kc][r] = (gn < N && k0 + kc < K) ? Bt[(int64_t)gn * K + k0 + kc] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < 16; ++kc) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kc][ty * 4 + i];
+        b[i] = Bs[kc][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const int64_t o = m * N + n;
+      C[o] = EPI == EPI_GATE ? aux[o] * silu_f32(acc[i][j]) : acc[i][j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* A, const void* Bt, void* C, const float* aux, int64_t M, int N, int K, int dtype,
+                       int epi, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (dtype == DT_BF16) {
+    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+    const uint16_t* a = (const uint16_t*)A;
+    const uint16_t* b = (const uint16_t*)Bt;
+    switch (epi) {
+      case EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
+      case EPI_STORE_DT: gemm_bf16_kernel<EPI_STORE_DT><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
+      default: gemm_bf16_kernel<EPI_GATE><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
+    }
+  } else {
+    dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    const float* a = (const float*)A;
+    const float* b = (const float*)Bt;
+    if (epi == EPI_GATE) gemm_f32_kernel<EPI_GATE><<<grid, 256, 0, s>>>(a, b, (float*)C, aux, M, N, K);
+    else gemm_f32_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(a, b, (float*)C, aux, M, N, K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkm

@@ -1,0 +1,79 @@
+// Host-only: validation of a pkm_config and the carving of the workspace.
+// Pure C++ (no HIP calls), so every check runs before the device is touched.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/pkm.h"
+
+namespace pkm {
+
+struct Layout {
+  size_t wqT = 0, khat = 0, w1T = 0, w2T = 0;        // create-time copies
+  size_t q = 0, qhat = 0, hidx = 0, hsc = 0;          // per-forward intermediates
+  size_t idx = 0, sc = 0, w = 0, y = 0, g = 0;
+  size_t total = 0;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Returns an empty string if the config is valid, else the reason.
+inline std::string check_config(const pkm_config* c) {
+  if (!c) return "config is NULL";
+  if (c->dtype != PKM_F32 && c->dtype != PKM_BF16) return "dtype must be PKM_F32 (0) or PKM_BF16 (1)";
+  const int eb = c->dtype == PKM_BF16 ? 2 : 4;
+  const int vec = 16 / eb;  // elements per 16-byte access
+  if (c->d_model <= 0 || c->d_model % vec != 0)
+    return "d_model must be positive and a multiple of " + std::to_string(vec) + " (16-byte rows)";
+  if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
+  if (c->d_query <= 0 || c->d_query % 2 != 0) return "d_query must be positive and even";
+  const int d_h = c->d_query / 2;
+  if (d_h != 64 && d_h != 128 && d_h != 256) return "d_query / 2 must be 64, 128 or 256";
+  if (c->n_sub < 1) return "n_sub must be >= 1";
+  if ((int64_t)c->n_sub * (int64_t)c->n_sub >= ((int64_t)1 << 31)) return "n_sub^2 must be < 2^31 (int32 flat index)";
+  if (c->k < 1 || c->k > 32 || c->k > c->n_sub) return "k must satisfy 1 <= k <= min(n_sub, 32)";
+  if (c->d_value <= 0 || ((int64_t)c->d_value * eb) % 16 != 0)
+    return "d_value * sizeof(dtype) must be a positive multiple of 16";
+  if (c->qk_norm != 0 && c->qk_norm != 1) return "qk_norm must be 0 or 1";
+  if (c->memory_plus != 0 && c->memory_plus != 1) return "memory_plus must be 0 or 1";
+  if (!(c->norm_eps >= 0.0f) || c->norm_eps > 1.0f) return "norm_eps must be in [0, 1]";
+  if (c->max_tokens < 1 || c->max_tokens > ((int64_t)1 << 24)) return "max_tokens must be in [1, 2^24]";
+  return "";
+}
+
+inline Layout make_layout(const pkm_config* c) {
+  Layout L;
+  const size_t eb = c->dtype == PKM_BF16 ? 2 : 4;
+  const size_t H = c->n_heads, dq = c->d_query, dm = c->d_model, dv = c->d_value, n = c->n_sub, k = c->k;
+  const size_t T = (size_t)c->max_tokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.wqT = take(H * dq * dm * eb);
+  L.khat = take(H * 2 * n * (dq / 2) * eb);
+  if (c->memory_plus) {
+    L.w1T = take(dv * dm * eb);
+    L.w2T = take(dm * dv * eb);
+  }
+  L.q = take(T * H * dq * 4);
+  L.qhat = take(T * H * dq * eb);
+  L.hidx = take(T * H * 2 * k * 4);
+  L.hsc = take(T * H * 2 * k * 4);
+  L.idx = take(T * H * k * 4);
+  L.sc = take(T * H * k * 4);
+  L.w = take(T * H * k * 4);
+  if (c->memory_plus) {
+    L.y = take(T * dv * 4);
+    L.g = take(T * dv * eb);
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace pkm

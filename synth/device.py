@@ -1,0 +1,45 @@
+"""ctypes wrapper of ``synth/libpkm_synth.so``: GPU-side input generation and
+bandwidth-reference kernels for tests and benchmarks (not the product path)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkm_synth.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_key_value_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_lib.synth_fill_values.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64, _vp]
+_lib.synth_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
+_lib.synth_copy.argtypes = [_vp, _vp, _i64, _i32, _vp]
+for _f in (_lib.synth_fill_values, _lib.synth_stream_read, _lib.synth_copy):
+    _f.restype = ctypes.c_int
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fill_values(table, seed: int, row0: int = 0, n_rows: int | None = None) -> None:
+    """Fill rows of a [N, d_v] torch tensor (float32 or bfloat16) on the GPU."""
+    import torch
+    dt = 1 if table.dtype == torch.bfloat16 else 0
+    n_rows = table.shape[0] - row0 if n_rows is None else n_rows
+    rc = _lib.synth_fill_values(table.data_ptr(), row0, n_rows, table.shape[1], dt, seed, _stream())
+    if rc:
+        raise RuntimeError(f"synth_fill_values failed: hip error {rc}")
+
+
+def stream_read(buf, sink, grid: int = 2048) -> None:
+    rc = _lib.synth_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), grid, _stream())
+    if rc:
+        raise RuntimeError(f"synth_stream_read failed: hip error {rc}")
+
+
+def copy(dst, src, grid: int = 2048) -> None:
+    rc = _lib.synth_copy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), grid, _stream())
+    if rc:
+        raise RuntimeError(f"synth_copy failed: hip error {rc}")

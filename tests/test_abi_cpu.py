@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: the libraries load, export every declared entry point, and
+reject bad arguments before touching a device (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared(header):
+    txt = open(os.path.join(ROOT, "include", header)).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkm_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def P():
+    import sparse_key_value_amd as P
+    return P
+
+
+def test_library_exports_every_declared_symbol(P):
+    lib = ctypes.CDLL(P.LIB_PATH)
+    names = _declared("pkm.h")
+    assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/pkm.h but not exported"
+    assert set(names) == set(P.EXPORTED), "binding and header disagree"
+
+
+def test_synth_library_exports():
+    from synth import device as SD
+    for n in ("synth_fill_values", "synth_stream_read", "synth_copy"):
+        assert hasattr(SD._lib, n)
+
+
+def _cfg(P, **kw):
+    base = dict(d_model=2048, n_heads=4, d_query=512, n_sub=4096, k=32, d_value=2048, dtype="bf16", qk_norm=1,
+                memory_plus=1, max_tokens=16384)
+    base.update(kw)
+    return P.make_config(**base)
+
+
+def test_workspace_size_matches_layout(P):
+    c = _cfg(P)
+    a = lambda v: (v + 255) // 256 * 256
+    T, H, dq, dm, dv, n, k = 16384, 4, 512, 2048, 2048, 4096, 32
+    want = (a(H * dq * dm * 2) + a(H * 2 * n * dq // 2 * 2) + a(dv * dm * 2) + a(dm * dv * 2) + a(T * H * dq * 4) +
+            a(T * H * dq * 2) + 2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 4) + a(T * dv * 2))
+    assert P.pkm_workspace_size(c) == want
+    # without the gate there is no W1/W2 copy and no y/g buffer
+    assert P.pkm_workspace_size(_cfg(P, memory_plus=0)) < want
+
+
+@pytest.mark.parametrize("bad,needle", [
+    (dict(dtype=7), "dtype"),
+    (dict(d_model=0), "d_model"),
+    (dict(d_model=1020), "d_model"),
+    (dict(n_heads=0), "n_heads"),
+    (dict(d_query=511), "d_query"),
+    (dict(d_query=96), "d_query / 2"),
+    (dict(n_sub=0), "n_sub"),
+    (dict(n_sub=46341), "2^31"),
+    (dict(k=0), "k must"),
+    (dict(k=33), "k must"),
+    (dict(k=9, n_sub=8), "k must"),
+    (dict(d_value=12), "d_value"),
+    (dict(qk_norm=2), "qk_norm"),
+    (dict(max_tokens=0), "max_tokens"),
+])
+def test_invalid_configs_are_rejected(P, bad, needle):
+    c = _cfg(P)
+    for key, v in bad.items():
+        setattr(c, key, v)
+    with pytest.raises(P.PkmError) as e:
+        P.pkm_workspace_size(c)
+    assert needle in str(e.value)
+    rc = P._lib._lib.pkm_create(ctypes.byref(c), 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 40, None,
+                                ctypes.byref(ctypes.c_void_p()))
+    assert rc == P.PKM_EINVAL and needle in P.pkm_last_error()
+
+
+def test_create_argument_errors_before_any_device_call(P):
+    c = _cfg(P)
+    lib = P._lib._lib
+    h = ctypes.c_void_p()
+    assert lib.pkm_create(ctypes.byref(c), None, 256, 256, 256, 256, 256, 1 << 40, None, ctypes.byref(h)) == P.PKM_EINVAL
+    assert lib.pkm_create(ctypes.byref(c), 256, 256, 256, None, 256, 256, 1 << 40, None, ctypes.byref(h)) == P.PKM_EINVAL
+    assert "W1 and W2" in P.pkm_last_error()
+    assert lib.pkm_create(ctypes.byref(c), 256, 256, 8, 256, 256, 256, 1 << 40, None, ctypes.byref(h)) == P.PKM_EINVAL
+    assert "16-byte" in P.pkm_last_error()
+    assert lib.pkm_create(ctypes.byref(c), 256, 256, 256, 256, 256, 256, 1024, None, ctypes.byref(h)) == P.PKM_EWORKSPACE
+    assert lib.pkm_create(ctypes.byref(c), 256, 256, 256, 256, 256, 256, 1 << 40, None, None) == P.PKM_EINVAL
+
+
+def test_other_entry_points_reject_bad_arguments(P):
+    lib = P._lib._lib
+    assert lib.pkm_forward(None, 256, 4, 256, None, None, None) == P.PKM_EINVAL
+    assert lib.pkm_forward_debug(None, 256, 4, 256, None, None) == P.PKM_EINVAL
+    assert lib.pkm_select(None, 256, 4, None, None, None, None, None, None) == P.PKM_EINVAL
+    assert lib.pkm_destroy(None) == P.PKM_EINVAL
+    assert lib.pkm_enable_stage_timing(None, 4) == P.PKM_EINVAL
+    assert lib.pkm_copy_normalized_subkeys(None, 256, None) == P.PKM_EINVAL
+    eb = lib.pkm_embedding_bag
+    assert eb(256, 10, 12, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL   # 12 bf16 = 24 bytes per row
+    assert eb(256, 10, 16, 3, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL   # bad dtype
+    assert eb(256, 0, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL    # no rows
+    assert eb(256, 10, 16, 1, 256, 256, 4, 0, 256, None) == P.PKM_EINVAL   # empty bags
+    assert eb(None, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL  # NULL table
+    assert eb(8, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL     # misaligned table
+    assert eb(None, 10, 16, 1, None, None, 0, 4, None, None) == P.PKM_OK   # zero bags: nothing to do

@@ -1,0 +1,323 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI (needs an MI355X).
+
+Small workloads are compared element by element over every token; the full-size
+workloads (16M and 64M keys) run exactly as the benchmark does and are compared on
+sampled tokens, which the oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import gc
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from oracle import pkm as O  # noqa: E402
+from synth import CONFIGS  # noqa: E402
+from synth import inputs as S  # noqa: E402
+from tests import parity as PAR  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _G():
+    from tests import gpu_util
+    return gpu_util
+
+
+def _oracle_inputs(wl, rows=None):
+    """float64 oracle views of the stored inputs (optionally a subset of tokens)."""
+    cfg, dt = wl.cfg, wl.cfg.dtype
+    x = O.to_f64(wl.inp["x"] if rows is None else wl.inp["x"][rows], dt)
+    return x, O.to_f64(wl.inp["W_q"], dt), O.to_f64(wl.inp["subkeys"], dt)
+
+
+def check_order_valid(idx, score, what):
+    """Each GPU list is sorted by score desc, and by index asc among exactly equal scores."""
+    s = score.reshape(-1, score.shape[-1]).astype(np.float64)
+    i = idx.reshape(s.shape).astype(np.int64)
+    assert (np.diff(s, axis=1) <= 0).all(), f"{what}: scores not non-increasing"
+    eq = np.diff(s, axis=1) == 0
+    assert (np.diff(i, axis=1)[eq] > 0).all(), f"{what}: equal scores not in ascending index order"
+
+
+def full_check(wl, o, rows=None, strict_e2e=None):
+    """Stage-wise and end-to-end parity of one debug forward `o` (numpy dict) for token subset `rows`."""
+    cfg, dt = wl.cfg, wl.cfg.dtype
+    G = _G()
+    tok = np.arange(wl.T) if rows is None else np.asarray(rows)
+    x, Wq, K = _oracle_inputs(wl, tok)
+    # a1-a2: normalised query (GPU within one storage ulp of the oracle's)
+    q1o, q2o = O.normalized_query(x, Wq, cfg.H, cfg.d_q, cfg.qk_norm, cfg.norm_eps, dt)
+    qg = o["qhat"][tok]
+    khat_dev = torch.empty((cfg.H, 2, cfg.n_sub, cfg.d_h), dtype=G.TORCH_DT[dt], device="cuda")
+    import sparse_key_value_amd as P
+    P.pkm_copy_normalized_subkeys(wl.pkm.handle, khat_dev)
+    torch.cuda.synchronize()
+    kg = G.to_host(khat_dev)
+    K1o, K2o = O.normalized_subkeys(K, cfg.qk_norm, cfg.norm_eps, dt)
+    if dt == "bf16":
+        # unrounded float64 references: the oracle's q-hat before its own bf16 rounding
+        qn = O.project_query(x, Wq, cfg.H, cfg.d_q)
+        qn = O.rmsnorm(qn, cfg.norm_eps) if cfg.qk_norm else qn
+        PAR.check_bf16_rounded(qg, qn.reshape(qg.shape), 2e-5, "qhat")
+        Kn = O.rmsnorm(K, cfg.norm_eps) if cfg.qk_norm else K
+        PAR.check_bf16_rounded(kg, Kn, 1e-6, "normalised sub-keys")
+    else:
+        qo = np.concatenate([q1o, q2o], axis=-1).reshape(qg.shape)
+        np.testing.assert_allclose(qg, qo, rtol=2e-5, atol=2e-6)
+        np.testing.assert_allclose(kg, np.stack([K1o, K2o], axis=1), rtol=2e-5, atol=2e-6)
+
+    # a3-a6 stage-wise: the oracle selects from the GPU's own qhat and khat bytes
+    qgf = O.to_f64(qg, dt).reshape(len(tok), cfg.H, cfg.d_q)
+    q1g, q2g = qgf[..., :cfg.d_h], qgf[..., cfg.d_h:]
+    kgf = O.to_f64(kg, dt)
+    K1g, K2g = kgf[:, 0], kgf[:, 1]
+    sel = O.select(q1g, q2g, K1g, K2g, cfg.k)
+    hidx, hsc = o["half_idx"][tok], o["half_score"][tok]
+    check_order_valid(hidx, hsc, "per-half lists")
+    ex_h = PAR.check_lists(hidx, sel["half_idx"], sel["half_score"],
+                           PAR.half_choice_scores(q1g, q2g, K1g, K2g, hidx), "per-half top-k")
+    gidx, gsc, gw = o["idx"][tok], o["score"][tok], o["w"][tok]
+    check_order_valid(gidx, gsc, "final lists")
+    ex_f = PAR.check_lists(gidx, sel["idx"], sel["score"], PAR.cell_choice_scores(q1g, q2g, K1g, K2g, gidx),
+                           "final top-k")
+    np.testing.assert_allclose(gw.sum(axis=-1), 1.0, atol=1e-5)
+    assert (gw > 0).all() and (np.diff(gw, axis=-1) <= 1e-7).all()
+    # GPU weights vs softmax of the GPU's own scores (float64)
+    np.testing.assert_allclose(gw, O.softmax(gsc.astype(np.float64)), rtol=2e-6, atol=1e-7)
+
+    # a7 stage-wise: oracle gather of the GPU's indices and weights
+    rows_of = lambda r: O.to_f64(wl.host_rows(r), dt)
+    y_st = O.weighted_bag(rows_of, gidx.astype(np.int64), gw.astype(np.float64))
+    PAR.check_rows(o["y"][tok], y_st, 1e-4, "gather (stage)")
+
+    # a8 stage-wise: gate from the GPU's y
+    if cfg.memory_plus:
+        out_st = O.memory_plus(o["y"][tok].astype(np.float64), x, O.to_f64(wl.inp["W1"], dt),
+                               O.to_f64(wl.inp["W2"], dt), dt)
+        PAR.check_rows(O.to_f64(o["out"][tok], dt), out_st, PAR.TOL[dt], "Memory+ gate (stage)")
+
+    # end to end from x: the oracle's own q, khat; indices under the near-tie rule, outputs re-evaluated
+    ora = O.select(q1o, q2o, K1o, K2o, cfg.k)
+    tau_scale = 1.0 if dt == "f32" else 100.0   # bf16: qhat may round the other way (about 4e-3 in a score)
+    old = PAR.TAU
+    PAR.TAU = old * tau_scale
+    try:
+        ex_e = PAR.check_lists(gidx, ora["idx"], ora["score"], PAR.cell_choice_scores(q1o, q2o, K1o, K2o, gidx),
+                               "end-to-end top-k")
+    finally:
+        PAR.TAU = old
+    y_ref, _ = PAR.reference_on_gpu_choice(q1o, q2o, K1o, K2o, gidx, rows_of)
+    out_ref = (O.memory_plus(y_ref, x, O.to_f64(wl.inp["W1"], dt), O.to_f64(wl.inp["W2"], dt), dt)
+               if cfg.memory_plus else y_ref)
+    rel = PAR.check_rows(O.to_f64(o["out"][tok], dt), out_ref, PAR.TOL[dt], "output (end to end)")
+    say(f"{cfg.name}: tokens {len(tok)}, excused per-half {ex_h}, final {ex_f}, end-to-end {ex_e}, "
+        f"worst out rel err {rel:.2e}")
+    return ex_e
+
+
+def run_debug(wl):
+    o = wl.forward_debug()
+    return {k: _G().to_host(v) for k, v in o.items()}
+
+
+# ----------------------------------------------------------------------------------
+
+
+def test_device_value_generator_is_bit_identical_to_host():
+    G = _G()
+    from synth import device as SD
+    for dt, d_v in (("bf16", 1024), ("f32", 256), ("bf16", 136)):
+        say(f"value generator {dt} d_v={d_v}")
+        t = torch.empty((4096, d_v), dtype=G.TORCH_DT[dt], device="cuda")
+        SD.fill_values(t, seed=11)
+        host = S.value_rows(11, np.arange(4096), d_v, dt)
+        np.testing.assert_array_equal(G.to_host(t), host)
+    # rows far into a 64M-row table (the counter row * d_v + col crosses 2^36): the kernel is given the
+    # address row 0 would have, and writes only rows [row0, row0 + 64), which are exactly the tensor `t`
+    t = torch.empty((64, 1024), dtype=torch.bfloat16, device="cuda")
+    row0 = (1 << 26) - 64
+    rc = SD._lib.synth_fill_values(t.data_ptr() - row0 * 1024 * 2, row0, 64, 1024, 1, 0,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.to_host(t), S.value_rows(0, np.arange(row0, row0 + 64), 1024, "bf16"))
+
+
+@pytest.mark.parametrize("dt,dim,n_rows,n_bags,bag", [
+    ("bf16", 2048, 5000, 37, 128), ("bf16", 1024, 3000, 130, 33), ("f32", 256, 4000, 65, 32),
+    ("bf16", 64, 700, 300, 5), ("f32", 12, 99, 17, 3), ("bf16", 4096, 257, 9, 16),
+])
+def test_embedding_bag_matches_oracle(dt, dim, n_rows, n_bags, bag):
+    import sparse_key_value_amd as P
+    G = _G()
+    say(f"embedding_bag {dt} dim={dim} rows={n_rows} bags={n_bags}x{bag}")
+    rng = np.random.default_rng([dim, n_bags])
+    table = S.value_rows(5, np.arange(n_rows), dim, dt)
+    idx = rng.integers(0, n_rows, (n_bags, bag)).astype(np.int32)
+    idx[0, 0] = idx[0, -1]            # a duplicate in a bag counts twice
+    idx[-1, 0] = -3                   # out-of-range indices contribute nothing
+    idx[-1, -1] = n_rows
+    w = rng.standard_normal((n_bags, bag)).astype(np.float32)
+    y = torch.empty((n_bags, dim), dtype=torch.float32, device="cuda")
+    P.pkm_embedding_bag(G.to_dev(table, dt), n_rows, dim, dt, torch.from_numpy(idx).cuda(),
+                        torch.from_numpy(w).cuda(), n_bags, bag, y)
+    torch.cuda.synchronize()
+    valid = (idx >= 0) & (idx < n_rows)
+    tab = O.to_f64(table, dt)
+    ref = O.weighted_bag(lambda r: tab[r], np.where(valid, idx, 0).astype(np.int64)[:, None, :],
+                         np.where(valid, w, 0.0).astype(np.float64)[:, None, :])
+    PAR.check_rows(G.to_host(y), ref, 1e-5, "embedding bag")
+    # n_bags = 0 is a no-op
+    P.pkm_embedding_bag(G.to_dev(table, dt), n_rows, dim, dt, torch.from_numpy(idx).cuda(),
+                        torch.from_numpy(w).cuda(), 0, bag, y)
+
+
+def test_tiny_fp32_end_to_end_all_tokens():
+    cfg = CONFIGS["tiny_fp32_65k"]
+    say(f"{cfg.name} T={cfg.T}")
+    wl = _G().Workload(cfg)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+
+
+@pytest.mark.parametrize("T", [1, 7, 129, 509])
+def test_tiny_fp32_ragged_token_counts(T):
+    cfg = CONFIGS["tiny_fp32_65k"]
+    say(f"{cfg.name} T={T}")
+    wl = _G().Workload(cfg, T=T, max_tokens=512)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+
+
+def test_pkm_1m_bf16_stagewise_ragged():
+    cfg = CONFIGS["pkm_1m_bf16"]
+    say(f"{cfg.name} T=300")
+    wl = _G().Workload(cfg, T=300)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="figD_n8_k2", n_sub=8, k=2, H=1, d_q=128, d_model=64, d_v=64, T=40),
+    dict(name="n100_k5_h3", n_sub=100, k=5, H=3, d_q=256, d_model=128, d_v=128, T=200),
+    dict(name="k1", n_sub=64, k=1, H=2, d_q=128, d_model=64, d_v=64, T=70),
+    dict(name="d_h128_gate", n_sub=200, k=32, H=2, d_q=256, d_model=256, d_v=128, T=131, memory_plus=True),
+    dict(name="n33_k32", n_sub=33, k=32, H=1, d_q=128, d_model=64, d_v=64, T=64),
+])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_edge_shapes(case, dt):
+    case = dict(case)
+    name = case.pop("name")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"{name}_{dt}", dtype=dt, qk_norm=(dt == "bf16"),
+                                        memory_plus=case.pop("memory_plus", False), **case)
+    say(f"edge {cfg.name}")
+    wl = _G().Workload(cfg, seed=3)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_ties_resolve_to_lowest_index(dt):
+    """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}", dtype=dt, n_sub=96, k=16, H=2, d_q=128, d_model=64,
+                                        d_v=64, T=100, qk_norm=True)
+    inp = S.make_inputs(cfg, seed=4)
+    sk = inp["subkeys"].copy()
+    sk[:, :, 1::2] = sk[:, :, 0::2]      # sub-key 2i+1 duplicates 2i in every codebook
+    inp["subkeys"] = sk
+    x = inp["x"].copy()
+    x[::5] = 0                          # every fifth token is all zero: every score is 0
+    inp["x"] = x
+    say(f"ties {dt}")
+    wl = _G().Workload(cfg, seed=4, host_inputs=inp)
+    o = run_debug(wl)
+    full_check(wl, o)
+    # zero tokens: per-half lists are 0..k-1 and the final list is cells (0, 0..k-1)
+    z = np.arange(0, cfg.T, 5)
+    assert (o["half_idx"][z] == np.arange(cfg.k)).all()
+    assert (o["idx"][z] == np.arange(cfg.k)).all()
+    np.testing.assert_allclose(o["w"][z], 1.0 / cfg.k, rtol=1e-6)
+    # duplicated sub-keys: whenever both of a pair are listed, the even one comes first
+    for lst in (o["half_idx"],):
+        l = lst.reshape(-1, cfg.k)
+        pos = {}
+        for r in range(l.shape[0]):
+            p = {int(v): j for j, v in enumerate(l[r])}
+            for v, j in p.items():
+                if v % 2 == 1 and (v - 1) in p:
+                    assert p[v - 1] < j
+    wl.close()
+
+
+def test_forward_is_deterministic_and_matches_plain_forward():
+    import sparse_key_value_amd as P
+    cfg = CONFIGS["pkm_1m_bf16"].with_(n_sub=256, T=257, d_v=256)
+    say("determinism")
+    wl = _G().Workload(cfg, seed=8)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((wl.T, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda")
+        P.pkm_forward(wl.pkm.handle, wl.dev["x"], wl.T, out, idx, w)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()))
+    dbg = run_debug(wl)
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(outs[0][1], dbg["idx"])
+    np.testing.assert_array_equal(outs[0][2], dbg["w"])
+    np.testing.assert_array_equal(outs[0][0], dbg["out"].view(np.int16))
+    # T = 0 enqueues nothing and succeeds
+    P.pkm_forward(wl.pkm.handle, wl.dev["x"], 0, out)
+    with pytest.raises(P.PkmError):
+        P.pkm_forward(wl.pkm.handle, wl.dev["x"], wl.T + 1, out)
+    wl.close()
+
+
+def _sample_rows(T, n=40, seed=1):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, n, replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["memplus_16m_bf16", "memplus_64m_bf16"])
+def test_full_size_sampled_tokens(name):
+    """The headline and the largest workload at full size, as the benchmark runs them."""
+    cfg = CONFIGS[name]
+    say(f"{name}: filling {cfg.N} x {cfg.d_v} value table on the GPU")
+    wl = _G().Workload(cfg)
+    say(f"{name}: forward T={cfg.T}")
+    o = run_debug(wl)
+    # properties over every token
+    assert (o["idx"] >= 0).all() and (o["idx"] < cfg.N).all()
+    np.testing.assert_allclose(o["w"].sum(axis=-1), 1.0, atol=1e-5)
+    check_order_valid(o["idx"], o["score"], "final lists (all tokens)")
+    rows = _sample_rows(cfg.T)
+    say(f"{name}: oracle on {len(rows)} sampled tokens")
+    full_check(wl, o, rows=rows)
+    wl.close()
+    del wl, o
+    gc.collect()
+    torch.cuda.empty_cache()
