@@ -11,17 +11,22 @@
 //    cores: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32).  The MFMA
 //    computes S^T = Khat * Qhat^T, so each lane's 16 accumulators belong to ONE token
 //    (column = lane % 32) and 16 sub-keys; the selection threshold is one register.
-//  * A block is 4 waves x 32 tokens for one (h, c); chunks of 64 sub-keys are staged
-//    through LDS once and shared by the 4 waves, the next chunk being prefetched into
-//    registers while the current one is scored.
-//  * The scores are never written out.  Each token keeps, in LDS, its current top-k
-//    plus a pending list (capacity 64 keys).  A score enters the pending list only if
-//    its key beats the token's current k-th best key.  When a tile could overflow the
-//    list, the token's keys are sorted across the wave (bitonic, one key per lane) and
-//    cut back to k, which raises the threshold.  After the first few chunks almost
-//    every score is rejected by one compare.
-//  * Keys are 64-bit (ordered score << 32 | ~index), so ties resolve to the lower
-//    index with no extra compare and every key is distinct.
+//  * A block is 4 waves x 32 tokens for one (h, c).  Chunks of 32 sub-keys are staged
+//    through LDS (XOR-swizzled 16-byte units, so the MFMA operand reads are free of
+//    bank conflicts without padding) and shared by the 4 waves; the next chunk is
+//    prefetched into registers while the current one is scored.  80 KiB of LDS per
+//    block lets two blocks share a CU, so one block's selection work overlaps the
+//    other's matrix work.
+//  * The scores are never written out.  Each token owns 64 LDS slots of 64-bit keys:
+//    its current top-k (sorted, slots 0..31) and a pending list (slots 32..63).  A
+//    score is pending only if it beats the token's current k-th best score (one fp32
+//    compare: every earlier sub-key has a lower index, so a tie never enters).  When a
+//    tile could overflow the pending list, the token's 64 slots are merged by the whole
+//    wave: each lane ranks its key against all 64 (v_readlane + one 64-bit compare per
+//    key, no dependent shuffle chain) and ds_permute moves every key to the lane of
+//    its rank, which leaves the new top-k sorted in lanes 0..31.
+//  * Keys are 64-bit (ordered score << 32 | ~index): ties resolve to the lower index
+//    and every key is distinct.  Empty slots carry their lane number, below any key.
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
 //    dealt round-robin to the 8 XCDs, so with 2H dividing 8 each XCD only ever reads
 //    one pair's sub-keys, which stay resident in that XCD's L2.
@@ -34,8 +39,9 @@ namespace {
 constexpr int TPW = 32;         // tokens per wave
 constexpr int NWAVES = 4;
 constexpr int TPB = TPW * NWAVES;
-constexpr int CHUNK = 64;       // sub-keys per LDS chunk (two 32-row MFMA tiles)
-constexpr int CAP = 64;         // keys per token in the LDS candidate list
+constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
+constexpr int SLOTS = 64;       // keys per token: 32 list + 32 pending
+constexpr int LIST = 32;
 
 template <typename DT, int DH>
 struct Mma;
@@ -50,8 +56,9 @@ struct Mma<uint16_t, DH> {
   __device__ static frag load_q(const uint16_t* q, int kk, int hi) {
     return *(const bf16x8*)(q + kk * KSTEP + hi * 8);
   }
-  __device__ static frag lds_k(const uint8_t* row, int kk, int hi) {
-    return *(const bf16x8*)(row + (kk * KSTEP + hi * 8) * EB);
+  // operand of k-step kk for this lane: 16-byte unit 2*kk + hi of the lane's row
+  __device__ static frag lds_k(const uint8_t* row, int swz, int kk, int hi) {
+    return *(const bf16x8*)(row + (((2 * kk + hi) ^ swz) << 4));
   }
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
 };
@@ -64,82 +71,125 @@ struct Mma<float, DH> {
   static constexpr int EB = 4;
   typedef float frag;
   __device__ static frag load_q(const float* q, int kk, int hi) { return q[kk * KSTEP + hi]; }
-  __device__ static frag lds_k(const uint8_t* row, int kk, int hi) {
-    return *(const float*)(row + (kk * KSTEP + hi) * EB);
+  __device__ static frag lds_k(const uint8_t* row, int swz, int kk, int hi) {
+    const int e = kk * KSTEP + hi;  // element; 4 per 16-byte unit
+    return *(const float*)(row + ((((e >> 2) ^ swz) << 4) | ((e & 3) << 2)));
   }
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
 };
 
-// Sort token jj's list across the wave, keep its best k, and update that token's
-// count and threshold (held by lanes jj and jj + 32).
-__device__ __forceinline__ void merge_token(uint64_t* cand_wave, int jj, int lane, int tok, int k, int& cnt,
-                                            uint64_t& thr) {
+__device__ __forceinline__ uint64_t permute_u64(uint64_t v, int dst_lane) {
+  const int addr = dst_lane << 2;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest float strictly below x (finite x): "s > below(x)" is "s >= x".
+__device__ __forceinline__ float float_below(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) == 0) return __uint_as_float(0x80000001u);
+  return __uint_as_float((b & 0x80000000u) ? b + 1 : b - 1);
+}
+
+// Per-token selection state, held by the two lanes that own the token.
+struct TokState {
+  int nl;      // keys in the sorted list (slots 0..31)
+  int np;      // pending keys (slots 32..)
+  float thr;   // a score must be > thr to be pending
+};
+
+// Merge token jj's list and pending keys with the whole wave, leaving the best
+// min(32, nl + np) keys sorted in slots 0.. .  Each lane ranks its key by comparing it
+// with every real key of the token (LDS broadcast reads, no cross-lane dependency
+// chain); ds_permute then sends every key to the lane of its rank.  Keys are distinct,
+// so the ranks of the real keys are 0 .. nl+np-1.
+__device__ __forceinline__ void merge_token(uint64_t* cand_wave, int jj, int lane, int tok, int k, TokState& st) {
   __builtin_amdgcn_wave_barrier();
-  const int cj = __shfl(cnt, jj, WAVE);
-  uint64_t* b = cand_wave + jj * CAP;
-  uint64_t key = lane < cj ? b[lane] : 0ull;
-  key = wave_sort_desc(key, lane);
-  const uint64_t kth = shfl_u64(key, k - 1);
+  const int nl = __builtin_amdgcn_readlane(st.nl, jj);
+  const int np = __builtin_amdgcn_readlane(st.np, jj);
+  uint64_t* b = cand_wave + jj * SLOTS;
+  const bool real = lane < nl || (lane >= LIST && lane - LIST < np);
+  const uint64_t key = real ? b[lane] : 0ull;
+  int rank = 0;
+  for (int i = 0; i < nl; ++i) rank += b[i] > key ? 1 : 0;
+  for (int i = 0; i < np; ++i) rank += b[LIST + i] > key ? 1 : 0;
+  const uint64_t sorted = permute_u64(key, real ? rank : SLOTS - 1);
+  const int total = nl + np;
   __builtin_amdgcn_wave_barrier();
-  if (lane < k) b[lane] = key;
+  if (lane < LIST && lane < total) b[lane] = sorted;
   __builtin_amdgcn_wave_barrier();
-  const int nc = cj < k ? cj : k;
+  const int nn = total < LIST ? total : LIST;
+  const uint64_t kth = (uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)(sorted >> 32), k - 1) << 32;
   if (tok == jj) {
-    cnt = nc;
-    thr = nc >= k ? kth : 0ull;
+    st.nl = nn;
+    st.np = 0;
+    // once k keys are listed, a later sub-key (higher index) must beat the k-th score strictly
+    if (nn >= k) st.thr = score_of_ord((uint32_t)(kth >> 32));
   }
 }
 
-// Offer one 32-sub-key tile of scores (this lane: 16 sub-keys of token `tok`).
+__device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_base + 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Pass 2: offer one 32-sub-key tile (this lane: 16 sub-keys of token `tok`).
 __device__ __forceinline__ void offer_tile(const f32x16& acc, int sub_base, int n, int lane, int tok, int hi, int k,
-                                           uint64_t* cand_wave, int& cnt, uint64_t& thr) {
-  uint64_t key[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int sub = sub_base + 8 * (r >> 2) + 4 * hi + (r & 3);
-    key[r] = sub < n ? make_key(acc[r], (uint32_t)sub) : 0ull;
-  }
+                                           uint64_t* cand_wave, TokState& st) {
   uint32_t m = 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) m |= (key[r] > thr ? 1u : 0u) << r;
+  for (int r = 0; r < 16; ++r) m |= (sub_of(sub_base, r, hi) < n && acc[r] > st.thr ? 1u : 0u) << r;
+  if (__ballot(m != 0) == 0) return;
   int c = __popc(m);
   int co = __shfl_xor(c, 32, WAVE);
-  const bool need = cnt + c + co > CAP;
-  uint64_t bal = __ballot(need) & 0xFFFFFFFFull;
+  uint64_t bal = __ballot(st.np + c + co > SLOTS - LIST) & 0xFFFFFFFFull;
   if (bal) {
     while (bal) {
       const int jj = __builtin_ctzll(bal);
       bal &= bal - 1;
-      merge_token(cand_wave, jj, lane, tok, k, cnt, thr);
+      merge_token(cand_wave, jj, lane, tok, k, st);
     }
     m = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m |= (key[r] > thr ? 1u : 0u) << r;
+    for (int r = 0; r < 16; ++r) m |= (sub_of(sub_base, r, hi) < n && acc[r] > st.thr ? 1u : 0u) << r;
     c = __popc(m);
     co = __shfl_xor(c, 32, WAVE);
   }
-  int off = cnt + (hi ? co : 0);
-  uint64_t* b = cand_wave + tok * CAP;
+  int off = LIST + st.np + (hi ? co : 0);
+  uint64_t* b = cand_wave + tok * SLOTS;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (m & (1u << r)) b[off++] = key[r];
+    if (m & (1u << r)) b[off++] = make_key(acc[r], (uint32_t)sub_of(sub_base, r, hi));
   }
-  cnt += c + co;
+  st.np += c + co;
+}
+
+// k-th largest of the values v0, v1 held by all 64 lanes (ordered-float bits; 0 = absent):
+// the largest x with #{v >= x} >= k, found bit by bit from the top with wave ballots.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v0, uint32_t v1, int k) {
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    const int cnt = __popcll(__ballot(v0 >= cand)) + __popcll(__ballot(v1 >= cand));
+    if (cnt >= k) prefix = cand;
+  }
+  return prefix;
 }
 
 template <typename DT, int DH>
-__global__ void __launch_bounds__(256) score_topk_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
-                                                         int64_t T, int H, int n, int k, int32_t* __restrict__ half_idx,
-                                                         float* __restrict__ half_score) {
+__global__ void __launch_bounds__(256, 2) score_topk_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+                                                            int64_t T, int H, int n, int k,
+                                                            int32_t* __restrict__ half_idx,
+                                                            float* __restrict__ half_score) {
   using M = Mma<DT, DH>;
   constexpr int RB = DH * M::EB;          // bytes per sub-key row
-  constexpr int RS = RB + 16;             // padded LDS row stride
   constexpr int U16 = RB / 16;            // 16-byte units per row
   constexpr int UPT = CHUNK * U16 / 256;  // units per thread per chunk
+  constexpr int MAXG = 128;               // group maxima per token kept by pass 1
   static_assert(UPT >= 1 && CHUNK * U16 % 256 == 0, "chunk must split evenly over 256 threads");
+  static_assert(MAXG * 4 == SLOTS * 8, "pass-1 maxima reuse the candidate slots");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ks[CHUNK * RS];
-  __shared__ uint64_t cand[TPB * CAP];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[CHUNK * RB];
+  __shared__ uint64_t cand[TPB * SLOTS];
 
   const int pairs = 2 * H;
   const int pair = blockIdx.x % pairs;
@@ -172,44 +222,75 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const DT* __restrict__ 
       pre[i] = sub < n ? *(const u32x4*)(kbase + (size_t)sub * RB + col * 16) : u32x4{0, 0, 0, 0};
     }
   };
-  fetch(0);
-
-  uint64_t* cand_wave = cand + wv * TPW * CAP;
-  int cnt = 0;
-  uint64_t thr = 0ull;
-
-  for (int ch = 0; ch < nch; ++ch) {
+  const int swz_r = (lane & 31) % U16;
+  const uint8_t* myrow = ks + (lane & 31) * RB;
+  // stage chunk ch into LDS (the caller has prefetched it into `pre`), prefetch ch + 1, score it
+  auto score_chunk = [&](int ch) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * 256;
       const int row = u / U16, col = u - row * U16;
-      *(u32x4*)(ks + row * RS + col * 16) = pre[i];
+      *(u32x4*)(ks + row * RB + ((col ^ (row % U16)) << 4)) = pre[i];
     }
     __syncthreads();
     if (ch + 1 < nch) fetch(ch + 1);
-
-    f32x16 acc0 = {}, acc1 = {};
-    const uint8_t* r0 = ks + (lane & 31) * RS;
-    const uint8_t* r1 = ks + (32 + (lane & 31)) * RS;
+    f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < M::NK; ++kk) {
-      acc0 = M::mma(M::lds_k(r0, kk, hi), qf[kk], acc0);
-      acc1 = M::mma(M::lds_k(r1, kk, hi), qf[kk], acc1);
+    for (int kk = 0; kk < M::NK; ++kk) acc = M::mma(M::lds_k(myrow, swz_r, kk, hi), qf[kk], acc);
+    return acc;
+  };
+
+  uint64_t* cand_wave = cand + wv * TPW * SLOTS;
+  float* gmax_wave = (float*)cand_wave;  // pass 1: [token][MAXG] group maxima
+
+  // ---- pass 1: the maximum score of each group of sub-keys, per token ------------------
+  // The k-th largest of these maxima is a score that at least k sub-keys reach, so it
+  // bounds the token's k-th best score from below.
+  const int gsz = (nch + MAXG - 1) / MAXG;   // chunks per group
+  const int ngroups = (nch + gsz - 1) / gsz;
+  fetch(0);
+  float gm = -__builtin_inff();
+  for (int ch = 0; ch < nch; ++ch) {
+    const f32x16 acc = score_chunk(ch);
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = sub_of(ch * CHUNK, r, hi) < n ? fmaxf(m, acc[r]) : m;
+    m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+    gm = fmaxf(gm, m);
+    if ((ch + 1) % gsz == 0 || ch + 1 == nch) {
+      if (hi == 0) gmax_wave[tok * MAXG + ch / gsz] = gm;
+      gm = -__builtin_inff();
     }
-    offer_tile(acc0, ch * CHUNK, n, lane, tok, hi, k, cand_wave, cnt, thr);
-    offer_tile(acc1, ch * CHUNK + 32, n, lane, tok, hi, k, cand_wave, cnt, thr);
+  }
+  __builtin_amdgcn_wave_barrier();
+  TokState st;
+  st.nl = 0;
+  st.np = 0;
+  st.thr = -__builtin_inff();
+  if (ngroups >= k) {
+    for (int jj = 0; jj < TPW; ++jj) {
+      const uint32_t v0 = lane < ngroups ? ord_score(gmax_wave[jj * MAXG + lane]) : 0u;
+      const uint32_t v1 = lane + 64 < ngroups ? ord_score(gmax_wave[jj * MAXG + lane + 64]) : 0u;
+      const uint32_t kth = wave_kth_largest(v0, v1, k);
+      if (tok == jj) st.thr = float_below(score_of_ord(kth));
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- pass 2: collect the sub-keys at or above the bound, keep the exact top-k -------
+  fetch(0);
+  for (int ch = 0; ch < nch; ++ch) {
+    const f32x16 acc = score_chunk(ch);
+    offer_tile(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
   }
 
-  // final sort of every token of this wave, then write its top-k
+  // final merge of every token of this wave, then write its top-k
   for (int jj = 0; jj < TPW; ++jj) {
-    const int cj = __shfl(cnt, jj, WAVE);
-    uint64_t* b = cand_wave + jj * CAP;
-    __builtin_amdgcn_wave_barrier();
-    uint64_t key = lane < cj ? b[lane] : 0ull;
-    key = wave_sort_desc(key, lane);
+    merge_token(cand_wave, jj, lane, tok, k, st);
     const int64_t tj = tile * TPB + wv * TPW + jj;
     if (tj < T && lane < k) {
+      const uint64_t key = cand_wave[jj * SLOTS + lane];
       const int64_t o = ((tj * H + h) * 2 + c) * (int64_t)k + lane;
       half_idx[o] = (int32_t)key_index(key);
       half_score[o] = key_score(key);
