@@ -4,21 +4,63 @@
 // second; its score is s_0[a] + s_1[b] and its flat index a * n_sub + b ("Memory inside
 // the model" overview, how it works: the best of the two half lists are combined,
 // which finds the right cell among all n_sub x n_sub).  The final top-k is taken under
-// (score desc, flat index asc) and its scores are turned into weights by a softmax
-// (digest, core idea: weighted sum of the top-k values; overview: weighted average of
-// about thirty values).
+// (score desc, flat index asc) over all k*k pairs of list positions, and its scores
+// are turned into weights by a softmax (digest, core idea: weighted sum of the top-k
+// values; overview: weighted average of about thirty values).  The sum is an fp32 add
+// of the two fp32 half scores.
 //
-// One wave per (token, head): each lane forms up to 16 of the k*k <= 1024 candidate
-// keys; k rounds of a wave-wide max pull the winners out in order.  The sum is an fp32
-// add of the two fp32 half scores.
+// One wave per (token, head).  Both lists are sorted, so the pair of positions (i, j)
+// is beaten by every (i', j') with i' <= i, j' <= j; in exact arithmetic only the
+// "staircase" (i + 1)(j + 1) <= k can reach the top-k (119 pairs for k = 32 instead of
+// 1,024).  The staircase is sorted with a bitonic network over two keys per lane.  The
+// fp32 rounding of a sum can merge two distinct sums into a tie that the flat index
+// then breaks the other way, so every one of the k*k pairs is checked against the
+// k-th key found; if any pair off the staircase beats it (a rounding tie, about never
+// with real data) the wave redoes the selection over all k*k pairs.
 #include "kernels.hpp"
 
 namespace pkm {
 
+namespace {
+
+struct Stair {
+  uint16_t pos[128];  // (i << 8) | j for staircase slot s, 0xFFFF = empty
+};
+
+__device__ __forceinline__ uint64_t cell_key(const float* s0, const int32_t* i0, const float* s1, const int32_t* i1,
+                                             int a, int b, int n) {
+  return make_key(s0[a] + s1[b], (uint32_t)i0[a] * (uint32_t)n + (uint32_t)i1[b]);
+}
+
+// Sort 128 keys held two per lane (element e = 2 * lane + slot) in descending order.
+__device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride == 1) {
+        // within the lane: elements 2l and 2l+1; block direction from bit `size` of e = 2l
+        const bool desc = ((2 * lane) & size) == 0;
+        const uint64_t mx = x0 > x1 ? x0 : x1, mn = x0 > x1 ? x1 : x0;
+        x0 = desc ? mx : mn;
+        x1 = desc ? mn : mx;
+      } else {
+        const int lx = stride >> 1;  // partner lane: e ^ stride = 2 * (lane ^ lx) + slot
+        const uint64_t o0 = shfl_xor_u64(x0, lx), o1 = shfl_xor_u64(x1, lx);
+        const bool desc = ((2 * lane) & size) == 0;
+        const bool lower = (lane & lx) == 0;
+        const bool take_max = desc == lower;
+        x0 = take_max ? (x0 > o0 ? x0 : o0) : (x0 > o0 ? o0 : x0);
+        x1 = take_max ? (x1 > o1 ? x1 : o1) : (x1 > o1 ? o1 : x1);
+      }
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ half_idx,
                                                       const float* __restrict__ half_score, int64_t rows, int n,
-                                                      int k, int32_t* __restrict__ idx, float* __restrict__ score,
-                                                      float* __restrict__ w) {
+                                                      int k, Stair st, int32_t* __restrict__ idx,
+                                                      float* __restrict__ score, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row = t * H + h
   if (row >= rows) return;
@@ -27,30 +69,48 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
   const float* s0 = half_score + row * 2 * k;
   const float* s1 = s0 + k;
 
+  // staircase keys, two per lane
+  const uint16_t p0 = st.pos[2 * lane], p1 = st.pos[2 * lane + 1];
+  uint64_t x0 = p0 != 0xFFFF ? cell_key(s0, i0, s1, i1, p0 >> 8, p0 & 0xFF, n) : 0ull;
+  uint64_t x1 = p1 != 0xFFFF ? cell_key(s0, i0, s1, i1, p1 >> 8, p1 & 0xFF, n) : 0ull;
+  sort128_desc(x0, x1, lane);
+  // element e = 2 * lane + slot; the k-th best is element k - 1
+  const uint64_t kth = shfl_u64((k - 1) & 1 ? x1 : x0, (k - 1) >> 1);
+
+  // check every pair: nothing off the staircase may beat the k-th key
   const int kk = k * k;
-  uint64_t key[16];
+  bool beaten = false;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int cidx = lane + 64 * r;
     if (cidx < kk) {
       const int a = cidx / k, b = cidx - a * k;
-      const float sc = s0[a] + s1[b];
-      const uint32_t flat = (uint32_t)i0[a] * (uint32_t)n + (uint32_t)i1[b];
-      key[r] = make_key(sc, flat);
-    } else {
-      key[r] = 0ull;
+      if ((a + 1) * (b + 1) > k && cell_key(s0, i0, s1, i1, a, b, n) > kth) beaten = true;
     }
   }
-
-  uint64_t mine = 0ull;  // lane j < k ends up holding the j-th best key
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0ull;
+  uint64_t mine;  // lane j < k ends up with the j-th best key
+  if (__ballot(beaten) == 0) {
+    // lane j takes element j = 2 * (j >> 1) + (j & 1)
+    const uint64_t a0 = shfl_u64(x0, lane >> 1), a1 = shfl_u64(x1, lane >> 1);
+    mine = (lane & 1) ? a1 : a0;
+  } else {
+    // exhaustive: k rounds of a wave-wide maximum over all k*k keys
+    uint64_t key[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) best = key[r] > best ? key[r] : best;
-    const uint64_t win = wave_max_u64(best);
+    for (int r = 0; r < 16; ++r) {
+      const int cidx = lane + 64 * r;
+      key[r] = cidx < kk ? cell_key(s0, i0, s1, i1, cidx / k, cidx % k, n) : 0ull;
+    }
+    mine = 0ull;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0ull;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) key[r] = key[r] == win ? 0ull : key[r];
-    if (lane == j) mine = win;
+      for (int r = 0; r < 16; ++r) best = key[r] > best ? key[r] : best;
+      const uint64_t win = wave_max_u64(best);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) key[r] = key[r] == win ? 0ull : key[r];
+      if (lane == j) mine = win;
+    }
   }
 
   // softmax over the k winners (max = the first one)
@@ -66,11 +126,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
   }
 }
 
+}  // namespace
+
 hipError_t launch_combine(const int32_t* half_idx, const float* half_score, int64_t T, int H, int n, int k,
                           int32_t* idx, float* score, float* w, hipStream_t s) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
-  combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(half_idx, half_score, rows, n, k, idx, score, w);
+  Stair st;
+  int m = 0;
+  for (int a = 0; a < k; ++a)
+    for (int b = 0; (a + 1) * (b + 1) <= k; ++b) st.pos[m++] = (uint16_t)((a << 8) | b);
+  for (; m < 128; ++m) st.pos[m] = 0xFFFF;
+  combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(half_idx, half_score, rows, n, k, st, idx, score, w);
   return hipGetLastError();
 }
 

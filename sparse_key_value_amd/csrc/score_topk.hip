@@ -17,14 +17,18 @@
 //    prefetched into registers while the current one is scored.  80 KiB of LDS per
 //    block lets two blocks share a CU, so one block's selection work overlaps the
 //    other's matrix work.
-//  * The scores are never written out.  Each token owns 64 LDS slots of 64-bit keys:
-//    its current top-k (sorted, slots 0..31) and a pending list (slots 32..63).  A
-//    score is pending only if it beats the token's current k-th best score (one fp32
-//    compare: every earlier sub-key has a lower index, so a tie never enters).  When a
-//    tile could overflow the pending list, the token's 64 slots are merged by the whole
-//    wave: each lane ranks its key against all 64 (v_readlane + one 64-bit compare per
-//    key, no dependent shuffle chain) and ds_permute moves every key to the lane of
-//    its rank, which leaves the new top-k sorted in lanes 0..31.
+//  * The scores are never written out.  Selection takes two passes over the sub-keys.
+//    Pass 1 keeps, per token, the maximum score of each group of sub-keys (at most 128
+//    groups); the k-th largest of these maxima is reached by at least k sub-keys, so it
+//    bounds the token's k-th best score from below (found bit by bit with wave
+//    ballots).  Pass 2 recomputes the same scores and keeps only those at or above the
+//    bound: with random-like data about 37 of 4,096 per token.
+//  * Each token owns 64 LDS slots of 64-bit keys: pending keys, and after a merge a
+//    sorted list in slots 0..31 with pending keys in 32..63.  After a merge a score
+//    must beat the k-th best score strictly (every later sub-key has a higher index,
+//    so a tie never enters).  A merge is done by the whole wave: each lane ranks its
+//    key by comparing it with every key of the token (LDS broadcast reads, no
+//    dependent shuffle chain) and ds_permute moves every key to the lane of its rank.
 //  * Keys are 64-bit (ordered score << 32 | ~index): ties resolve to the lower index
 //    and every key is distinct.  Empty slots carry their lane number, below any key.
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
@@ -94,9 +98,11 @@ __device__ __forceinline__ float float_below(float x) {
 
 // Per-token selection state, held by the two lanes that own the token.
 struct TokState {
-  int nl;      // keys in the sorted list (slots 0..31)
-  int np;      // pending keys (slots 32..)
+  int nl;      // keys in the sorted list (slots 0..nl-1); 0 until the first merge
+  int np;      // pending keys, from slot pbase(): all 64 slots are pending until a list exists
   float thr;   // a score must be > thr to be pending
+  __device__ int pbase() const { return nl ? LIST : 0; }
+  __device__ int cap() const { return nl ? SLOTS - LIST : SLOTS; }
 };
 
 // Merge token jj's list and pending keys with the whole wave, leaving the best
@@ -108,52 +114,58 @@ __device__ __forceinline__ void merge_token(uint64_t* cand_wave, int jj, int lan
   __builtin_amdgcn_wave_barrier();
   const int nl = __builtin_amdgcn_readlane(st.nl, jj);
   const int np = __builtin_amdgcn_readlane(st.np, jj);
+  const int pb = nl ? LIST : 0;
   uint64_t* b = cand_wave + jj * SLOTS;
-  const bool real = lane < nl || (lane >= LIST && lane - LIST < np);
+  const bool real = lane < nl || (lane >= pb && lane - pb < np);
   const uint64_t key = real ? b[lane] : 0ull;
   int rank = 0;
   for (int i = 0; i < nl; ++i) rank += b[i] > key ? 1 : 0;
-  for (int i = 0; i < np; ++i) rank += b[LIST + i] > key ? 1 : 0;
+  for (int i = 0; i < np; ++i) rank += b[pb + i] > key ? 1 : 0;
   const uint64_t sorted = permute_u64(key, real ? rank : SLOTS - 1);
   const int total = nl + np;
   __builtin_amdgcn_wave_barrier();
   if (lane < LIST && lane < total) b[lane] = sorted;
   __builtin_amdgcn_wave_barrier();
   const int nn = total < LIST ? total : LIST;
-  const uint64_t kth = (uint64_t)__builtin_amdgcn_readlane((int)(uint32_t)(sorted >> 32), k - 1) << 32;
+  const uint32_t kth_ord = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(sorted >> 32), k - 1);
   if (tok == jj) {
     st.nl = nn;
     st.np = 0;
     // once k keys are listed, a later sub-key (higher index) must beat the k-th score strictly
-    if (nn >= k) st.thr = score_of_ord((uint32_t)(kth >> 32));
+    if (nn >= k) st.thr = score_of_ord(kth_ord);
   }
 }
 
 __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_base + 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-// Pass 2: offer one 32-sub-key tile (this lane: 16 sub-keys of token `tok`).
-__device__ __forceinline__ void offer_tile(const f32x16& acc, int sub_base, int n, int lane, int tok, int hi, int k,
-                                           uint64_t* cand_wave, TokState& st) {
+template <bool FULL>
+__device__ __forceinline__ uint32_t survivors(const f32x16& acc, int sub_base, int n, int hi, float thr) {
   uint32_t m = 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) m |= (sub_of(sub_base, r, hi) < n && acc[r] > st.thr ? 1u : 0u) << r;
+  for (int r = 0; r < 16; ++r) m |= ((FULL || sub_of(sub_base, r, hi) < n) && acc[r] > thr ? 1u : 0u) << r;
+  return m;
+}
+
+// Pass 2: offer one 32-sub-key tile (this lane: 16 sub-keys of token `tok`).
+template <bool FULL>
+__device__ __forceinline__ void offer_tile(const f32x16& acc, int sub_base, int n, int lane, int tok, int hi, int k,
+                                           uint64_t* cand_wave, TokState& st) {
+  uint32_t m = survivors<FULL>(acc, sub_base, n, hi, st.thr);
   if (__ballot(m != 0) == 0) return;
   int c = __popc(m);
   int co = __shfl_xor(c, 32, WAVE);
-  uint64_t bal = __ballot(st.np + c + co > SLOTS - LIST) & 0xFFFFFFFFull;
+  uint64_t bal = __ballot(st.np + c + co > st.cap()) & 0xFFFFFFFFull;
   if (bal) {
     while (bal) {
       const int jj = __builtin_ctzll(bal);
       bal &= bal - 1;
       merge_token(cand_wave, jj, lane, tok, k, st);
     }
-    m = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m |= (sub_of(sub_base, r, hi) < n && acc[r] > st.thr ? 1u : 0u) << r;
+    m = survivors<FULL>(acc, sub_base, n, hi, st.thr);
     c = __popc(m);
     co = __shfl_xor(c, 32, WAVE);
   }
-  int off = LIST + st.np + (hi ? co : 0);
+  int off = st.pbase() + st.np + (hi ? co : 0);
   uint64_t* b = cand_wave + tok * SLOTS;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -282,7 +294,8 @@ __global__ void __launch_bounds__(256, 2) score_topk_kernel(const DT* __restrict
   fetch(0);
   for (int ch = 0; ch < nch; ++ch) {
     const f32x16 acc = score_chunk(ch);
-    offer_tile(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
+    if ((ch + 1) * CHUNK <= n) offer_tile<true>(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
+    else offer_tile<false>(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
   }
 
   // final merge of every token of this wave, then write its top-k

@@ -321,3 +321,47 @@ def test_full_size_sampled_tokens(name):
     del wl, o
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_combine_rounding_tie_takes_exhaustive_path():
+    """fp32 sums that round to the same value reorder by flat index off the staircase.
+
+    Half 0 scores: sub-key 10 -> 2^25, sub-key 3 -> 2^25 - 2; half 1: sub-key 20 -> 1.5,
+    sub-key 7 -> 1.25 (every other sub-key -1000).  All four sums of the top-2 x top-2
+    pairs round to 2^25 in fp32, so by flat index (a * 64 + b) the top-2 cells are
+    3*64+7 = 199 and 3*64+20 = 212; (1,1) lies off the staircase (i+1)(j+1) <= 2, which
+    the exhaustive path must catch.  The float64 oracle orders them by the exact sums;
+    the two answers differ only inside the near-tie margin.
+    """
+    import sparse_key_value_amd as P
+    n, dh = 64, 64
+    K = np.full((1, 2, n, dh), 0.0, dtype=np.float32)
+    K[0, :, :, 0] = -1000.0
+    K[0, 0, 10, 0], K[0, 0, 3, 0] = 2.0 ** 25, 2.0 ** 25 - 2
+    K[0, 1, 20, 0], K[0, 1, 7, 0] = 1.5, 1.25
+    dev = torch.from_numpy(K).cuda()
+    wq = torch.zeros((64, 128), dtype=torch.float32, device="cuda")
+    vals = torch.zeros((n * n, 4), dtype=torch.float32, device="cuda")
+    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=128, n_sub=n, k=2, d_value=4, dtype="f32", qk_norm=0,
+                            memory_plus=0, max_tokens=4, W_q=wq, subkeys=dev, values=vals)
+    q = np.zeros((1, 1, 2, dh), dtype=np.float32)
+    q[0, 0, :, 0] = 1.0
+    hi_ = torch.empty((1, 1, 2, 2), dtype=torch.int32, device="cuda")
+    hs_ = torch.empty((1, 1, 2, 2), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, 1, 2), dtype=torch.int32, device="cuda")
+    sc = torch.empty((1, 1, 2), dtype=torch.float32, device="cuda")
+    w = torch.empty((1, 1, 2), dtype=torch.float32, device="cuda")
+    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), 1, hi_, hs_, idx, sc, w)
+    torch.cuda.synchronize()
+    assert hi_.cpu().numpy().tolist() == [[[[10, 3], [20, 7]]]]
+    assert idx.cpu().numpy().tolist() == [[[199, 212]]]
+    assert sc.cpu().numpy().tolist() == [[[2.0 ** 25, 2.0 ** 25]]]
+    np.testing.assert_allclose(w.cpu().numpy(), 0.5)
+    # the oracle's float64 answer differs only within the near-tie margin
+    q64 = q.astype(np.float64).reshape(1, 1, 2 * dh)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64), 2)
+    assert sel["idx"].tolist() == [[[660, 647]]]
+    ch = PAR.cell_choice_scores(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64),
+                                idx.cpu().numpy())
+    PAR.check_lists(idx.cpu().numpy(), sel["idx"], sel["score"], ch, "rounding-tie case")
+    pk.close()
