@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the forward has no multi-GPU path "
@@ -142,6 +143,7 @@ def main():
     log(f"workload {cfg.name}: T={T}, N={cfg.N}, d_v={cfg.d_v}, {cfg.dtype}; filling the value table")
     wl = Workload(cfg, seed=a.seed)
     h = wl.pkm.handle
+    P.pkm_set_pipeline_chunks(h, a.chunks)
     x = wl.dev["x"]
     out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
     stream = torch.cuda.current_stream()
@@ -204,7 +206,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights; value table generated on the GPU)",
-        "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
+        "config": {"workload": cfg.name, "tokens": T, "pipeline_chunks": a.chunks or "auto", "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
                    "n_sub": cfg.n_sub, "n_keys": cfg.N, "d_value": cfg.d_v, "k": cfg.k, "qk_norm": cfg.qk_norm,
                    "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30},
         "roofline": {"bound": "hbm", "kernel": "gather (weighted EmbeddingBag)", "achieved": achieved,

@@ -33,8 +33,10 @@
  *  - Pointers to tensors are DEVICE pointers, row-major, owned by the caller
  *    (typically PyTorch tensors) and must stay valid while in use.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *    Every call only enqueues work on that stream and returns without waiting
- *    for the GPU; the forward allocates nothing and performs no host sync.
+ *    Every call only enqueues work and returns without waiting for the GPU;
+ *    the forward allocates nothing and performs no host sync.  Its results are
+ *    ordered on `stream`: work enqueued on `stream` afterwards sees them.
+ *  - A handle belongs to the device that is current at pkm_create.
  *  - Return value: PKM_OK (0) or a negative PKM_E* code; on error, the message
  *    is available from pkm_last_error() (thread-local) and nothing was enqueued
  *    unless the code is PKM_EHIP.  Nothing aborts and no C++ exception leaves
@@ -64,7 +66,7 @@ typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 typedef struct {
   int32_t d_model;      /* width of x */
   int32_t n_heads;      /* H >= 1 */
-  int32_t d_query;      /* per-head query width d_q; even; d_q / 2 in {64, 128, 256} */
+  int32_t d_query;      /* per-head query width d_q; d_q / 2 in {64, 128, 256} (256: bf16 only) */
   int32_t n_sub;        /* sub-keys per half; the table has N = n_sub^2 < 2^31 rows */
   int32_t k;            /* per-half and final top-k, 1 <= k <= min(n_sub, 32) */
   int32_t d_value;      /* value width; d_value * sizeof(dtype) must be a multiple of 16 */
@@ -131,6 +133,14 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
                pkm_handle** out);
 
 /* The forward for T tokens (0 <= T <= max_tokens; T = 0 enqueues nothing).
+ * By default every stage runs in order on `stream`.  With
+ * pkm_set_pipeline_chunks(h, c > 1) the tokens are split into c chunks that are
+ * pipelined over two internal streams of the handle (created at pkm_create,
+ * default priority): one runs the matrix-core work (selection of every chunk,
+ * then the gate of a chunk once its gather is done), the other the gathers, so
+ * a chunk's HBM-bound gather runs beside its neighbours' matrix work.  Both
+ * streams fork from `stream` after the work already queued there and join back
+ * into it.  The results are bitwise the same for every chunk count.
  *   x        [T, d_model] dtype
  *   out      [T, d_model] dtype if memory_plus, else [T, d_value] dtype
  *   idx_out  [T, H, k] int32, optional (NULL): final flat indices
@@ -161,14 +171,21 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
                       const int32_t* idx, const float* w, int64_t n_bags, int32_t bag_size, float* y,
                       void* stream);
 
-/* Per-stage timing with HIP events recorded on the forward's stream.
+/* Per-stage timing with HIP events recorded on the stream each stage runs on.
  * pkm_enable_stage_timing keeps the last `max_records` forwards (0 turns it off);
  * it allocates the events, so call it outside any timed or captured region.
  * pkm_stage_times waits for the recorded events, writes up to `n` durations in
  * milliseconds of stage `stage` (PKM_STAGE_*) for the recorded forwards, oldest
- * first, and returns how many it wrote (or a negative error code). */
+ * first, and returns how many it wrote (or a negative error code).  A stage's
+ * duration is the sum over the forward's chunks of the time between the events
+ * around that stage's launches; stages of different chunks can overlap, so
+ * the stage times may add up to more than PKM_STAGE_TOTAL. */
 int pkm_enable_stage_timing(pkm_handle* h, int32_t max_records);
 int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n);
+
+/* Number of token chunks pkm_forward pipelines a batch over: 0 (the default) or
+ * 1 runs every stage on the caller's stream in order; 2..8 that many chunks. */
+int pkm_set_pipeline_chunks(pkm_handle* h, int32_t chunks);
 
 /* Release the handle's host state and events (the workspace stays the caller's). */
 int pkm_destroy(pkm_handle* h);

@@ -21,7 +21,7 @@ STAGES = ["project", "qnorm", "score", "combine", "gather", "gate1", "gate2", "t
 STAGE_ID = {n: i for i, n in enumerate(STAGES)}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_key_value_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_key_value_amd/build.py` "
                       "(the product-key memory path has no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -51,6 +51,7 @@ _sig = {
     "pkm_embedding_bag": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp]),
     "pkm_enable_stage_timing": (ctypes.c_int, [_vp, _i32]),
     "pkm_stage_times": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_float), _i32]),
+    "pkm_set_pipeline_chunks": (ctypes.c_int, [_vp, _i32]),
     "pkm_destroy": (ctypes.c_int, [_vp]),
     "pkm_last_error": (ctypes.c_char_p, []),
 }
@@ -148,6 +149,10 @@ def pkm_stage_times(h: int, stage, n: int) -> list[float]:
     buf = (ctypes.c_float * max(1, n))()
     got = _check(_lib.pkm_stage_times(h, sid, buf, n), "pkm_stage_times")
     return [buf[i] for i in range(got)]
+
+
+def pkm_set_pipeline_chunks(h: int, chunks: int) -> None:
+    _check(_lib.pkm_set_pipeline_chunks(h, chunks), "pkm_set_pipeline_chunks")
 
 
 def pkm_destroy(h: int) -> None:

@@ -1,6 +1,6 @@
 """Build the HIP libraries in-tree for gfx950.
 
-    python -m sparse_key_value_amd.build
+    python sparse_key_value_amd/build.py
 
 compiles every ``*.hip`` under ``sparse_key_value_amd/csrc`` into
 ``sparse_key_value_amd/libpkm.so`` and the input-generator kernels under

@@ -44,15 +44,27 @@ int check_device() {
 
 }  // namespace
 
+constexpr int MAX_CHUNKS = 8;
+
 struct pkm_handle {
   pkm_config cfg;
   int d_h = 0;
   const void* values = nullptr;
   uint8_t* ws = nullptr;
   pkm::Layout L;
-  // stage timing: max_rec records of PKM_NUM_STAGES boundary events each
+  int chunks = 0;  // 0 = automatic
+  // pipelining: stream A runs the matrix-core work (selection a1-a6 of every chunk and
+  // the gate a8), stream B the gathers (a7); both fork from and join back to the
+  // caller's stream
+  hipStream_t sA = nullptr, sB = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_joinA = nullptr, ev_joinB = nullptr;
+  hipEvent_t ev_sel[MAX_CHUNKS] = {};
+  hipEvent_t ev_gat[MAX_CHUNKS] = {};
+  // stage timing: max_rec records, each with (begin, end) events per stage and chunk plus
+  // the whole forward
   int max_rec = 0, next = 0, count = 0;
   std::vector<hipEvent_t> ev;
+  std::vector<int> rec_chunks;
 
   template <typename T = void>
   T* at(size_t off) const { return (T*)(ws + off); }
@@ -60,21 +72,58 @@ struct pkm_handle {
 
 namespace {
 
-void destroy_events(pkm_handle* h) {
+constexpr int EV_PER_REC = 7 * MAX_CHUNKS * 2 + 2;
+
+void destroy_timing(pkm_handle* h) {
   for (hipEvent_t e : h->ev)
     if (e) (void)hipEventDestroy(e);
   h->ev.clear();
+  h->rec_chunks.clear();
   h->max_rec = h->next = h->count = 0;
+}
+
+void destroy_pipeline(pkm_handle* h) {
+  for (hipEvent_t* e : {&h->ev_fork, &h->ev_joinA, &h->ev_joinB})
+    if (*e) (void)hipEventDestroy(*e), *e = nullptr;
+  for (hipEvent_t& e : h->ev_sel)
+    if (e) (void)hipEventDestroy(e), e = nullptr;
+  for (hipEvent_t& e : h->ev_gat)
+    if (e) (void)hipEventDestroy(e), e = nullptr;
+  if (h->sA) (void)hipStreamDestroy(h->sA), h->sA = nullptr;
+  if (h->sB) (void)hipStreamDestroy(h->sB), h->sB = nullptr;
+}
+
+int create_pipeline(pkm_handle* h) {
+  PKM_HIP(hipStreamCreateWithFlags(&h->sA, hipStreamNonBlocking));
+  PKM_HIP(hipStreamCreateWithFlags(&h->sB, hipStreamNonBlocking));
+  for (hipEvent_t* e : {&h->ev_fork, &h->ev_joinA, &h->ev_joinB}) PKM_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  for (hipEvent_t& e : h->ev_sel) PKM_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (hipEvent_t& e : h->ev_gat) PKM_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  return PKM_OK;
+}
+
+// Number of token chunks a forward of T tokens is pipelined over.  Measured on MI355X,
+// running the gather beside the matrix-core kernels slows both about as much as it
+// overlaps them, so the default is one chunk (every stage in order on one stream).
+int chunks_for(const pkm_handle* h, int64_t T) {
+  if (h->chunks > 0) return (int)(T < h->chunks ? (T > 0 ? T : 1) : h->chunks);
+  return 1;
 }
 
 struct Timer {
   pkm_handle* h;
-  hipStream_t s;
   int slot;
-  explicit Timer(pkm_handle* h_, hipStream_t s_) : h(h_), s(s_), slot(h_->max_rec ? h_->next : -1) {}
-  hipError_t mark(int boundary) {
+  Timer(pkm_handle* h_, int nch) : h(h_), slot(h_->max_rec ? h_->next : -1) {
+    if (slot >= 0) h->rec_chunks[slot] = nch;
+  }
+  hipEvent_t* base() const { return &h->ev[(size_t)slot * EV_PER_REC]; }
+  hipError_t stage(int st, int chunk, int end, hipStream_t s) {
     if (slot < 0) return hipSuccess;
-    return hipEventRecord(h->ev[(size_t)slot * PKM_NUM_STAGES + boundary], s);
+    return hipEventRecord(base()[(st * MAX_CHUNKS + chunk) * 2 + end], s);
+  }
+  hipError_t total(int end, hipStream_t s) {
+    if (slot < 0) return hipSuccess;
+    return hipEventRecord(base()[7 * MAX_CHUNKS * 2 + end], s);
   }
   void commit() {
     if (slot < 0) return;
@@ -89,13 +138,104 @@ struct Timer {
     if (e_ != hipSuccess) return fail(PKM_EHIP, "launch %s failed: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
-int run_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* hidx, float* hsc, int32_t* idx, float* sc,
-               float* w, hipStream_t s, Timer* tm) {
+// Selection scratch of the rows of tokens [t0, ...): group maxima, bounds, candidates.
+struct SelScratch {
+  float* gmax;
+  float* theta;
+  uint64_t* cand;
+  int32_t* count;
+};
+
+SelScratch scratch_at(pkm_handle* h, int64_t t0) {
+  const pkm::Layout& L = h->L;
+  const size_t r0 = (size_t)t0 * h->cfg.n_heads * 2;  // first row (token, head, half)
+  return {h->at<float>(L.gmax) + r0 * pkm::MAX_GROUPS, h->at<float>(L.theta) + r0,
+          h->at<uint64_t>(L.cand) + r0 * pkm::CAND, h->at<int32_t>(L.count) + 2 * r0};
+}
+
+int run_select(pkm_handle* h, const void* qhat, int64_t T, const SelScratch& sx, int32_t* hidx, float* hsc,
+               int32_t* idx, float* sc, float* w, hipStream_t s, Timer* tm, int chunk) {
   const pkm_config& c = h->cfg;
-  PKM_LAUNCH(pkm::launch_score_topk(qhat, h->at(h->L.khat), T, c.n_heads, h->d_h, c.n_sub, c.k, c.dtype, hidx, hsc, s));
-  if (tm) PKM_LAUNCH(tm->mark(3));
-  PKM_LAUNCH(pkm::launch_combine(hidx, hsc, T, c.n_heads, c.n_sub, c.k, idx, sc, w, s));
-  if (tm) PKM_LAUNCH(tm->mark(4));
+  if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, chunk, 0, s));
+  PKM_LAUNCH(pkm::launch_score_candidates(qhat, h->at(h->L.khat), T, c.n_heads, h->d_h, c.n_sub, c.k, c.dtype,
+                                          sx.gmax, sx.theta, sx.cand, sx.count, s));
+  if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, chunk, 1, s));
+  if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_COMBINE, chunk, 0, s));
+  PKM_LAUNCH(pkm::launch_combine(sx.cand, sx.count, T, c.n_heads, c.n_sub, c.k, hidx, hsc, idx, sc, w, s));
+  if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_COMBINE, chunk, 1, s));
+  return PKM_OK;
+}
+
+// Selection (a1-a6) for tokens [t0, t0 + tc) on stream sa.
+int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream_t sa, Timer& tm, int chunk) {
+  const pkm_config& c = h->cfg;
+  const pkm::Layout& L = h->L;
+  const int H = c.n_heads, dq = c.d_query, k = c.k;
+  const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
+  const uint8_t* xc = (const uint8_t*)x + (size_t)t0 * c.d_model * eb;
+  float* q = h->at<float>(L.q) + (size_t)t0 * H * dq;
+  uint8_t* qhat = h->at<uint8_t>(L.qhat) + (size_t)t0 * H * dq * eb;
+  // a1: q = x W_q (fp32)
+  PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 0, sa));
+  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.wqT), q, nullptr, tc, H * dq, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 1, sa));
+  // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves
+  PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 0, sa));
+  PKM_LAUNCH(pkm::launch_rownorm(q, 1, qhat, c.dtype, tc * H, dq, c.qk_norm, c.norm_eps, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 1, sa));
+  // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
+  const size_t sel = (size_t)t0 * H * k;
+  return run_select(h, qhat, tc, scratch_at(h, t0), h->at<int32_t>(L.hidx) + 2 * sel, h->at<float>(L.hsc) + 2 * sel,
+                    h->at<int32_t>(L.idx) + sel, h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
+}
+
+// Gather (a7) for tokens [t0, t0 + tc) on stream sb: into y (fp32) with the gate, else
+// straight into out.
+int chunk_gather(pkm_handle* h, int64_t t0, int64_t tc, void* out, float* ydbg, hipStream_t sb, Timer& tm,
+                 int chunk) {
+  const pkm_config& c = h->cfg;
+  const pkm::Layout& L = h->L;
+  const int H = c.n_heads, k = c.k;
+  const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
+  const int64_t N = (int64_t)c.n_sub * c.n_sub;
+  const size_t sel = (size_t)t0 * H * k;
+  const int32_t* idx = h->at<int32_t>(L.idx) + sel;
+  const float* w = h->at<float>(L.w) + sel;
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATHER, chunk, 0, sb));
+  if (c.memory_plus) {
+    float* y = (ydbg ? ydbg : h->at<float>(L.y)) + (size_t)t0 * c.d_value;
+    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, y, 0, sb));
+  } else {
+    uint8_t* o = (uint8_t*)out + (size_t)t0 * c.d_value * eb;
+    if (ydbg) {
+      float* y = ydbg + (size_t)t0 * c.d_value;
+      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, y, 0, sb));
+      PKM_LAUNCH(pkm::launch_convert_f32(y, o, tc * c.d_value, c.dtype, sb));
+    } else {
+      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, o, 1, sb));
+    }
+  }
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATHER, chunk, 1, sb));
+  return PKM_OK;
+}
+
+// Memory+ gate (a8) for tokens [t0, t0 + tc) on stream sa: g = y * silu(x W1) in dtype, out = g W2.
+int chunk_gate(pkm_handle* h, const void* x, int64_t t0, int64_t tc, void* out, float* ydbg, hipStream_t sa,
+               Timer& tm, int chunk) {
+  const pkm_config& c = h->cfg;
+  const pkm::Layout& L = h->L;
+  const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
+  const uint8_t* xc = (const uint8_t*)x + (size_t)t0 * c.d_model * eb;
+  const float* y = (ydbg ? ydbg : h->at<float>(L.y)) + (size_t)t0 * c.d_value;
+  uint8_t* g = h->at<uint8_t>(L.g) + (size_t)t0 * c.d_value * eb;
+  uint8_t* o = (uint8_t*)out + (size_t)t0 * c.d_model * eb;
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 0, sa));
+  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.w1T), g, y, tc, c.d_value, c.d_model, c.dtype, pkm::EPI_GATE, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 1, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE2, chunk, 0, sa));
+  PKM_LAUNCH(pkm::launch_gemm(g, h->at(L.w2T), o, nullptr, tc, c.d_model, c.d_value, c.dtype,
+                              c.dtype == PKM_BF16 ? pkm::EPI_STORE_DT : pkm::EPI_STORE_F32, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE2, chunk, 1, sa));
   return PKM_OK;
 }
 
@@ -109,46 +249,69 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   const pkm::Layout& L = h->L;
   const int H = c.n_heads, dq = c.d_query, k = c.k;
   const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
-
-  Timer tm(h, s);
-  PKM_LAUNCH(tm.mark(0));
-  // a1: q = x W_q (fp32)
-  PKM_LAUNCH(pkm::launch_gemm(x, h->at(L.wqT), h->at(L.q), nullptr, T, H * dq, c.d_model, c.dtype, pkm::EPI_STORE_F32, s));
-  PKM_LAUNCH(tm.mark(1));
-  // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves
-  PKM_LAUNCH(pkm::launch_rownorm(h->at(L.q), 1, h->at(L.qhat), c.dtype, T * H, dq, c.qk_norm, c.norm_eps, s));
-  PKM_LAUNCH(tm.mark(2));
-  // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
-  int32_t* idx = h->at<int32_t>(L.idx);
-  float* w = h->at<float>(L.w);
-  int rc = run_select(h, h->at(L.qhat), T, h->at<int32_t>(L.hidx), h->at<float>(L.hsc), idx, h->at<float>(L.sc), w, s, &tm);
-  if (rc) return rc;
-  // a7: weighted EmbeddingBag of the H*k rows of every token
-  const int64_t N = (int64_t)c.n_sub * c.n_sub;
   float* ydbg = dbg ? dbg->y : nullptr;
-  if (c.memory_plus) {
-    float* y = ydbg ? ydbg : h->at<float>(L.y);
-    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, T, H * k, y, 0, s));
-    PKM_LAUNCH(tm.mark(5));
-    // a8: g = y * silu(x W1) in dtype, out = g W2
-    PKM_LAUNCH(pkm::launch_gemm(x, h->at(L.w1T), h->at(L.g), y, T, c.d_value, c.d_model, c.dtype, pkm::EPI_GATE, s));
-    PKM_LAUNCH(tm.mark(6));
-    PKM_LAUNCH(pkm::launch_gemm(h->at(L.g), h->at(L.w2T), out, nullptr, T, c.d_model, c.d_value, c.dtype,
-                                c.dtype == PKM_BF16 ? pkm::EPI_STORE_DT : pkm::EPI_STORE_F32, s));
-    PKM_LAUNCH(tm.mark(7));
+
+  const int nch = chunks_for(h, T);
+  const int64_t tcs = (T + nch - 1) / nch;
+  Timer tm(h, nch);
+  PKM_LAUNCH(tm.total(0, s));
+  const bool gated = c.memory_plus != 0;
+  if (nch == 1) {
+    int rc = chunk_select(h, x, 0, T, s, tm, 0);
+    if (!rc) rc = chunk_gather(h, 0, T, out, ydbg, s, tm, 0);
+    if (!rc && gated) rc = chunk_gate(h, x, 0, T, out, ydbg, s, tm, 0);
+    if (rc) return rc;
   } else {
-    if (ydbg) {
-      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, T, H * k, ydbg, 0, s));
-      PKM_LAUNCH(pkm::launch_convert_f32(ydbg, out, T * c.d_value, c.dtype, s));
-    } else {
-      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, T, H * k, out, 1, s));
+    // fork: both internal streams start after the work already queued on `s`.
+    // Stream A: select(0), select(1), gate(0), select(2), gate(1), ...; stream B:
+    // gather(c) as soon as select(c) is done.  So the gather of one chunk runs beside
+    // the matrix-core work of its neighbours.
+    PKM_HIP(hipEventRecord(h->ev_fork, s));
+    PKM_HIP(hipStreamWaitEvent(h->sA, h->ev_fork, 0));
+    PKM_HIP(hipStreamWaitEvent(h->sB, h->ev_fork, 0));
+    auto span = [&](int ch, int64_t& t0, int64_t& tc) {
+      t0 = ch * tcs;
+      tc = T - t0 < tcs ? T - t0 : tcs;
+    };
+    int last = -1;
+    for (int ch = 0; ch < nch; ++ch) {
+      int64_t t0, tc;
+      span(ch, t0, tc);
+      if (tc <= 0) break;
+      int rc = chunk_select(h, x, t0, tc, h->sA, tm, ch);
+      if (rc) return rc;
+      PKM_HIP(hipEventRecord(h->ev_sel[ch], h->sA));
+      PKM_HIP(hipStreamWaitEvent(h->sB, h->ev_sel[ch], 0));
+      rc = chunk_gather(h, t0, tc, out, ydbg, h->sB, tm, ch);
+      if (rc) return rc;
+      PKM_HIP(hipEventRecord(h->ev_gat[ch], h->sB));
+      if (gated && ch > 0) {
+        int64_t p0, pc;
+        span(ch - 1, p0, pc);
+        PKM_HIP(hipStreamWaitEvent(h->sA, h->ev_gat[ch - 1], 0));
+        rc = chunk_gate(h, x, p0, pc, out, ydbg, h->sA, tm, ch - 1);
+        if (rc) return rc;
+      }
+      last = ch;
     }
-    PKM_LAUNCH(tm.mark(5));
-    PKM_LAUNCH(tm.mark(6));
-    PKM_LAUNCH(tm.mark(7));
+    if (gated && last >= 0) {
+      int64_t p0, pc;
+      span(last, p0, pc);
+      PKM_HIP(hipStreamWaitEvent(h->sA, h->ev_gat[last], 0));
+      int rc = chunk_gate(h, x, p0, pc, out, ydbg, h->sA, tm, last);
+      if (rc) return rc;
+    }
+    // join: `s` continues after both internal streams
+    PKM_HIP(hipEventRecord(h->ev_joinA, h->sA));
+    PKM_HIP(hipEventRecord(h->ev_joinB, h->sB));
+    PKM_HIP(hipStreamWaitEvent(s, h->ev_joinA, 0));
+    PKM_HIP(hipStreamWaitEvent(s, h->ev_joinB, 0));
   }
+  PKM_LAUNCH(tm.total(1, s));
   tm.commit();
 
+  int32_t* idx = h->at<int32_t>(L.idx);
+  float* w = h->at<float>(L.w);
   const size_t nsel = (size_t)T * H * k;
   if (idx_out) PKM_HIP(hipMemcpyAsync(idx_out, idx, nsel * 4, hipMemcpyDeviceToDevice, s));
   if (w_out) PKM_HIP(hipMemcpyAsync(w_out, w, nsel * 4, hipMemcpyDeviceToDevice, s));
@@ -204,9 +367,15 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   hipStream_t s = (hipStream_t)stream;
   const pkm_config& c = *cfg;
   auto bail = [&](int code) {
+    destroy_pipeline(h);
     delete h;
     return code;
   };
+  rc = create_pipeline(h);
+  if (rc) {
+    destroy_pipeline(h);
+    return bail(rc);
+  }
   hipError_t e;
   // W_q [d_model, H*d_q] -> [H*d_q, d_model]
   if ((e = pkm::launch_transpose(W_q, h->at(L.wqT), c.d_model, c.n_heads * c.d_query, c.dtype, s)) != hipSuccess)
@@ -239,9 +408,9 @@ int pkm_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* half_idx, fl
   if (T == 0) return PKM_OK;
   if (!qhat) return fail(PKM_EINVAL, "qhat must not be NULL");
   const pkm::Layout& L = h->L;
-  return run_select(h, qhat, T, half_idx ? half_idx : h->at<int32_t>(L.hidx), half_score ? half_score : h->at<float>(L.hsc),
+  return run_select(h, qhat, T, scratch_at(h, 0), half_idx ? half_idx : h->at<int32_t>(L.hidx), half_score ? half_score : h->at<float>(L.hsc),
                     idx ? idx : h->at<int32_t>(L.idx), score ? score : h->at<float>(L.sc), w ? w : h->at<float>(L.w),
-                    (hipStream_t)stream, nullptr);
+                    (hipStream_t)stream, nullptr, 0);
 }
 
 int pkm_copy_normalized_subkeys(pkm_handle* h, void* dst, void* stream) {
@@ -269,14 +438,15 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
 
 int pkm_enable_stage_timing(pkm_handle* h, int32_t max_records) {
   if (!h) return fail(PKM_EINVAL, "handle is NULL");
-  if (max_records < 0 || max_records > 4096) return fail(PKM_EINVAL, "max_records must be in [0, 4096]");
-  destroy_events(h);
+  if (max_records < 0 || max_records > 1024) return fail(PKM_EINVAL, "max_records must be in [0, 1024]");
+  destroy_timing(h);
   if (max_records == 0) return PKM_OK;
-  h->ev.assign((size_t)max_records * PKM_NUM_STAGES, nullptr);
+  h->ev.assign((size_t)max_records * EV_PER_REC, nullptr);
+  h->rec_chunks.assign(max_records, 0);
   for (hipEvent_t& e : h->ev) {
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) {
-      destroy_events(h);
+      destroy_timing(h);
       return fail(PKM_EHIP, "hipEventCreate: %s", hipGetErrorString(r));
     }
   }
@@ -291,20 +461,39 @@ int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n) {
   const int have = h->count < n ? h->count : n;
   const int first = (h->next - h->count + h->max_rec) % h->max_rec;  // oldest record
   const int skip = h->count - have;
+  const bool gated = h->cfg.memory_plus != 0;
   for (int i = 0; i < have; ++i) {
     const int slot = (first + skip + i) % h->max_rec;
-    hipEvent_t* e = &h->ev[(size_t)slot * PKM_NUM_STAGES];
-    const int b0 = stage == PKM_STAGE_TOTAL ? 0 : stage;
-    const int b1 = stage == PKM_STAGE_TOTAL ? PKM_NUM_STAGES - 1 : stage + 1;
-    PKM_HIP(hipEventSynchronize(e[b1]));
-    PKM_HIP(hipEventElapsedTime(&ms[i], e[b0], e[b1]));
+    hipEvent_t* e = &h->ev[(size_t)slot * EV_PER_REC];
+    float sum = 0.f;
+    if (stage == PKM_STAGE_TOTAL) {
+      PKM_HIP(hipEventSynchronize(e[7 * MAX_CHUNKS * 2 + 1]));
+      PKM_HIP(hipEventElapsedTime(&sum, e[7 * MAX_CHUNKS * 2], e[7 * MAX_CHUNKS * 2 + 1]));
+    } else if (gated || (stage != PKM_STAGE_GATE1 && stage != PKM_STAGE_GATE2)) {
+      // sum over the chunks: the time this stage's kernels spent, each measured on its stream
+      for (int c = 0; c < h->rec_chunks[slot]; ++c) {
+        float t = 0.f;
+        PKM_HIP(hipEventSynchronize(e[(stage * MAX_CHUNKS + c) * 2 + 1]));
+        PKM_HIP(hipEventElapsedTime(&t, e[(stage * MAX_CHUNKS + c) * 2], e[(stage * MAX_CHUNKS + c) * 2 + 1]));
+        sum += t;
+      }
+    }
+    ms[i] = sum;
   }
   return have;
 }
 
+int pkm_set_pipeline_chunks(pkm_handle* h, int32_t chunks) {
+  if (!h) return fail(PKM_EINVAL, "handle is NULL");
+  if (chunks < 0 || chunks > MAX_CHUNKS) return fail(PKM_EINVAL, "chunks must be in [0, %d]", MAX_CHUNKS);
+  h->chunks = chunks;
+  return PKM_OK;
+}
+
 int pkm_destroy(pkm_handle* h) {
   if (!h) return fail(PKM_EINVAL, "handle is NULL");
-  destroy_events(h);
+  destroy_timing(h);
+  destroy_pipeline(h);
   delete h;
   return PKM_OK;
 }

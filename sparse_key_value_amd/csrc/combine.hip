@@ -9,7 +9,11 @@
 // values; overview: weighted average of about thirty values).  The sum is an fp32 add
 // of the two fp32 half scores.
 //
-// One wave per (token, head).  Both lists are sorted, so the pair of positions (i, j)
+// One wave per (token, head).  First the two per-half lists: each half's candidates
+// (at most CAND keys from the scoring kernel, a superset of its top-k) are ranked by
+// comparing every key with every other (v_readlane broadcasts), and the k best are
+// written, in order, to LDS and to the per-half outputs.  Both lists are then sorted,
+// so the pair of positions (i, j)
 // is beaten by every (i', j') with i' <= i, j' <= j; in exact arithmetic only the
 // "staircase" (i + 1)(j + 1) <= k can reach the top-k (119 pairs for k = 32 instead of
 // 1,024).  The staircase is sorted with a bitonic network over two keys per lane.  The
@@ -26,11 +30,6 @@ namespace {
 struct Stair {
   uint16_t pos[128];  // (i << 8) | j for staircase slot s, 0xFFFF = empty
 };
-
-__device__ __forceinline__ uint64_t cell_key(const float* s0, const int32_t* i0, const float* s1, const int32_t* i1,
-                                             int a, int b, int n) {
-  return make_key(s0[a] + s1[b], (uint32_t)i0[a] * (uint32_t)n + (uint32_t)i1[b]);
-}
 
 // Sort 128 keys held two per lane (element e = 2 * lane + slot) in descending order.
 __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lane) {
@@ -57,22 +56,58 @@ __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lan
   }
 }
 
-__global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ half_idx,
-                                                      const float* __restrict__ half_score, int64_t rows, int n,
-                                                      int k, Stair st, int32_t* __restrict__ idx,
+__global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict__ cand,
+                                                      const int32_t* __restrict__ count, int64_t rows, int n, int k,
+                                                      Stair st, int32_t* __restrict__ half_idx,
+                                                      float* __restrict__ half_score, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row = t * H + h
+  __shared__ uint64_t lists[4][2][32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;  // row = t * H + h
   if (row >= rows) return;
-  const int32_t* i0 = half_idx + row * 2 * k;
-  const int32_t* i1 = i0 + k;
-  const float* s0 = half_score + row * 2 * k;
-  const float* s1 = s0 + k;
+
+  // per-half top-k from the candidates, sorted by rank
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    // candidates: lane half 0 in slots [0, CAND/2), half 1 in [CAND/2, CAND)
+    const int64_t r2 = row * 2 + c;
+    const int na = count[2 * r2], nb = count[2 * r2 + 1];  // <= CAND / 2 after the overflow pass
+    const uint64_t* cr = cand + r2 * CAND;
+    const uint64_t x0 = lane < na ? cr[lane] : 0ull;
+    const uint64_t x1 = lane < nb ? cr[CAND / 2 + lane] : 0ull;
+    int r0 = 0, r1 = 0;
+    for (int i = 0; i < na; ++i) {
+      const uint64_t y = readlane_u64(x0, i);
+      r0 += y > x0;
+      r1 += y > x1;
+    }
+    for (int i = 0; i < nb; ++i) {
+      const uint64_t y = readlane_u64(x1, i);
+      r0 += y > x0;
+      r1 += y > x1;
+    }
+    if (lane < na && r0 < k) lists[wv][c][r0] = x0;
+    if (lane < nb && r1 < k) lists[wv][c][r1] = x1;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  if (lane < 2 * k) {
+    const int c = lane / k, j = lane - c * k;
+    const uint64_t key = lists[wv][c][j];
+    const int64_t o = (row * 2 + c) * k + j;
+    half_idx[o] = (int32_t)key_index(key);
+    half_score[o] = key_score(key);
+  }
+  const uint64_t* L0 = lists[wv][0];
+  const uint64_t* L1 = lists[wv][1];
+  auto cell_key = [&](int a, int b) -> uint64_t {
+    return make_key(key_score(L0[a]) + key_score(L1[b]), key_index(L0[a]) * (uint32_t)n + key_index(L1[b]));
+  };
 
   // staircase keys, two per lane
   const uint16_t p0 = st.pos[2 * lane], p1 = st.pos[2 * lane + 1];
-  uint64_t x0 = p0 != 0xFFFF ? cell_key(s0, i0, s1, i1, p0 >> 8, p0 & 0xFF, n) : 0ull;
-  uint64_t x1 = p1 != 0xFFFF ? cell_key(s0, i0, s1, i1, p1 >> 8, p1 & 0xFF, n) : 0ull;
+  uint64_t x0 = p0 != 0xFFFF ? cell_key(p0 >> 8, p0 & 0xFF) : 0ull;
+  uint64_t x1 = p1 != 0xFFFF ? cell_key(p1 >> 8, p1 & 0xFF) : 0ull;
   sort128_desc(x0, x1, lane);
   // element e = 2 * lane + slot; the k-th best is element k - 1
   const uint64_t kth = shfl_u64((k - 1) & 1 ? x1 : x0, (k - 1) >> 1);
@@ -85,7 +120,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
     const int cidx = lane + 64 * r;
     if (cidx < kk) {
       const int a = cidx / k, b = cidx - a * k;
-      if ((a + 1) * (b + 1) > k && cell_key(s0, i0, s1, i1, a, b, n) > kth) beaten = true;
+      if ((a + 1) * (b + 1) > k && cell_key(a, b) > kth) beaten = true;
     }
   }
   uint64_t mine;  // lane j < k ends up with the j-th best key
@@ -99,7 +134,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int cidx = lane + 64 * r;
-      key[r] = cidx < kk ? cell_key(s0, i0, s1, i1, cidx / k, cidx % k, n) : 0ull;
+      key[r] = cidx < kk ? cell_key(cidx / k, cidx % k) : 0ull;
     }
     mine = 0ull;
     for (int j = 0; j < k; ++j) {
@@ -128,8 +163,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_combine(const int32_t* half_idx, const float* half_score, int64_t T, int H, int n, int k,
-                          int32_t* idx, float* score, float* w, hipStream_t s) {
+hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T, int H, int n, int k,
+                          int32_t* half_idx, float* half_score, int32_t* idx, float* score, float* w, hipStream_t s) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
   Stair st;
@@ -137,7 +172,8 @@ hipError_t launch_combine(const int32_t* half_idx, const float* half_score, int6
   for (int a = 0; a < k; ++a)
     for (int b = 0; (a + 1) * (b + 1) <= k; ++b) st.pos[m++] = (uint16_t)((a << 8) | b);
   for (; m < 128; ++m) st.pos[m] = 0xFFFF;
-  combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(half_idx, half_score, rows, n, k, st, idx, score, w);
+  combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(cand, count, rows, n, k, st, half_idx, half_score,
+                                                                  idx, score, w);
   return hipGetLastError();
 }
 

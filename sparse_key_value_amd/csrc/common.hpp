@@ -60,6 +60,13 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The 64-bit value of lane `src` (a wave-uniform lane index), broadcast to every lane.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Sort one key per lane across the 64 lanes of a wave, descending (lane 0 = largest).
 // Bitonic network (Batcher 1968): log2(64) * (log2(64) + 1) / 2 = 21 compare-exchange steps.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {

@@ -37,20 +37,35 @@ struct VecTraits<4> {  // fp32: 4 elements per 16 bytes
   }
 };
 
-// Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bag blockIdx.x*BPB+g and
-// the 16-byte column slices [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of its rows.
+template <int EB, int UNROLL>
+__device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
+                                           const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
+                                           int bag, void* __restrict__ y, int y_f32);
+
+// Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bags blockIdx.x*BPB+g,
+// then + gridDim.x*BPB, ... (a persistent grid, sized to the CU count so that the
+// gather keeps the HBM busy with about one wave per SIMD and leaves the rest of every
+// CU to kernels running beside it), and the 16-byte column slices
+// [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of their rows.
 template <int EB, int UNROLL, bool UNIFORM>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, int64_t n_rows,
                                                      int row_vecs, int tpr, int bags_per_block,
                                                      const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                      int64_t n_bags, int bag, void* __restrict__ y, int y_f32) {
-  using VT = VecTraits<EB>;
-  constexpr int E = VT::E;
   int g = threadIdx.x / tpr;
   if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
   const int col = blockIdx.y * tpr + (threadIdx.x - g * tpr);  // 16-byte slice index in the row
-  const int64_t b = (int64_t)blockIdx.x * bags_per_block + g;
-  if (g >= bags_per_block || b >= n_bags || col >= row_vecs) return;
+  if (g >= bags_per_block || col >= row_vecs) return;
+  for (int64_t b = (int64_t)blockIdx.x * bags_per_block + g; b < n_bags; b += (int64_t)gridDim.x * bags_per_block)
+    gather_bag<EB, UNROLL>(table, n_rows, row_vecs, col, idx, w, b, bag, y, y_f32);
+}
+
+template <int EB, int UNROLL>
+__device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
+                                           const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
+                                           int bag, void* __restrict__ y, int y_f32) {
+  using VT = VecTraits<EB>;
+  constexpr int E = VT::E;
   const int32_t* bi = idx + b * bag;
   const float* bw = w + b * bag;
   const size_t row_bytes = (size_t)row_vecs * 16;
@@ -106,16 +121,26 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s) {
   if (n_bags == 0) return hipSuccess;
+  static int max_blocks = 0;  // two blocks per CU
+  if (max_blocks == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    max_blocks = 2 * cus;
+  }
   const int eb = dtype == DT_BF16 ? 2 : 4;
   const int row_vecs = (int)((int64_t)dim * eb / 16);
   const int tpr = row_vecs < 256 ? row_vecs : 256;
   const int bpb = 256 / tpr;
   const int threads = bpb * tpr;
-  dim3 grid((unsigned)((n_bags + bpb - 1) / bpb), (unsigned)((row_vecs + tpr - 1) / tpr));
+  const int64_t groups = (n_bags + bpb - 1) / bpb;
+  const int cols = (row_vecs + tpr - 1) / tpr;
+  const int64_t bx = groups < max_blocks / cols ? groups : (max_blocks / cols > 0 ? max_blocks / cols : 1);
+  dim3 grid((unsigned)bx, (unsigned)cols);
   const int y_f32 = (!y_dtype_is_table || dtype == DT_F32) ? 1 : 0;
   const bool uniform = (tpr % 64) == 0;
 #define PKM_GATHER(EBV, UNI)                                                                                  \
-  gather_kernel<EBV, 8, UNI><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, w, \
+  gather_kernel<EBV, 16, UNI><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, w, \
                                                        n_bags, bag, y, y_f32)
   if (eb == 2) {
     if (uniform) PKM_GATHER(2, true); else PKM_GATHER(2, false);

@@ -4,10 +4,11 @@
 //
 // C[M, N] = A[M, K] * Bt[N, K]^T: both operands are K-contiguous (the weights are
 // transposed once at create), fp32 accumulation.
-//  * bf16: matrix cores, v_mfma_f32_32x32x16_bf16.  Block tile 128 x 128 x 64, four
-//    waves in a 2 x 2 arrangement, each wave 64 x 64 (2 x 2 MFMA tiles).  Tiles are
-//    staged through padded LDS rows; the next K-tile is prefetched into registers
-//    while the current one is multiplied.
+//  * bf16: matrix cores, v_mfma_f32_32x32x16_bf16.  Block tile 256 x 128 x 64 (128 x 128
+//    for small problems), four waves in a 2 x 2 arrangement, each wave 128 x 64 (4 x 2
+//    MFMA tiles, so each 16-byte LDS operand read feeds 1.33 MFMAs on average).  Tiles
+//    are staged through padded LDS rows; the next K-tile is prefetched into registers
+//    while the current one is multiplied; two blocks share a CU.
 //  * fp32: a plain SIMT tile (64 x 64 x 16, 4 x 4 per thread) for the fp32 workloads.
 #include "kernels.hpp"
 
@@ -15,13 +16,20 @@ namespace pkm {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): 144 bytes
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): 144 bytes, conflict-free 16-byte reads
 
-template <int EPI>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt,
-                                                        void* __restrict__ C, const float* __restrict__ aux, int64_t M,
-                                                        int N, int K) {
+// Block tile BM x BN, four waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) made of
+// 32 x 32 MFMA tiles.  A and B tiles are staged through padded LDS; the next K-tile is
+// prefetched into registers while the current one is multiplied.
+template <int BM, int BN, int EPI>
+__global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ Bt, void* __restrict__ C,
+                                                           const float* __restrict__ aux, int64_t M, int N, int K) {
+  constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;    // MFMA tiles per wave
+  constexpr int AU = BM * (BK / 8) / 256;      // 16-byte units of A per thread
+  constexpr int BU = BN * (BK / 8) / 256;
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
 
@@ -30,64 +38,71 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(const uint16_t* __restri
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
 
-  // global -> register prefetch: each tile is 128 rows x 8 units of 16 bytes; 4 units per thread
-  u32x4 pa[4], pb[4];
+  u32x4 pa[AU], pb[BU];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AU; ++i) {
       const int u = tid + i * 256;
-      const int r = u >> 3, cu = u & 7;
-      const int kc = k0 + cu * 8;
+      const int r = u >> 3, kc = k0 + (u & 7) * 8;
       const int64_t gm = m0 + r;
-      const int gn = n0 + r;
       pa[i] = (gm < M && kc < K) ? *(const u32x4*)(A + gm * K + kc) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + i * 256;
+      const int r = u >> 3, kc = k0 + (u & 7) * 8;
+      const int gn = n0 + r;
       pb[i] = (gn < N && kc < K) ? *(const u32x4*)(Bt + (int64_t)gn * K + kc) : u32x4{0, 0, 0, 0};
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
   fetch(0);
   for (int k0 = 0; k0 < K; k0 += BK) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AU; ++i) {
       const int u = tid + i * 256;
-      const int r = u >> 3, cu = u & 7;
-      *(u32x4*)(As + r * LDK + cu * 8) = pa[i];
-      *(u32x4*)(Bs + r * LDK + cu * 8) = pb[i];
+      *(u32x4*)(As + (u >> 3) * LDK + (u & 7) * 8) = pa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + i * 256;
+      *(u32x4*)(Bs + (u >> 3) * LDK + (u & 7) * 8) = pb[i];
     }
     __syncthreads();
     if (k0 + BK < K) fetch(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[TM], bfr[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *(const bf16x8*)(As + (wm * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
-        bfr[i] = *(const bf16x8*)(Bs + (wn * 64 + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
-      }
+      for (int i = 0; i < TM; ++i)
+        af[i] = *(const bf16x8*)(As + (wm * WM + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *(const bf16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
 
   // epilogue: lane holds column n = .. + lane % 32 and 16 rows of each 32 x 32 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WN + j * 32 + (lane & 31);
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= M) continue;
         const float v = acc[i][j][r];
         const int64_t o = m * N + n;
@@ -161,14 +176,27 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, const float* aux,
                        int epi, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (dtype == DT_BF16) {
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     const uint16_t* a = (const uint16_t*)A;
     const uint16_t* b = (const uint16_t*)Bt;
-    switch (epi) {
-      case EPI_STORE_F32: gemm_bf16_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
-      case EPI_STORE_DT: gemm_bf16_kernel<EPI_STORE_DT><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
-      default: gemm_bf16_kernel<EPI_GATE><<<grid, 256, 0, s>>>(a, b, C, aux, M, N, K); break;
+    // large problems: 256 x 128 block tiles; small ones keep more blocks with 128 x 128
+    const bool big = M >= 4096 && N >= 512;
+#define PKM_GEMM(BMV, BNV, E)                                                                            \
+  gemm_bf16_kernel<BMV, BNV, E><<<dim3((unsigned)((N + BNV - 1) / BNV), (unsigned)((M + BMV - 1) / BMV)), 256, 0, s>>>( \
+      a, b, C, aux, M, N, K)
+    if (big) {
+      switch (epi) {
+        case EPI_STORE_F32: PKM_GEMM(256, 128, EPI_STORE_F32); break;
+        case EPI_STORE_DT: PKM_GEMM(256, 128, EPI_STORE_DT); break;
+        default: PKM_GEMM(256, 128, EPI_GATE); break;
+      }
+    } else {
+      switch (epi) {
+        case EPI_STORE_F32: PKM_GEMM(128, 128, EPI_STORE_F32); break;
+        case EPI_STORE_DT: PKM_GEMM(128, 128, EPI_STORE_DT); break;
+        default: PKM_GEMM(128, 128, EPI_GATE); break;
+      }
     }
+#undef PKM_GEMM
   } else {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     const float* a = (const float*)A;

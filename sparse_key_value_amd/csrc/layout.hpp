@@ -14,6 +14,7 @@ namespace pkm {
 struct Layout {
   size_t wqT = 0, khat = 0, w1T = 0, w2T = 0;        // create-time copies
   size_t q = 0, qhat = 0, hidx = 0, hsc = 0;          // per-forward intermediates
+  size_t gmax = 0, theta = 0, cand = 0, count = 0;    // selection scratch
   size_t idx = 0, sc = 0, w = 0, y = 0, g = 0;
   size_t total = 0;
 };
@@ -32,6 +33,7 @@ inline std::string check_config(const pkm_config* c) {
   if (c->d_query <= 0 || c->d_query % 2 != 0) return "d_query must be positive and even";
   const int d_h = c->d_query / 2;
   if (d_h != 64 && d_h != 128 && d_h != 256) return "d_query / 2 must be 64, 128 or 256";
+  if (d_h == 256 && c->dtype == PKM_F32) return "d_query / 2 = 256 is built for bf16 only (fp32: 64 or 128)";
   if (c->n_sub < 1) return "n_sub must be >= 1";
   if ((int64_t)c->n_sub * (int64_t)c->n_sub >= ((int64_t)1 << 31)) return "n_sub^2 must be < 2^31 (int32 flat index)";
   if (c->k < 1 || c->k > 32 || c->k > c->n_sub) return "k must satisfy 1 <= k <= min(n_sub, 32)";
@@ -63,6 +65,10 @@ inline Layout make_layout(const pkm_config* c) {
   }
   L.q = take(T * H * dq * 4);
   L.qhat = take(T * H * dq * eb);
+  L.gmax = take(T * H * 2 * 128 * 4);   // MAX_GROUPS group maxima per row
+  L.theta = take(T * H * 2 * 4);
+  L.cand = take(T * H * 2 * 128 * 8);   // CAND candidate keys per row
+  L.count = take(T * H * 2 * 2 * 4);   // candidates per lane half
   L.hidx = take(T * H * 2 * k * 4);
   L.hsc = take(T * H * 2 * k * 4);
   L.idx = take(T * H * k * 4);

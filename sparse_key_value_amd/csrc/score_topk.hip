@@ -1,36 +1,35 @@
-// Sub-key scoring fused with the per-half top-k.
+// Sub-key scoring and the candidates of the per-half top-k.
 //
-// For each (token t, head h, half c): s[i] = <qhat_c[t, h], khat[h, c, i]> for all
-// i < n_sub, and the k best i under (score desc, index asc) ("Memory Layers at Scale"
-// digest, product-key search: a key is two sub-keys, so each half is scored against
-// sqrt(N) sub-keys; "Memory inside the model" overview, how it works: each half is
-// compared with its own list of half-keys and the best ones are kept).
+// For each (token t, head h, half c), a "row": s[i] = <qhat_c[t, h], khat[h, c, i]> for
+// all i < n_sub ("Memory Layers at Scale" digest, product-key search: a key is two
+// sub-keys, so each half is scored against sqrt(N) sub-keys; "Memory inside the model"
+// overview, how it works: each half is compared with its own list of half-keys and the
+// best ones are kept).  The k best of every row, under (score desc, index asc), are
+// chosen from the candidates written here by the combine kernel.
 //
 // Design for gfx950:
-//  * The scores are a dense contraction (tokens x sub-keys x d_h) and run on the matrix
-//    cores: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32).  The MFMA
-//    computes S^T = Khat * Qhat^T, so each lane's 16 accumulators belong to ONE token
-//    (column = lane % 32) and 16 sub-keys; the selection threshold is one register.
-//  * A block is 4 waves x 32 tokens for one (h, c).  Chunks of 32 sub-keys are staged
-//    through LDS (XOR-swizzled 16-byte units, so the MFMA operand reads are free of
-//    bank conflicts without padding) and shared by the 4 waves; the next chunk is
-//    prefetched into registers while the current one is scored.  80 KiB of LDS per
-//    block lets two blocks share a CU, so one block's selection work overlaps the
-//    other's matrix work.
-//  * The scores are never written out.  Selection takes two passes over the sub-keys.
-//    Pass 1 keeps, per token, the maximum score of each group of sub-keys (at most 128
-//    groups); the k-th largest of these maxima is reached by at least k sub-keys, so it
-//    bounds the token's k-th best score from below (found bit by bit with wave
-//    ballots).  Pass 2 recomputes the same scores and keeps only those at or above the
-//    bound: with random-like data about 37 of 4,096 per token.
-//  * Each token owns 64 LDS slots of 64-bit keys: pending keys, and after a merge a
-//    sorted list in slots 0..31 with pending keys in 32..63.  After a merge a score
-//    must beat the k-th best score strictly (every later sub-key has a higher index,
-//    so a tie never enters).  A merge is done by the whole wave: each lane ranks its
-//    key by comparing it with every key of the token (LDS broadcast reads, no
-//    dependent shuffle chain) and ds_permute moves every key to the lane of its rank.
+//  * The scores are a dense contraction (tokens x sub-keys x d_h) on the matrix cores:
+//    v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32), computing
+//    S^T = Khat * Qhat^T so that each lane's 16 accumulators belong to ONE token.  A wave
+//    owns 64 tokens (two 32-token MFMA columns), so every 16-byte LDS operand read feeds
+//    two MFMAs.  A block is 4 waves = 256 tokens of one (h, c); 32-sub-key chunks are
+//    staged through a double-buffered, XOR-swizzled LDS tile shared by the 4 waves, the
+//    next chunk being prefetched into registers.  Nothing else lives in LDS.
+//  * The scores are never written out; selection takes two passes:
+//      pass 1 writes, per row, the maximum score of every group of G consecutive
+//             sub-keys (G in {8, 16, 32, 64, ...}, the smallest giving <= 128 groups);
+//      theta  picks per row the k-th largest group maximum: at least k sub-keys reach
+//             it, so it bounds the row's k-th best score from below (found bit by bit
+//             with wave ballots);
+//      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring
+//             above the bound, and of those scoring exactly the bound the first k each
+//             lane sees (lowest indices first), as 64-bit keys to the row's candidate
+//             list (CAND slots, half per lane).  With random-like data about 37 of
+//             4,096 per row.
+//    A lane's count may exceed its CAND / 2 slots (structured data); that row is then
+//    scored exhaustively by the overflow kernel before the combine kernel reads it.
 //  * Keys are 64-bit (ordered score << 32 | ~index): ties resolve to the lower index
-//    and every key is distinct.  Empty slots carry their lane number, below any key.
+//    and every key is distinct.
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
 //    dealt round-robin to the 8 XCDs, so with 2H dividing 8 each XCD only ever reads
 //    one pair's sub-keys, which stay resident in that XCD's L2.
@@ -40,12 +39,10 @@ namespace pkm {
 
 namespace {
 
-constexpr int TPW = 32;         // tokens per wave
+constexpr int TPW = 64;         // tokens per wave (two MFMA columns of 32)
 constexpr int NWAVES = 4;
 constexpr int TPB = TPW * NWAVES;
 constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
-constexpr int SLOTS = 64;       // keys per token: 32 list + 32 pending
-constexpr int LIST = 32;
 
 template <typename DT, int DH>
 struct Mma;
@@ -82,101 +79,194 @@ struct Mma<float, DH> {
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
 };
 
-__device__ __forceinline__ uint64_t permute_u64(uint64_t v, int dst_lane) {
-  const int addr = dst_lane << 2;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Largest float strictly below x (finite x): "s > below(x)" is "s >= x".
-__device__ __forceinline__ float float_below(float x) {
-  const uint32_t b = __float_as_uint(x);
-  if ((b & 0x7FFFFFFFu) == 0) return __uint_as_float(0x80000001u);
-  return __uint_as_float((b & 0x80000000u) ? b + 1 : b - 1);
-}
-
-// Per-token selection state, held by the two lanes that own the token.
-struct TokState {
-  int nl;      // keys in the sorted list (slots 0..nl-1); 0 until the first merge
-  int np;      // pending keys, from slot pbase(): all 64 slots are pending until a list exists
-  float thr;   // a score must be > thr to be pending
-  __device__ int pbase() const { return nl ? LIST : 0; }
-  __device__ int cap() const { return nl ? SLOTS - LIST : SLOTS; }
-};
-
-// Merge token jj's list and pending keys with the whole wave, leaving the best
-// min(32, nl + np) keys sorted in slots 0.. .  Each lane ranks its key by comparing it
-// with every real key of the token (LDS broadcast reads, no cross-lane dependency
-// chain); ds_permute then sends every key to the lane of its rank.  Keys are distinct,
-// so the ranks of the real keys are 0 .. nl+np-1.
-__device__ __forceinline__ void merge_token(uint64_t* cand_wave, int jj, int lane, int tok, int k, TokState& st) {
-  __builtin_amdgcn_wave_barrier();
-  const int nl = __builtin_amdgcn_readlane(st.nl, jj);
-  const int np = __builtin_amdgcn_readlane(st.np, jj);
-  const int pb = nl ? LIST : 0;
-  uint64_t* b = cand_wave + jj * SLOTS;
-  const bool real = lane < nl || (lane >= pb && lane - pb < np);
-  const uint64_t key = real ? b[lane] : 0ull;
-  int rank = 0;
-  for (int i = 0; i < nl; ++i) rank += b[i] > key ? 1 : 0;
-  for (int i = 0; i < np; ++i) rank += b[pb + i] > key ? 1 : 0;
-  const uint64_t sorted = permute_u64(key, real ? rank : SLOTS - 1);
-  const int total = nl + np;
-  __builtin_amdgcn_wave_barrier();
-  if (lane < LIST && lane < total) b[lane] = sorted;
-  __builtin_amdgcn_wave_barrier();
-  const int nn = total < LIST ? total : LIST;
-  const uint32_t kth_ord = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(sorted >> 32), k - 1);
-  if (tok == jj) {
-    st.nl = nn;
-    st.np = 0;
-    // once k keys are listed, a later sub-key (higher index) must beat the k-th score strictly
-    if (nn >= k) st.thr = score_of_ord(kth_ord);
-  }
-}
+__device__ __forceinline__ float load_elem_f32(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem_f32(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 
 __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_base + 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-template <bool FULL>
-__device__ __forceinline__ uint32_t survivors(const f32x16& acc, int sub_base, int n, int hi, float thr) {
-  uint32_t m = 0;
+// The shared MFMA sweep over all sub-keys of one pair for the block's 256 tokens.
+// `on_tile(ch, acc)` receives, per 32-sub-key chunk, the scores of this lane's two
+// tokens (acc[0]: token lane%32 of the wave, acc[1]: token 32 + lane%32).
+template <typename DT, int DH, typename F>
+__device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t T, int H, int n,
+                                      uint8_t* ks, F&& on_tile) {
+  using M = Mma<DT, DH>;
+  constexpr int RB = DH * M::EB;          // bytes per sub-key row
+  constexpr int U16 = RB / 16;            // 16-byte units per row
+
+  const int pairs = 2 * H;
+  const int pair = blockIdx.x % pairs;
+  const int64_t tile = blockIdx.x / pairs;
+  const int h = pair >> 1, c = pair & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+
+  typename M::frag qf[2][M::NK];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) m |= ((FULL || sub_of(sub_base, r, hi) < n) && acc[r] > thr ? 1u : 0u) << r;
+  for (int g = 0; g < 2; ++g) {
+    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    const DT* qrow = qhat + ((t * H + h) * 2 + c) * (int64_t)DH;
+#pragma unroll
+    for (int kk = 0; kk < M::NK; ++kk) qf[g][kk] = t < T ? M::load_q(qrow, kk, hi) : typename M::frag{};
+  }
+
+  const uint8_t* kbase = (const uint8_t*)(khat + (size_t)pair * n * DH);
+  const int nch = (n + CHUNK - 1) / CHUNK;
+  // Chunk ch goes to LDS buffer b by direct global->LDS loads: wave wv's i-th load fills
+  // the 64 consecutive 16-byte units starting at unit (wv * DPW + i) * 64, and each lane
+  // fetches the global unit that belongs at its LDS unit under the XOR swizzle.  Rows past
+  // n_sub load row 0 instead (in bounds); their scores are masked by every consumer.
+  constexpr int DPW = CHUNK * U16 / 64 / NWAVES;  // loads per wave per chunk
+  static_assert(DPW >= 1 && CHUNK * U16 % (64 * NWAVES) == 0, "chunk must split evenly over the waves");
+  auto fetch = [&](int ch, int buf) {
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int p = (wv * DPW + i) * 64 + lane;          // LDS unit this lane fills
+      const int row = p / U16, col = (p % U16) ^ (row % U16);
+      int sub = ch * CHUNK + row;
+      sub = sub < n ? sub : 0;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + (size_t)sub * RB + col * 16),
+          (void __attribute__((address_space(3)))*)(ks + buf * CHUNK * RB + (wv * DPW + i) * 64 * 16), 16, 0, 0);
+    }
+  };
+  const int swz = (lane & 31) % U16;
+
+  fetch(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    // the other buffer was last read in the previous chunk, before the barrier that ended it
+    if (ch + 1 < nch) fetch(ch + 1, buf ^ 1);
+    const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < M::NK; ++kk) {
+      const typename M::frag a = M::lds_k(myrow, swz, kk, hi);
+      acc[0] = M::mma(a, qf[0][kk], acc[0]);
+      acc[1] = M::mma(a, qf[1][kk], acc[1]);
+    }
+    on_tile(ch, acc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+}
+
+// Max over the 16 scores of one lane, or only over those of sub-keys < n.
+template <bool FULL>
+__device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, int hi, int r0, int r1) {
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int r = r0; r < r1; ++r) m = (FULL || sub_of(sub_base, r, hi) < n) ? fmaxf(m, a[r]) : m;
   return m;
 }
 
-// Pass 2: offer one 32-sub-key tile (this lane: 16 sub-keys of token `tok`).
-template <bool FULL>
-__device__ __forceinline__ void offer_tile(const f32x16& acc, int sub_base, int n, int lane, int tok, int hi, int k,
-                                           uint64_t* cand_wave, TokState& st) {
-  uint32_t m = survivors<FULL>(acc, sub_base, n, hi, st.thr);
-  if (__ballot(m != 0) == 0) return;
-  int c = __popc(m);
-  int co = __shfl_xor(c, 32, WAVE);
-  uint64_t bal = __ballot(st.np + c + co > st.cap()) & 0xFFFFFFFFull;
-  if (bal) {
-    while (bal) {
-      const int jj = __builtin_ctzll(bal);
-      bal &= bal - 1;
-      merge_token(cand_wave, jj, lane, tok, k, st);
-    }
-    m = survivors<FULL>(acc, sub_base, n, hi, st.thr);
-    c = __popc(m);
-    co = __shfl_xor(c, 32, WAVE);
-  }
-  int off = st.pbase() + st.np + (hi ? co : 0);
-  uint64_t* b = cand_wave + tok * SLOTS;
+// Pass 1: per row, the maximum of every group of G = 8 << GS sub-keys.  The maxima of
+// 8 consecutive groups are collected in registers (a shift register) and written as
+// two 16-byte stores, so that few stores are in flight when a chunk waits for its loads.
+template <typename DT, int DH, int GS>
+__global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+                                                       int64_t T, int H, int n, float* __restrict__ gmax) {
+  constexpr int RB = DH * Mma<DT, DH>::EB;
+  constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
+  constexpr int SPAN = GS <= 2 ? 1 : (1 << (GS - 2)); // chunks per group when a group spans chunks
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * CHUNK * RB];
+  const int pairs = 2 * H;
+  const int pair = blockIdx.x % pairs;
+  const int64_t tile = blockIdx.x / pairs;
+  const int h = pair >> 1, c = pair & 1;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5;
+  float run[2] = {-__builtin_inff(), -__builtin_inff()};
+  float buf[2][8];
+  int nbuf = 0;  // groups in buf (wave-uniform)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (m & (1u << r)) b[off++] = make_key(acc[r], (uint32_t)sub_of(sub_base, r, hi));
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) buf[g][j] = 0.f;
+  float* gm[2];
+  bool live[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    live[g] = hi == 0 && t < T;
+    gm[g] = gmax + ((t * H + h) * 2 + c) * (int64_t)MAX_GROUPS;
   }
-  st.np += c + co;
+  int done = 0;  // groups written
+  auto push = [&](const float* m) {  // one finished group per token of this lane
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int j = 0; j < 7; ++j) buf[g][j] = buf[g][j + 1];
+      buf[g][7] = m[g];
+    }
+    // shift register: the newest is buf[7]; after 8 pushes buf[0] is the oldest
+    if (++nbuf == 8) {
+      // reorder: oldest first at gm[done]
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (!live[g]) continue;
+        *(f32x4*)(gm[g] + done) = f32x4{buf[g][0], buf[g][1], buf[g][2], buf[g][3]};
+        *(f32x4*)(gm[g] + done + 4) = f32x4{buf[g][4], buf[g][5], buf[g][6], buf[g][7]};
+      }
+      done += 8;
+      nbuf = 0;
+    }
+  };
+  sweep<DT, DH>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+    const bool full = (ch + 1) * CHUNK <= n;
+    float mg[2][GPC];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // a group of 8 << GS sub-keys inside the chunk covers rows [4j, 4j + 4 << GS) of both lanes
+#pragma unroll
+      for (int j = 0; j < GPC; ++j) {
+        constexpr int RW = GS <= 2 ? (4 << GS) : 16;
+        const float m = full ? lane_max<true>(acc[g], ch * CHUNK, n, hi, j * RW, j * RW + RW)
+                             : lane_max<false>(acc[g], ch * CHUNK, n, hi, j * RW, j * RW + RW);
+        mg[g][j] = fmaxf(m, __shfl_xor(m, 32, WAVE));
+      }
+    }
+    if (GS <= 2) {
+#pragma unroll
+      for (int j = 0; j < GPC; ++j) {
+        if (ch * CHUNK + j * (8 << GS) < n) {
+          const float m[2] = {mg[0][j], mg[1][j]};
+          push(m);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) run[g] = fmaxf(run[g], mg[g][0]);
+      if (((ch + 1) & (SPAN - 1)) == 0 || (ch + 1) * CHUNK >= n) {
+        push(run);
+        run[0] = run[1] = -__builtin_inff();
+      }
+    }
+  });
+  // the last < 8 groups: buf[8 - nbuf .. 7] hold groups done .. done + nbuf - 1
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (!live[g]) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nbuf) gm[g][done + i] = buf[g][8 - nbuf + i];
+  }
 }
 
-// k-th largest of the values v0, v1 held by all 64 lanes (ordered-float bits; 0 = absent):
-// the largest x with #{v >= x} >= k, found bit by bit from the top with wave ballots.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v0, uint32_t v1, int k) {
+// theta: per row the k-th largest of its group maxima (-inf if there are fewer than k).
+__global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gmax, int64_t rows, int ngroups, int k,
+                                                    float* __restrict__ theta) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  if (ngroups < k) {
+    if (lane == 0) theta[row] = -__builtin_inff();
+    return;
+  }
+  const float* gm = gmax + row * MAX_GROUPS;
+  const uint32_t v0 = lane < ngroups ? ord_score(gm[lane]) : 0u;
+  const uint32_t v1 = lane + 64 < ngroups ? ord_score(gm[lane + 64]) : 0u;
+  // largest x with #{v >= x} >= k, bit by bit from the top
   uint32_t prefix = 0;
 #pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
@@ -184,165 +274,176 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v0, uint32_t v1, i
     const int cnt = __popcll(__ballot(v0 >= cand)) + __popcll(__ballot(v1 >= cand));
     if (cnt >= k) prefix = cand;
   }
-  return prefix;
+  if (lane == 0) theta[row] = score_of_ord(prefix);
 }
 
+// Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
+// theta).  Each of a token's two lanes owns half of the row's CAND slots and counts its
+// own candidates, so the common case (no survivor) costs one compare per score and a
+// skipped branch.
 template <typename DT, int DH>
-__global__ void __launch_bounds__(256, 2) score_topk_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
-                                                            int64_t T, int H, int n, int k,
-                                                            int32_t* __restrict__ half_idx,
-                                                            float* __restrict__ half_score) {
-  using M = Mma<DT, DH>;
-  constexpr int RB = DH * M::EB;          // bytes per sub-key row
-  constexpr int U16 = RB / 16;            // 16-byte units per row
-  constexpr int UPT = CHUNK * U16 / 256;  // units per thread per chunk
-  constexpr int MAXG = 128;               // group maxima per token kept by pass 1
-  static_assert(UPT >= 1 && CHUNK * U16 % 256 == 0, "chunk must split evenly over 256 threads");
-  static_assert(MAXG * 4 == SLOTS * 8, "pass-1 maxima reuse the candidate slots");
-
-  __shared__ __attribute__((aligned(16))) uint8_t ks[CHUNK * RB];
-  __shared__ uint64_t cand[TPB * SLOTS];
-
+__global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+                                                       int64_t T, int H, int n, int k, const float* __restrict__ theta,
+                                                       uint64_t* __restrict__ cand, int32_t* __restrict__ count) {
+  constexpr int RB = DH * Mma<DT, DH>::EB;
+  constexpr int HALF = CAND / 2;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * CHUNK * RB];
   const int pairs = 2 * H;
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tok = lane & 31, hi = lane >> 5;
-  const int64_t t = tile * TPB + wv * TPW + tok;
-
-  // this lane's query fragment (token t, half c, head h); zero past the last token
-  typename M::frag qf[M::NK];
-  {
-    const DT* qrow = qhat + ((t * H + h) * 2 + c) * (int64_t)DH;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5;
+  float thr[2];
+  int cnt[2] = {0, 0}, eq[2] = {0, 0};
+  uint64_t* dst[2];
+  int64_t row[2];
 #pragma unroll
-    for (int kk = 0; kk < M::NK; ++kk) {
-      if (t < T) qf[kk] = M::load_q(qrow, kk, hi);
-      else qf[kk] = typename M::frag{};
-    }
+  for (int g = 0; g < 2; ++g) {
+    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    row[g] = (t * H + h) * 2 + c;
+    thr[g] = t < T ? theta[row[g]] : __builtin_inff();
+    dst[g] = cand + row[g] * CAND + hi * HALF;
   }
-
-  const uint8_t* kbase = (const uint8_t*)(khat + (size_t)pair * n * DH);
-  const int nch = (n + CHUNK - 1) / CHUNK;
-  u32x4 pre[UPT];
-  auto fetch = [&](int ch) {
+  sweep<DT, DH>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+    const bool full = (ch + 1) * CHUNK <= n;
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * 256;
-      const int row = u / U16, col = u - row * U16;
-      const int sub = ch * CHUNK + row;
-      pre[i] = sub < n ? *(const u32x4*)(kbase + (size_t)sub * RB + col * 16) : u32x4{0, 0, 0, 0};
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float s = acc[g][r];
+        if (s >= thr[g]) {
+          const int sub = sub_of(ch * CHUNK, r, hi);
+          bool take = full || sub < n;
+          if (take && s == thr[g]) take = eq[g]++ < k;  // exact ties with the bound: the first k suffice
+          if (take) {
+            if (cnt[g] < HALF) dst[g][cnt[g]] = make_key(s, (uint32_t)sub);
+            ++cnt[g];
+          }
+        }
+      }
     }
-  };
-  const int swz_r = (lane & 31) % U16;
-  const uint8_t* myrow = ks + (lane & 31) * RB;
-  // stage chunk ch into LDS (the caller has prefetched it into `pre`), prefetch ch + 1, score it
-  auto score_chunk = [&](int ch) {
-    __syncthreads();
+  });
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = tid + i * 256;
-      const int row = u / U16, col = u - row * U16;
-      *(u32x4*)(ks + row * RB + ((col ^ (row % U16)) << 4)) = pre[i];
-    }
-    __syncthreads();
-    if (ch + 1 < nch) fetch(ch + 1);
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < M::NK; ++kk) acc = M::mma(M::lds_k(myrow, swz_r, kk, hi), qf[kk], acc);
-    return acc;
-  };
-
-  uint64_t* cand_wave = cand + wv * TPW * SLOTS;
-  float* gmax_wave = (float*)cand_wave;  // pass 1: [token][MAXG] group maxima
-
-  // ---- pass 1: the maximum score of each group of sub-keys, per token ------------------
-  // The k-th largest of these maxima is a score that at least k sub-keys reach, so it
-  // bounds the token's k-th best score from below.
-  const int gsz = (nch + MAXG - 1) / MAXG;   // chunks per group
-  const int ngroups = (nch + gsz - 1) / gsz;
-  fetch(0);
-  float gm = -__builtin_inff();
-  for (int ch = 0; ch < nch; ++ch) {
-    const f32x16 acc = score_chunk(ch);
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m = sub_of(ch * CHUNK, r, hi) < n ? fmaxf(m, acc[r]) : m;
-    m = fmaxf(m, __shfl_xor(m, 32, WAVE));
-    gm = fmaxf(gm, m);
-    if ((ch + 1) % gsz == 0 || ch + 1 == nch) {
-      if (hi == 0) gmax_wave[tok * MAXG + ch / gsz] = gm;
-      gm = -__builtin_inff();
-    }
+  for (int g = 0; g < 2; ++g) {
+    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    if (t < T) count[row[g] * 2 + hi] = cnt[g];
   }
-  __builtin_amdgcn_wave_barrier();
-  TokState st;
-  st.nl = 0;
-  st.np = 0;
-  st.thr = -__builtin_inff();
-  if (ngroups >= k) {
-    for (int jj = 0; jj < TPW; ++jj) {
-      const uint32_t v0 = lane < ngroups ? ord_score(gmax_wave[jj * MAXG + lane]) : 0u;
-      const uint32_t v1 = lane + 64 < ngroups ? ord_score(gmax_wave[jj * MAXG + lane + 64]) : 0u;
-      const uint32_t kth = wave_kth_largest(v0, v1, k);
-      if (tok == jj) st.thr = float_below(score_of_ord(kth));
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
+}
 
-  // ---- pass 2: collect the sub-keys at or above the bound, keep the exact top-k -------
-  fetch(0);
-  for (int ch = 0; ch < nch; ++ch) {
-    const f32x16 acc = score_chunk(ch);
-    if ((ch + 1) * CHUNK <= n) offer_tile<true>(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
-    else offer_tile<false>(acc, ch * CHUNK, n, lane, tok, hi, k, cand_wave, st);
-  }
-
-  // final merge of every token of this wave, then write its top-k
-  for (int jj = 0; jj < TPW; ++jj) {
-    merge_token(cand_wave, jj, lane, tok, k, st);
-    const int64_t tj = tile * TPB + wv * TPW + jj;
-    if (tj < T && lane < k) {
-      const uint64_t key = cand_wave[jj * SLOTS + lane];
-      const int64_t o = ((tj * H + h) * 2 + c) * (int64_t)k + lane;
-      half_idx[o] = (int32_t)key_index(key);
-      half_score[o] = key_score(key);
+// Rows whose candidates overflowed (more than CAND / 2 in either lane's half: structured
+// data with many sub-keys above the bound) are scored again here, exhaustively, in plain fp32 FMAs: each lane keeps the
+// best 32 keys of its share of the sub-keys in registers, the 64 lane lists are merged
+// by k rounds of a wave-wide maximum, and the row's candidate list becomes exactly its
+// top-k.  A persistent grid scans the counts; with no overflow it only reads them.
+template <typename DT, int DH>
+__global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+                                                       int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
+                                                       int32_t* __restrict__ count) {
+  __shared__ float qs[4][DH];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + wv) * 64; base < rows2; base += waves * 64) {
+    const int64_t r = base + lane;
+    uint64_t over = __ballot(r < rows2 && (count[2 * r] > CAND / 2 || count[2 * r + 1] > CAND / 2));
+    while (over) {
+      const int64_t r2 = base + __builtin_ctzll(over);
+      over &= over - 1;
+      const int pair = (int)(r2 % (2 * H));
+      const DT* q = qhat + r2 * DH;
+      for (int d = lane; d < DH; d += 64) qs[wv][d] = load_elem_f32(q, d);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      uint64_t L[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) L[j] = 0ull;
+      const DT* kb = khat + (size_t)pair * n * DH;
+      for (int i = lane; i < n; i += 64) {
+        float s = 0.f;
+        for (int d = 0; d < DH; ++d) s = __builtin_fmaf(qs[wv][d], load_elem_f32(kb + (size_t)i * DH, d), s);
+        uint64_t key = make_key(s, (uint32_t)i);
+        if (key > L[31]) {
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            const uint64_t lo = key > L[j] ? L[j] : key;
+            L[j] = key > L[j] ? key : L[j];
+            key = lo;
+          }
+        }
+      }
+      for (int j = 0; j < k; ++j) {
+        const uint64_t win = wave_max_u64(L[0]);
+        if (L[0] == win) {
+#pragma unroll
+          for (int i = 0; i < 31; ++i) L[i] = L[i + 1];
+          L[31] = 0ull;
+        }
+        if (lane == 0) cand[r2 * CAND + j] = win;
+      }
+      if (lane == 0) {
+        count[2 * r2] = k;
+        count[2 * r2 + 1] = 0;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
 template <typename DT, int DH>
-hipError_t launch_st(const void* qhat, const void* khat, int64_t T, int H, int n, int k, int32_t* hi, float* hs,
-                     hipStream_t s) {
+hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax, float* theta,
+                         uint64_t* cand, int32_t* count, hipStream_t s) {
   const int64_t tiles = (T + TPB - 1) / TPB;
-  const int64_t blocks = tiles * 2 * H;
-  score_topk_kernel<DT, DH><<<dim3((unsigned)blocks), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, hi, hs);
+  const dim3 grid((unsigned)(tiles * 2 * H));
+  int gshift = 0;
+  while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
+  const int ngroups = (n + (8 << gshift) - 1) >> (3 + gshift);
+  hipError_t e;
+#define PKM_P1(G) pass1_kernel<DT, DH, G><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
+  switch (gshift) {
+    case 0: PKM_P1(0); break;
+    case 1: PKM_P1(1); break;
+    case 2: PKM_P1(2); break;
+    case 3: PKM_P1(3); break;
+    case 4: PKM_P1(4); break;
+    case 5: PKM_P1(5); break;
+    default: return hipErrorInvalidValue;  // n_sub > 8192 * 4: not built
+  }
+#undef PKM_P1
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = T * H * 2;
+  theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  pass2_kernel<DT, DH><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t scan_waves = (rows + 63) / 64;
+  const int64_t ob = (scan_waves + 3) / 4 < 1024 ? (scan_waves + 3) / 4 : 1024;
+  overflow_kernel<DT, DH><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand, count);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool score_topk_supported(int d_h, int dtype) {
-  (void)dtype;
-  return d_h == 64 || d_h == 128 || d_h == 256;
+  return d_h == 64 || d_h == 128 || (d_h == 256 && dtype == DT_BF16);
 }
 
-hipError_t launch_score_topk(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k, int dtype,
-                             int32_t* half_idx, float* half_score, hipStream_t s) {
+hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k,
+                                   int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
+                                   hipStream_t s) {
   if (T == 0) return hipSuccess;
+#define PKM_PASSES(DT, DHV) return launch_passes<DT, DHV>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s)
   if (dtype == DT_BF16) {
     switch (d_h) {
-      case 64: return launch_st<uint16_t, 64>(qhat, khat, T, H, n, k, half_idx, half_score, s);
-      case 128: return launch_st<uint16_t, 128>(qhat, khat, T, H, n, k, half_idx, half_score, s);
-      case 256: return launch_st<uint16_t, 256>(qhat, khat, T, H, n, k, half_idx, half_score, s);
+      case 64: PKM_PASSES(uint16_t, 64);
+      case 128: PKM_PASSES(uint16_t, 128);
+      case 256: PKM_PASSES(uint16_t, 256);
     }
   } else {
     switch (d_h) {
-      case 64: return launch_st<float, 64>(qhat, khat, T, H, n, k, half_idx, half_score, s);
-      case 128: return launch_st<float, 128>(qhat, khat, T, H, n, k, half_idx, half_score, s);
-      case 256: return launch_st<float, 256>(qhat, khat, T, H, n, k, half_idx, half_score, s);
+      case 64: PKM_PASSES(float, 64);
+      case 128: PKM_PASSES(float, 128);
     }
   }
+#undef PKM_PASSES
   return hipErrorInvalidValue;
 }
 

@@ -8,7 +8,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkm_synth.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_key_value_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_key_value_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _lib.synth_fill_values.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64, _vp]

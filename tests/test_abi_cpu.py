@@ -49,7 +49,8 @@ def test_workspace_size_matches_layout(P):
     a = lambda v: (v + 255) // 256 * 256
     T, H, dq, dm, dv, n, k = 16384, 4, 512, 2048, 2048, 4096, 32
     want = (a(H * dq * dm * 2) + a(H * 2 * n * dq // 2 * 2) + a(dv * dm * 2) + a(dm * dv * 2) + a(T * H * dq * 4) +
-            a(T * H * dq * 2) + 2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 4) + a(T * dv * 2))
+            a(T * H * dq * 2) + a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * 128 * 8) + a(T * H * 2 * 2 * 4) +
+            2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 4) + a(T * dv * 2))
     assert P.pkm_workspace_size(c) == want
     # without the gate there is no W1/W2 copy and no y/g buffer
     assert P.pkm_workspace_size(_cfg(P, memory_plus=0)) < want

@@ -365,3 +365,66 @@ def test_combine_rounding_tie_takes_exhaustive_path():
                                 idx.cpu().numpy())
     PAR.check_lists(idx.cpu().numpy(), sel["idx"], sel["score"], ch, "rounding-tie case")
     pk.close()
+
+
+@pytest.mark.parametrize("memory_plus", [False, True])
+def test_pipelined_chunks_match_single_stream(memory_plus):
+    """Pipelining over token chunks (two internal streams) gives bitwise the same forward."""
+    import sparse_key_value_amd as P
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name="chunks", n_sub=128, T=1000, d_v=256, d_model=256,
+                                        memory_plus=memory_plus)
+    say(f"pipelined chunks memory_plus={memory_plus}")
+    wl = _G().Workload(cfg, seed=12)
+    res = {}
+    for chunks in (1, 3, 8):
+        P.pkm_set_pipeline_chunks(wl.pkm.handle, chunks)
+        out = torch.empty((wl.T, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda")
+        P.pkm_forward(wl.pkm.handle, wl.dev["x"], wl.T, out, idx, w)
+        torch.cuda.synchronize()
+        res[chunks] = (out.view(torch.int16).cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy())
+    for chunks in (3, 8):
+        for a, b in zip(res[1], res[chunks]):
+            np.testing.assert_array_equal(a, b)
+    P.pkm_set_pipeline_chunks(wl.pkm.handle, 0)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+
+
+def test_candidate_overflow_takes_exhaustive_path():
+    """Scores rising with the sub-key index make the group-maximum bound loose.
+
+    With s_i = i over 2,048 sub-keys in groups of 16, the 32nd largest group maximum is
+    1551, so about 500 sub-keys reach the bound and overflow the candidate list; that row
+    is then scored exhaustively.  Every score is an exact small integer, so the result
+    must equal the oracle's exactly: per-half lists 2047..2016, final cells by sum.
+    """
+    import sparse_key_value_amd as P
+    n, dh, k = 2048, 64, 32
+    K = np.zeros((1, 2, n, dh), dtype=np.float32)
+    K[0, 0, :, 0] = np.arange(n, dtype=np.float32)
+    K[0, 1, :, 1] = np.arange(n, dtype=np.float32)[::-1] * 0.5   # half 1: best at low indices
+    wq = torch.zeros((64, 128), dtype=torch.float32, device="cuda")
+    vals = torch.zeros((n * n, 4), dtype=torch.float32, device="cuda")
+    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=128, n_sub=n, k=k, d_value=4, dtype="f32", qk_norm=0,
+                            memory_plus=0, max_tokens=8, W_q=wq, subkeys=torch.from_numpy(K).cuda(), values=vals)
+    q = np.zeros((3, 1, 2, dh), dtype=np.float32)
+    q[:, 0, 0, 0] = [1.0, 2.0, 0.5]
+    q[:, 0, 1, 1] = [1.0, 1.0, 3.0]
+    T = q.shape[0]
+    hi_ = torch.empty((T, 1, 2, k), dtype=torch.int32, device="cuda")
+    hs_ = torch.empty((T, 1, 2, k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, 1, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+    w = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), T, hi_, hs_, idx, sc, w)
+    torch.cuda.synchronize()
+    q64 = q.astype(np.float64).reshape(T, 1, 2 * dh)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64), k)
+    assert (hi_.cpu().numpy()[:, 0, 0] == np.arange(n - 1, n - 1 - k, -1)).all()
+    np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"])
+    np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"])
+    np.testing.assert_allclose(sc.cpu().numpy(), sel["score"], rtol=0, atol=0)
+    pk.close()
