@@ -16,43 +16,56 @@ namespace pkm {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): 144 bytes, conflict-free 16-byte reads
-
 // Block tile BM x BN, four waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) made of
-// 32 x 32 MFMA tiles.  A and B tiles are staged through padded LDS; the next K-tile is
-// prefetched into registers while the current one is multiplied.
+// 32 x 32 MFMA tiles.  A and B K-tiles reach LDS by direct global->LDS loads
+// (global_load_lds_dwordx4: each wave instruction fills 64 consecutive 16-byte LDS
+// units) into a double buffer of padded rows (9 units of 16 bytes per 8 data units, so
+// the MFMA operand reads are free of bank conflicts); a lane whose unit is padding
+// loads a harmless in-bounds address.  One barrier per K-tile.
 template <int BM, int BN, int EPI>
 __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ Bt, void* __restrict__ C,
                                                            const float* __restrict__ aux, int64_t M, int N, int K) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // MFMA tiles per wave
-  constexpr int AU = BM * (BK / 8) / 256;      // 16-byte units of A per thread
-  constexpr int BU = BN * (BK / 8) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  constexpr int BKT = 32;                      // K per LDS tile
+  constexpr int RU = BKT / 8 + 1;              // 16-byte units per padded LDS row (4 data + 1 pad)
+  constexpr int AUN = BM * RU, BUN = BN * RU;  // units per tile
+  constexpr int AL = (AUN + 255) / 256, BL = (BUN + 255) / 256;  // loads per wave (4 waves x 64 lanes)
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][AL * 256 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BL * 256 * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
 
-  u32x4 pa[AU], pb[BU];
-  auto fetch = [&](int k0) {
+  // LDS unit p of a tile holds row p / RU, 16-byte column p % RU (column 4 = padding,
+  // filled with a copy of column 3 and never read).  Rows past M / N read row 0 instead:
+  // their products only reach outputs that are never stored.  K is a multiple of 32
+  // (checked when the handle is created), so every column is real.
+  auto fetch = [&](int k0, int buf) {
 #pragma unroll
-    for (int i = 0; i < AU; ++i) {
-      const int u = tid + i * 256;
-      const int r = u >> 3, kc = k0 + (u & 7) * 8;
-      const int64_t gm = m0 + r;
-      pa[i] = (gm < M && kc < K) ? *(const u32x4*)(A + gm * K + kc) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < AL; ++i) {
+      const int p = (wv * AL + i) * 64 + lane;
+      int r = p / RU, cu = p - r * RU;
+      int64_t gm = m0 + r;
+      gm = (gm < M && p < AUN) ? gm : 0;
+      cu = cu < 4 ? cu : 3;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(A + gm * K + k0 + cu * 8),
+          (void __attribute__((address_space(3)))*)(As[buf] + (wv * AL + i) * 64 * 16), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < BU; ++i) {
-      const int u = tid + i * 256;
-      const int r = u >> 3, kc = k0 + (u & 7) * 8;
-      const int gn = n0 + r;
-      pb[i] = (gn < N && kc < K) ? *(const u32x4*)(Bt + (int64_t)gn * K + kc) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < BL; ++i) {
+      const int p = (wv * BL + i) * 64 + lane;
+      int r = p / RU, cu = p - r * RU;
+      int gn = n0 + r;
+      gn = (gn < N && p < BUN) ? gn : 0;
+      cu = cu < 4 ? cu : 3;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(Bt + (int64_t)gn * K + k0 + cu * 8),
+          (void __attribute__((address_space(3)))*)(Bs[buf] + (wv * BL + i) * 64 * 16), 16, 0, 0);
     }
   };
 
@@ -62,35 +75,33 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
+  const int nk = K / BKT;
+  fetch(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // the other buffer was last read in the previous K-tile, before the barrier that ended it
+    if (kt + 1 < nk) fetch((kt + 1) * BKT, buf ^ 1);
+    const uint8_t* as = As[buf];
+    const uint8_t* bs = Bs[buf];
 #pragma unroll
-    for (int i = 0; i < AU; ++i) {
-      const int u = tid + i * 256;
-      *(u32x4*)(As + (u >> 3) * LDK + (u & 7) * 8) = pa[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BU; ++i) {
-      const int u = tid + i * 256;
-      *(u32x4*)(Bs + (u >> 3) * LDK + (u & 7) * 8) = pb[i];
-    }
-    __syncthreads();
-    if (k0 + BK < K) fetch(k0 + BK);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < BKT / 16; ++kk) {
       bf16x8 af[TM], bfr[TN];
+      const int cu = kk * 2 + (lane >> 5);  // 16-byte column of this lane's 8 k-values
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *(const bf16x8*)(As + (wm * WM + i * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+        af[i] = *(const bf16x8*)(as + ((wm * WM + i * 32 + (lane & 31)) * RU + cu) * 16);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const bf16x8*)(Bs + (wn * WN + j * 32 + (lane & 31)) * LDK + kk * 16 + (lane >> 5) * 8);
+        bfr[j] = *(const bf16x8*)(bs + ((wn * WN + j * 32 + (lane & 31)) * RU + cu) * 16);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
 
   // epilogue: lane holds column n = .. + lane % 32 and 16 rows of each 32 x 32 tile

@@ -29,6 +29,9 @@ inline std::string check_config(const pkm_config* c) {
   const int vec = 16 / eb;  // elements per 16-byte access
   if (c->d_model <= 0 || c->d_model % vec != 0)
     return "d_model must be positive and a multiple of " + std::to_string(vec) + " (16-byte rows)";
+  if (c->dtype == PKM_BF16 && c->d_model % 32 != 0) return "d_model must be a multiple of 32 for bf16 (GEMM K-tile)";
+  if (c->dtype == PKM_BF16 && c->memory_plus && c->d_value % 32 != 0)
+    return "d_value must be a multiple of 32 for the bf16 Memory+ gate (GEMM K-tile)";
   if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
   if (c->d_query <= 0 || c->d_query % 2 != 0) return "d_query must be positive and even";
   const int d_h = c->d_query / 2;
