@@ -70,3 +70,60 @@ HEADLINE = "memplus_16m_bf16"
 
 def get_config(name: str) -> Config:
     return CONFIGS[name]
+
+
+@dataclass(frozen=True)
+class EngramConfig:
+    """Hashed n-gram lookup (Engram review: multi-head hashing into per-(n, head)
+    tables, eq. 1; context-aware gate, eq. 2)."""
+    name: str
+    T: int             # tokens
+    seq_len: int       # tokens per sequence (n-grams never cross a sequence start)
+    vocab: int         # token ids are in [0, vocab)
+    zipf_s: float      # token ranks follow a truncated Zipf law P(r) ~ r^-s, id = r - 1
+    min_order: int     # smallest n
+    n_orders: int      # orders min_order .. min_order + n_orders - 1
+    heads: int         # hash heads per order
+    head_dim: int      # embedding width of one head; d = heads * head_dim
+    table_rows: int    # rows of every table E_{n,k} (a prime)
+    dtype: str         # "f32" or "bf16": tables, hidden states and output
+    residual: bool = False   # out = h + alpha * e instead of alpha * e
+    n_concepts: int = 0      # > 0: token ids first pass through a vocabulary map onto this many ids
+    norm_eps: float = 1e-6
+
+    @property
+    def d(self) -> int:
+        return self.heads * self.head_dim
+
+    @property
+    def n_tables(self) -> int:
+        return self.n_orders * self.heads
+
+    @property
+    def total_rows(self) -> int:
+        return self.n_tables * self.table_rows
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def with_(self, **kw) -> "EngramConfig":
+        return replace(self, **kw)
+
+
+ENGRAM_CONFIGS = {
+    # 16,384 Zipf(1.1) token ids over a 128,000 vocabulary, 2- and 3-grams, 8 heads per
+    # order, 16 tables of 2,097,143 (prime) rows x 128 bf16 (8.0 GiB), d = 1024
+    "engram_zipf_2m_bf16": EngramConfig("engram_zipf_2m_bf16", T=16384, seq_len=16384, vocab=128000, zipf_s=1.1,
+                                        min_order=2, n_orders=2, heads=8, head_dim=128, table_rows=2097143,
+                                        dtype="bf16"),
+    # small fp32 case: three sequences of 200 tokens, 4 heads of width 32, 1,009-row tables
+    "engram_tiny_f32": EngramConfig("engram_tiny_f32", T=600, seq_len=200, vocab=500, zipf_s=1.1, min_order=2,
+                                    n_orders=2, heads=4, head_dim=32, table_rows=1009, dtype="f32"),
+    # vocabulary map onto 3,000 concept ids, orders 2..4, residual output
+    "engram_compress_bf16": EngramConfig("engram_compress_bf16", T=1000, seq_len=250, vocab=5000, zipf_s=1.1,
+                                         min_order=2, n_orders=3, heads=8, head_dim=64, table_rows=10007,
+                                         dtype="bf16", residual=True, n_concepts=3000),
+}
+
+ENGRAM_HEADLINE = "engram_zipf_2m_bf16"

@@ -3,7 +3,7 @@
 //
 //  * synth_fill_values: the row-addressable value table, bit-identical to the host
 //    generator in synth/inputs.py:
-//        seed_V = splitmix64((seed << 8) | 6)
+//        seed_V = splitmix64((seed << 8) | tid)     (tid 6: the value table)
 //        u      = splitmix64(seed_V ^ (row * d_v + col))
 //        S      = sum of the four 16-bit limbs of u
 //        v      = (S - 131070) * 0x1.1bc779ef9b324p-21      (IEEE double)
@@ -79,16 +79,23 @@ __global__ void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ s
 
 extern "C" {
 
-// Fill rows [row0, row0 + n_rows) of a [*, d_v] table at `table` (device pointer to row 0).
-// dtype 0 = fp32, 1 = bf16.  Returns 0 or a hipError_t code.
-int synth_fill_values(void* table, int64_t row0, int64_t n_rows, int32_t d_v, int32_t dtype, uint64_t seed,
-                      void* stream) {
+// Fill rows [row0, row0 + n_rows) of a [*, d_v] table at `table` (device pointer to row 0)
+// from the stream of tensor id `tid`.  dtype 0 = fp32, 1 = bf16.  Returns 0 or a
+// hipError_t code.
+int synth_fill_table(void* table, int64_t row0, int64_t n_rows, int32_t d_v, int32_t dtype, uint64_t seed,
+                     uint32_t tid, void* stream) {
   const int per = dtype == 1 ? 8 : 4;
-  if (!table || n_rows < 0 || row0 < 0 || d_v <= 0 || d_v % per != 0) return (int)hipErrorInvalidValue;
+  if (!table || n_rows < 0 || row0 < 0 || d_v <= 0 || d_v % per != 0 || tid > 255) return (int)hipErrorInvalidValue;
   if (n_rows == 0) return 0;
-  const uint64_t sv = splitmix64((seed << 8) | 6u);
+  const uint64_t sv = splitmix64((seed << 8) | tid);
   fill_values_kernel<<<8192, 256, 0, (hipStream_t)stream>>>((uint8_t*)table, row0, n_rows, d_v, dtype == 1, sv);
   return (int)hipGetLastError();
+}
+
+// The value table of the product-key memory: tensor id 6.
+int synth_fill_values(void* table, int64_t row0, int64_t n_rows, int32_t d_v, int32_t dtype, uint64_t seed,
+                      void* stream) {
+  return synth_fill_table(table, row0, n_rows, d_v, dtype, seed, 6u, stream);
 }
 
 int synth_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {

@@ -12,9 +12,10 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _lib.synth_fill_values.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64, _vp]
+_lib.synth_fill_table.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64, ctypes.c_uint32, _vp]
 _lib.synth_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
 _lib.synth_copy.argtypes = [_vp, _vp, _i64, _i32, _vp]
-for _f in (_lib.synth_fill_values, _lib.synth_stream_read, _lib.synth_copy):
+for _f in (_lib.synth_fill_values, _lib.synth_fill_table, _lib.synth_stream_read, _lib.synth_copy):
     _f.restype = ctypes.c_int
 
 
@@ -23,14 +24,15 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def fill_values(table, seed: int, row0: int = 0, n_rows: int | None = None) -> None:
-    """Fill rows of a [N, d_v] torch tensor (float32 or bfloat16) on the GPU."""
+def fill_values(table, seed: int, row0: int = 0, n_rows: int | None = None, tid: int = 6) -> None:
+    """Fill rows of a [N, d_v] torch tensor (float32 or bfloat16) on the GPU from the
+    row-addressable stream of tensor id ``tid`` (6: the value table)."""
     import torch
     dt = 1 if table.dtype == torch.bfloat16 else 0
     n_rows = table.shape[0] - row0 if n_rows is None else n_rows
-    rc = _lib.synth_fill_values(table.data_ptr(), row0, n_rows, table.shape[1], dt, seed, _stream())
+    rc = _lib.synth_fill_table(table.data_ptr(), row0, n_rows, table.shape[1], dt, seed, tid, _stream())
     if rc:
-        raise RuntimeError(f"synth_fill_values failed: hip error {rc}")
+        raise RuntimeError(f"synth_fill_table failed: hip error {rc}")
 
 
 def stream_read(buf, sink, grid: int = 2048) -> None:

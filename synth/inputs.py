@@ -13,7 +13,7 @@ values ~ N(0, 0.02^2) through the row-addressable generator below.
 The value table is row-addressable so that a 64-128 GiB table can be filled on
 the GPU and any of its rows regenerated on the host:
 
-    seed_V = splitmix64((seed << 8) | 6)
+    seed_V = splitmix64((seed << 8) | tid)       (tid = 6 for the value table)
     u      = splitmix64(seed_V XOR (row * d_v + col))
     S      = sum of the four 16-bit limbs of u          (Irwin-Hall, n = 4)
     v      = (S - 131070) * VALUE_SCALE                (IEEE float64)
@@ -32,6 +32,7 @@ import numpy as np
 from .configs import Config
 
 TID_X, TID_WQ, TID_KEYS, TID_W1, TID_W2, TID_V, TID_UIDX, TID_TOKENS, TID_HIDDEN = range(1, 10)
+TID_ENGRAM, TID_MULT, TID_COMPRESS = 10, 11, 12
 
 VALUE_SCALE = float.fromhex("0x1.1bc779ef9b324p-21")  # 0.02 / 37837.2272...
 IRWIN_HALL_MEAN = 131070
@@ -57,8 +58,8 @@ def splitmix64(z: np.ndarray) -> np.ndarray:
     return z ^ (z >> np.uint64(31))
 
 
-def value_seed(seed: int) -> int:
-    return splitmix64_scalar(((seed << 8) | TID_V) & _M64)
+def value_seed(seed: int, tid: int = TID_V) -> int:
+    return splitmix64_scalar(((seed << 8) | tid) & _M64)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -82,10 +83,11 @@ def normal_tensor(seed: int, tid: int, shape, std: float, dtype: str) -> np.ndar
     return _store(rng.standard_normal(size=shape) * std, dtype)
 
 
-def value_rows(seed: int, rows, d_v: int, dtype: str) -> np.ndarray:
-    """Rows ``rows`` of the value table, shape [len(rows), d_v] (float32 or bf16 bits)."""
+def value_rows(seed: int, rows, d_v: int, dtype: str, tid: int = TID_V) -> np.ndarray:
+    """Rows ``rows`` of the row-addressable table of tensor id ``tid`` (default: the
+    value table), shape [len(rows), d_v] (float32 or bf16 bits)."""
     rows = np.asarray(rows, dtype=np.uint64).reshape(-1)
-    sv = np.uint64(value_seed(seed))
+    sv = np.uint64(value_seed(seed, tid))
     ctr = rows[:, None] * np.uint64(d_v) + np.arange(d_v, dtype=np.uint64)[None, :]
     u = splitmix64(sv ^ ctr)
     m = np.uint64(0xFFFF)
@@ -94,12 +96,12 @@ def value_rows(seed: int, rows, d_v: int, dtype: str) -> np.ndarray:
     return _store(v64, dtype)
 
 
-def value_table(seed: int, n_rows: int, d_v: int, dtype: str, chunk: int = 1 << 14) -> np.ndarray:
+def value_table(seed: int, n_rows: int, d_v: int, dtype: str, chunk: int = 1 << 14, tid: int = TID_V) -> np.ndarray:
     """The whole table (small tables only)."""
     out = np.empty((n_rows, d_v), dtype=np.float32 if dtype == "f32" else np.uint16)
     for r0 in range(0, n_rows, chunk):
         r1 = min(n_rows, r0 + chunk)
-        out[r0:r1] = value_rows(seed, np.arange(r0, r1), d_v, dtype)
+        out[r0:r1] = value_rows(seed, np.arange(r0, r1), d_v, dtype, tid)
     return out
 
 
@@ -133,3 +135,57 @@ def uniform_bags(seed: int, n_bags: int, bag: int, n_rows: int):
     w = rng.random(size=(n_bags, bag)) + 0.5
     w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
     return idx, w
+
+
+# ---- hashed n-gram lookup (Engram) inputs ---------------------------------------------
+
+def zipf_tokens(seed: int, T: int, vocab: int, s: float) -> np.ndarray:
+    """T token ids: rank r in 1..vocab drawn with probability proportional to r^-s
+    (a Zipf law truncated at the vocabulary), id = r - 1; int32."""
+    rng = np.random.default_rng([seed, TID_TOKENS])
+    p = np.arange(1, vocab + 1, dtype=np.float64) ** (-s)
+    cdf = np.cumsum(p)
+    cdf /= cdf[-1]
+    u = rng.random(T)
+    return np.minimum(np.searchsorted(cdf, u, side="right"), vocab - 1).astype(np.int32)
+
+
+def hidden_states(seed: int, T: int, d: int, dtype: str) -> np.ndarray:
+    """h ~ N(0, 1), [T, d]."""
+    return normal_tensor(seed, TID_HIDDEN, (T, d), 1.0, dtype)
+
+
+def engram_multipliers(seed: int, min_order: int, n_orders: int, heads: int) -> np.ndarray:
+    """Odd 64-bit multipliers m[o, k] of the hash of order n = min_order + o, head k:
+    splitmix64(base XOR (n << 8 | k)) with the low bit set, base = splitmix64((seed << 8) | 11)."""
+    base = splitmix64_scalar(((seed << 8) | TID_MULT) & _M64)
+    m = np.empty((n_orders, heads), dtype=np.uint64)
+    for o in range(n_orders):
+        for k in range(heads):
+            m[o, k] = splitmix64_scalar(base ^ (((min_order + o) << 8) | k)) | 1
+    return m
+
+
+def compress_map(seed: int, vocab: int, n_concepts: int) -> np.ndarray:
+    """A vocabulary map onto n_concepts ids (uniform, many-to-one), int32 [vocab]."""
+    rng = np.random.default_rng([seed, TID_COMPRESS])
+    return rng.integers(0, n_concepts, size=vocab, dtype=np.int64).astype(np.int32)
+
+
+def engram_table_rows(seed: int, rows, head_dim: int, dtype: str) -> np.ndarray:
+    """Rows of the stacked Engram tables (tensor id 10), N(0, 0.02^2) like the value table."""
+    return value_rows(seed, rows, head_dim, dtype, tid=TID_ENGRAM)
+
+
+def make_engram_inputs(cfg, seed: int = 0, T: int | None = None) -> dict:
+    """ids [T] int32, h [T, d], mult [n_orders, heads] uint64 and, with a vocabulary map,
+    compress [vocab] int32.  ``T`` takes a prefix of the full workload's tokens."""
+    T = cfg.T if T is None else T
+    full = max(T, cfg.T)
+    d = {
+        "ids": zipf_tokens(seed, full, cfg.vocab, cfg.zipf_s)[:T].copy(),
+        "h": np.ascontiguousarray(hidden_states(seed, full, cfg.d, cfg.dtype)[:T]),
+        "mult": engram_multipliers(seed, cfg.min_order, cfg.n_orders, cfg.heads),
+        "compress": compress_map(seed, cfg.vocab, cfg.n_concepts) if cfg.n_concepts else None,
+    }
+    return d
