@@ -1,4 +1,4 @@
-"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h``).
+"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h`` and ``include/engram.h``).
 
 Argument marshalling only: every function has the name of the C entry point it
 calls, takes torch tensors (or raw device addresses as ints, or None for NULL)
@@ -40,6 +40,14 @@ class pkm_debug_ptrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("qhat", "half_idx", "half_score", "idx", "score", "w", "y")]
 
 
+class engram_config(ctypes.Structure):
+    _fields_ = [
+        ("min_order", ctypes.c_int32), ("n_orders", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("table_rows", ctypes.c_int64), ("vocab", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("residual", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+    ]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _sig = {
     "pkm_workspace_size": (_sz, [ctypes.POINTER(pkm_config)]),
@@ -54,6 +62,9 @@ _sig = {
     "pkm_set_pipeline_chunks": (ctypes.c_int, [_vp, _i32]),
     "pkm_destroy": (ctypes.c_int, [_vp]),
     "pkm_last_error": (ctypes.c_char_p, []),
+    "engram_hash": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "engram_forward": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -157,3 +168,21 @@ def pkm_set_pipeline_chunks(h: int, chunks: int) -> None:
 
 def pkm_destroy(h: int) -> None:
     _check(_lib.pkm_destroy(h), "pkm_destroy")
+
+
+def make_engram_config(min_order, n_orders, n_heads, head_dim, table_rows, vocab, dtype, residual=False,
+                       norm_eps=1e-6) -> engram_config:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    return engram_config(int(min_order), int(n_orders), int(n_heads), int(head_dim), int(table_rows), int(vocab),
+                         int(dt), int(bool(residual)), float(norm_eps))
+
+
+def engram_hash(cfg: engram_config, ids, T: int, seq_len: int, compress, mult, rows, stream=None) -> None:
+    _check(_lib.engram_hash(ctypes.byref(cfg), _ptr(ids), T, seq_len, _ptr(compress), _ptr(mult), _ptr(rows),
+                            _stream(stream)), "engram_hash")
+
+
+def engram_forward(cfg: engram_config, tables, ids, T: int, seq_len: int, compress, mult, h, out, e_out=None,
+                   alpha_out=None, stream=None) -> None:
+    _check(_lib.engram_forward(ctypes.byref(cfg), _ptr(tables), _ptr(ids), T, seq_len, _ptr(compress), _ptr(mult),
+                               _ptr(h), _ptr(out), _ptr(e_out), _ptr(alpha_out), _stream(stream)), "engram_forward")

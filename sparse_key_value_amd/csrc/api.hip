@@ -9,12 +9,15 @@
 #include <string>
 #include <vector>
 
+#include "abi.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
-namespace {
+namespace pkm_abi {
 
+namespace {
 thread_local std::string g_err;
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -26,12 +29,6 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-#define PKM_HIP(call)                                                                       \
-  do {                                                                                      \
-    hipError_t e_ = (call);                                                                 \
-    if (e_ != hipSuccess) return fail(PKM_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
-  } while (0)
-
 int check_device() {
   int dev = 0;
   PKM_HIP(hipGetDevice(&dev));
@@ -42,7 +39,12 @@ int check_device() {
   return PKM_OK;
 }
 
-}  // namespace
+const char* last_error() { return g_err.c_str(); }
+
+}  // namespace pkm_abi
+
+using pkm_abi::check_device;
+using pkm_abi::fail;
 
 constexpr int MAX_CHUNKS = 8;
 
@@ -131,12 +133,6 @@ struct Timer {
     if (h->count < h->max_rec) ++h->count;
   }
 };
-
-#define PKM_LAUNCH(call)                                                                              \
-  do {                                                                                                \
-    hipError_t e_ = (call);                                                                           \
-    if (e_ != hipSuccess) return fail(PKM_EHIP, "launch %s failed: %s", #call, hipGetErrorString(e_)); \
-  } while (0)
 
 // Selection scratch of the rows of tokens [t0, ...): group maxima, bounds, candidates.
 struct SelScratch {
@@ -330,7 +326,7 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
 
 extern "C" {
 
-const char* pkm_last_error(void) { return g_err.c_str(); }
+const char* pkm_last_error(void) { return pkm_abi::last_error(); }
 
 size_t pkm_workspace_size(const pkm_config* cfg) {
   std::string why = pkm::check_config(cfg);

@@ -1,0 +1,299 @@
+// Hashed n-gram lookup (review of "Conditional Memory via Scalable Lookup" (Engram):
+// sparse retrieval with multi-head hashing, key equation 1; context-aware gating, key
+// equation 2; residual connection) and its C entry points.
+//
+// One wave per token does the whole lookup: the token ids of the longest n-gram ending
+// at the token are read once (wave-uniform), every lane folds the hashes of the
+// (order, head) pairs its 16-byte column slices belong to, puts all the rows it needs
+// in flight at once (nontemporal: the tables are far larger than the caches), sums the
+// orders in fp32, and the wave reduces <h, e>, |h|^2 and |e|^2 for the gate before
+// writing alpha * e (+ h).  The embedding is never written to memory unless asked for,
+// so a token costs its table rows, its hidden state and its output: for 2 orders x 8
+// heads x 128 bf16 at d = 1024, 4 KiB + 2 KiB + 2 KiB.
+#include <string>
+
+#include "../../include/engram.h"
+#include "abi.hpp"
+#include "common.hpp"
+
+namespace pkm {
+
+namespace {
+
+constexpr int MAX_ORDER = 8;   // largest n-gram order
+constexpr int MAX_ORDERS = 4;  // orders per lookup
+constexpr int MAX_SPL = 4;     // 16-byte slices of a token per lane (d * sizeof <= 4096 bytes)
+
+struct EngramArgs {
+  const uint8_t* tables;
+  const int32_t* ids;
+  const int32_t* compress;
+  const uint64_t* mult;
+  const uint8_t* h;
+  uint8_t* out;
+  float* e_out;
+  float* alpha_out;
+  int64_t T, seq_len, P;
+  int vocab, min_order, n_orders, heads;
+  int head_vecs;  // 16-byte slices of one table row
+  int slices;     // 16-byte slices of a token's d values
+  int d, residual;
+  float eps;
+};
+
+// The id the hash sees (ids outside [0, vocab) read as 0; optional vocabulary map).
+__device__ __forceinline__ uint64_t norm_id(const EngramArgs& a, int64_t j) {
+  int32_t v = a.ids[j];
+  v = (v >= 0 && v < a.vocab) ? v : 0;
+  return a.compress ? (uint64_t)(uint32_t)a.compress[v] : (uint64_t)(uint32_t)v;
+}
+
+// phi before the modulus: fold of the last n of the MAX_ORDER ids in `tok` (oldest first).
+__device__ __forceinline__ uint64_t fold(const uint64_t (&tok)[MAX_ORDER], int n, uint64_t m) {
+  uint64_t hh = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_ORDER; ++i)
+    if (i >= MAX_ORDER - n) hh = (hh ^ tok[i]) * m;
+  return hh;
+}
+
+template <int EB>
+struct Elems;
+template <>
+struct Elems<2> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_lo(v[e]);
+      f[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* f) {
+    u32x4 p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = (uint32_t)f32_to_bf16(f[2 * e]) | ((uint32_t)f32_to_bf16(f[2 * e + 1]) << 16);
+    return p;
+  }
+};
+template <>
+struct Elems<4> {
+  static constexpr int E = 4;
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  }
+};
+
+// Four tokens per block, one per wave.
+template <int EB>
+__global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
+  using EL = Elems<EB>;
+  constexpr int E = EL::E;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+
+  // ids of the longest n-gram ending at t, oldest first; before the sequence start: 0
+  const int nmax = a.min_order + a.n_orders - 1;
+  const int64_t start = t - t % a.seq_len;
+  uint64_t tok[MAX_ORDER];
+#pragma unroll
+  for (int i = 0; i < MAX_ORDER; ++i) {
+    const int64_t j = t - (MAX_ORDER - 1 - i);
+    tok[i] = (i >= MAX_ORDER - nmax && j >= start) ? norm_id(a, j) : 0ull;
+  }
+
+  // this lane's slices: s = lane + 64 i, head s / head_vecs, column s % head_vecs
+  const size_t row_bytes = (size_t)a.head_vecs * 16;
+  u32x4 v[MAX_ORDERS][MAX_SPL];
+  u32x4 hv[MAX_SPL];
+#pragma unroll
+  for (int i = 0; i < MAX_SPL; ++i) {
+    const int s = lane + 64 * i;
+    const bool ok = s < a.slices;
+    const int k = ok ? s / a.head_vecs : 0;
+    const int col = ok ? s - k * a.head_vecs : 0;
+#pragma unroll
+    for (int o = 0; o < MAX_ORDERS; ++o) {
+      v[o][i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && o < a.n_orders) {
+        const uint64_t m = a.mult[o * a.heads + k];
+        const uint64_t phi = fold(tok, a.min_order + o, m) % (uint64_t)a.P;
+        const int64_t row = ((int64_t)o * a.heads + k) * a.P + (int64_t)phi;
+        v[o][i] = __builtin_nontemporal_load((const u32x4*)(a.tables + (size_t)row * row_bytes + (size_t)col * 16));
+      }
+    }
+    hv[i] = ok ? *(const u32x4*)(a.h + ((size_t)t * a.slices + s) * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // e = sum over orders (fp32, order 0 first); the three sums of the gate
+  float e[MAX_SPL][E], hf[MAX_SPL][E];
+  float ee = 0.f, hh = 0.f, eh = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAX_SPL; ++i) {
+#pragma unroll
+    for (int x = 0; x < E; ++x) e[i][x] = 0.f;
+#pragma unroll
+    for (int o = 0; o < MAX_ORDERS; ++o) {
+      float f[E];
+      EL::unpack(v[o][i], f);
+#pragma unroll
+      for (int x = 0; x < E; ++x) e[i][x] += f[x];
+    }
+    EL::unpack(hv[i], hf[i]);
+#pragma unroll
+    for (int x = 0; x < E; ++x) {
+      ee = __builtin_fmaf(e[i][x], e[i][x], ee);
+      hh = __builtin_fmaf(hf[i][x], hf[i][x], hh);
+      eh = __builtin_fmaf(hf[i][x], e[i][x], eh);
+    }
+  }
+  ee = wave_sum_f32(ee);
+  hh = wave_sum_f32(hh);
+  eh = wave_sum_f32(eh);
+  const float inv_d = 1.0f / (float)a.d;
+  const float z = eh / (__fsqrt_rn(hh * inv_d + a.eps) * __fsqrt_rn(ee * inv_d + a.eps) * __fsqrt_rn((float)a.d));
+  const float alpha = 1.0f / (1.0f + __expf(-z));
+
+#pragma unroll
+  for (int i = 0; i < MAX_SPL; ++i) {
+    const int s = lane + 64 * i;
+    if (s >= a.slices) continue;
+    float o[E];
+#pragma unroll
+    for (int x = 0; x < E; ++x) o[x] = a.residual ? __builtin_fmaf(alpha, e[i][x], hf[i][x]) : alpha * e[i][x];
+    *(u32x4*)(a.out + ((size_t)t * a.slices + s) * 16) = EL::pack(o);
+    if (a.e_out) {
+      float* eo = a.e_out + (size_t)t * a.d + (size_t)s * E;
+#pragma unroll
+      for (int x = 0; x < E; x += 4) *(f32x4*)(eo + x) = f32x4{e[i][x], e[i][x + 1], e[i][x + 2], e[i][x + 3]};
+    }
+  }
+  if (a.alpha_out && lane == 0) a.alpha_out[t] = alpha;
+}
+
+// One thread per (token, head, order): rows[t, k, o].
+__global__ void __launch_bounds__(256) engram_hash_kernel(EngramArgs a, int32_t* __restrict__ rows) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = a.T * a.heads * a.n_orders;
+  if (i >= total) return;
+  const int o = (int)(i % a.n_orders);
+  const int k = (int)((i / a.n_orders) % a.heads);
+  const int64_t t = i / ((int64_t)a.n_orders * a.heads);
+  const int n = a.min_order + o;
+  const int64_t start = t - t % a.seq_len;
+  const uint64_t m = a.mult[o * a.heads + k];
+  uint64_t hh = 0;
+  for (int64_t j = t - n + 1; j <= t; ++j) hh = (hh ^ (j >= start ? norm_id(a, j) : 0ull)) * m;
+  rows[i] = (int32_t)(((int64_t)o * a.heads + k) * a.P + (int64_t)(hh % (uint64_t)a.P));
+}
+
+std::string check_engram(const engram_config* c) {
+  if (!c) return "config is NULL";
+  if (c->dtype != PKM_F32 && c->dtype != PKM_BF16) return "dtype must be PKM_F32 (0) or PKM_BF16 (1)";
+  const int64_t eb = c->dtype == PKM_BF16 ? 2 : 4;
+  if (c->min_order < 1) return "min_order must be >= 1";
+  if (c->n_orders < 1 || c->n_orders > MAX_ORDERS) return "n_orders must be in [1, 4]";
+  if (c->min_order + c->n_orders - 1 > MAX_ORDER) return "the largest order min_order + n_orders - 1 must be <= 8";
+  if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
+  if (c->head_dim < 1 || (c->head_dim * eb) % 16 != 0) return "head_dim * sizeof(dtype) must be a positive multiple of 16";
+  if ((int64_t)c->n_heads * c->head_dim * eb > 64 * 16 * MAX_SPL)
+    return "n_heads * head_dim * sizeof(dtype) must be <= 4096 bytes";
+  if (c->table_rows < 1) return "table_rows must be >= 1";
+  if ((int64_t)c->n_orders * c->n_heads * c->table_rows >= ((int64_t)1 << 31))
+    return "n_orders * n_heads * table_rows must be < 2^31 (int32 rows)";
+  if (c->vocab < 1) return "vocab must be >= 1";
+  if (c->residual != 0 && c->residual != 1) return "residual must be 0 or 1";
+  if (!(c->norm_eps >= 0.0f) || c->norm_eps > 1.0f) return "norm_eps must be in [0, 1]";
+  return "";
+}
+
+// Argument checks shared by both entry points; fills `a` on success.
+int prepare(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t seq_len, const int32_t* compress,
+            const uint64_t* mult, EngramArgs& a) {
+  const std::string why = check_engram(cfg);
+  if (!why.empty()) return pkm_abi::fail(PKM_EINVAL, "invalid engram config: %s", why.c_str());
+  if (T < 0 || T > ((int64_t)1 << 31) - 1) return pkm_abi::fail(PKM_EINVAL, "T must be in [0, 2^31)");
+  if (seq_len < 1) return pkm_abi::fail(PKM_EINVAL, "seq_len must be >= 1");
+  if (T > 0 && (!ids || !mult)) return pkm_abi::fail(PKM_EINVAL, "ids and mult must not be NULL");
+  const int eb = cfg->dtype == PKM_BF16 ? 2 : 4;
+  a = EngramArgs{};
+  a.ids = ids;
+  a.compress = compress;
+  a.mult = mult;
+  a.T = T;
+  a.seq_len = seq_len;
+  a.P = cfg->table_rows;
+  a.vocab = cfg->vocab;
+  a.min_order = cfg->min_order;
+  a.n_orders = cfg->n_orders;
+  a.heads = cfg->n_heads;
+  a.head_vecs = cfg->head_dim * eb / 16;
+  a.slices = a.heads * a.head_vecs;
+  a.d = cfg->n_heads * cfg->head_dim;
+  a.residual = cfg->residual;
+  a.eps = cfg->norm_eps;
+  return PKM_OK;
+}
+
+// The device check once per device and process.
+int device_ok() {
+  static int state[64] = {};  // 0 unknown, 1 gfx950
+  int dev = 0;
+  PKM_HIP(hipGetDevice(&dev));
+  if (dev >= 0 && dev < 64 && state[dev] == 1) return PKM_OK;
+  const int rc = pkm_abi::check_device();
+  if (rc == PKM_OK && dev >= 0 && dev < 64) state[dev] = 1;
+  return rc;
+}
+
+}  // namespace
+
+}  // namespace pkm
+
+extern "C" {
+
+int engram_hash(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t seq_len, const int32_t* compress,
+                const uint64_t* mult, int32_t* rows, void* stream) {
+  pkm::EngramArgs a;
+  int rc = pkm::prepare(cfg, ids, T, seq_len, compress, mult, a);
+  if (rc != PKM_OK) return rc;
+  if (T == 0) return PKM_OK;
+  if (!rows) return pkm_abi::fail(PKM_EINVAL, "rows must not be NULL");
+  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
+  const int64_t total = T * a.heads * a.n_orders;
+  if ((total + 255) / 256 > ((int64_t)1 << 31) - 1) return pkm_abi::fail(PKM_EINVAL, "T * n_heads * n_orders too large");
+  PKM_LAUNCH((pkm::engram_hash_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, (hipStream_t)stream>>>(a, rows),
+              hipGetLastError()));
+  return PKM_OK;
+}
+
+int engram_forward(const engram_config* cfg, const void* tables, const int32_t* ids, int64_t T, int64_t seq_len,
+                   const int32_t* compress, const uint64_t* mult, const void* h, void* out, float* e_out,
+                   float* alpha_out, void* stream) {
+  pkm::EngramArgs a;
+  int rc = pkm::prepare(cfg, ids, T, seq_len, compress, mult, a);
+  if (rc != PKM_OK) return rc;
+  if (T == 0) return PKM_OK;
+  if (!tables || !h || !out) return pkm_abi::fail(PKM_EINVAL, "tables, h and out must not be NULL");
+  if ((((uintptr_t)tables | (uintptr_t)h | (uintptr_t)out | (uintptr_t)e_out) & 15) != 0)
+    return pkm_abi::fail(PKM_EINVAL, "tables, h, out and e_out must be 16-byte aligned");
+  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
+  a.tables = (const uint8_t*)tables;
+  a.h = (const uint8_t*)h;
+  a.out = (uint8_t*)out;
+  a.e_out = e_out;
+  a.alpha_out = alpha_out;
+  const dim3 grid((unsigned)((T + 3) / 4));
+  if (cfg->dtype == PKM_BF16)
+    PKM_LAUNCH((pkm::engram_forward_kernel<2><<<grid, 256, 0, (hipStream_t)stream>>>(a), hipGetLastError()));
+  else
+    PKM_LAUNCH((pkm::engram_forward_kernel<4><<<grid, 256, 0, (hipStream_t)stream>>>(a), hipGetLastError()));
+  return PKM_OK;
+}
+
+}  // extern "C"

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared(header):
     txt = open(os.path.join(ROOT, "include", header)).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkm_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b((?:pkm|engram)_[a-z_]+)\s*\(", txt)))
 
 
 @pytest.fixture(scope="module")
@@ -24,8 +24,10 @@ def P():
 
 def test_library_exports_every_declared_symbol(P):
     lib = ctypes.CDLL(P.LIB_PATH)
-    names = _declared("pkm.h")
-    assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag"} <= set(names)
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["engram.h", "pkm.h"]
+    names = sorted(set(n for hd in headers for n in _declared(hd)))
+    assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag", "engram_hash", "engram_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/pkm.h but not exported"
     assert set(names) == set(P.EXPORTED), "binding and header disagree"
@@ -113,3 +115,52 @@ def test_other_entry_points_reject_bad_arguments(P):
     assert eb(None, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL  # NULL table
     assert eb(8, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL     # misaligned table
     assert eb(None, 10, 16, 1, None, None, 0, 4, None, None) == P.PKM_OK   # zero bags: nothing to do
+
+
+def _ecfg(P, **kw):
+    base = dict(min_order=2, n_orders=2, n_heads=8, head_dim=128, table_rows=2097143, vocab=128000, dtype="bf16")
+    base.update(kw)
+    return P.make_engram_config(**base)
+
+
+@pytest.mark.parametrize("bad,needle", [
+    (dict(dtype=5), "dtype"),
+    (dict(min_order=0), "min_order"),
+    (dict(n_orders=0), "n_orders"),
+    (dict(n_orders=5), "n_orders"),
+    (dict(min_order=6, n_orders=4), "largest order"),
+    (dict(n_heads=65), "n_heads"),
+    (dict(head_dim=4), "head_dim"),
+    (dict(head_dim=512), "4096 bytes"),
+    (dict(table_rows=0), "table_rows"),
+    (dict(table_rows=1 << 27), "2^31"),
+    (dict(vocab=0), "vocab"),
+    (dict(residual=2), "residual"),
+    (dict(norm_eps=-1.0), "norm_eps"),
+])
+def test_engram_invalid_configs_are_rejected(P, bad, needle):
+    c = _ecfg(P)
+    for key, v in bad.items():
+        setattr(c, key, v)
+    lib = P._lib._lib
+    assert lib.engram_hash(ctypes.byref(c), 256, 4, 4, None, 256, 256, None) == P.PKM_EINVAL
+    assert needle in P.pkm_last_error()
+    assert lib.engram_forward(ctypes.byref(c), 256, 256, 4, 4, None, 256, 256, 256, None, None, None) == P.PKM_EINVAL
+    assert needle in P.pkm_last_error()
+
+
+def test_engram_argument_errors_before_any_device_call(P):
+    c = _ecfg(P)
+    lib = P._lib._lib
+    assert lib.engram_hash(None, 256, 4, 4, None, 256, 256, None) == P.PKM_EINVAL
+    assert lib.engram_hash(ctypes.byref(c), 256, -1, 4, None, 256, 256, None) == P.PKM_EINVAL
+    assert lib.engram_hash(ctypes.byref(c), 256, 4, 0, None, 256, 256, None) == P.PKM_EINVAL
+    assert "seq_len" in P.pkm_last_error()
+    assert lib.engram_hash(ctypes.byref(c), None, 4, 4, None, 256, 256, None) == P.PKM_EINVAL
+    assert lib.engram_hash(ctypes.byref(c), 256, 4, 4, None, 256, None, None) == P.PKM_EINVAL
+    assert lib.engram_forward(ctypes.byref(c), None, 256, 4, 4, None, 256, 256, 256, None, None, None) == P.PKM_EINVAL
+    assert lib.engram_forward(ctypes.byref(c), 256, 256, 4, 4, None, 256, 264, 256, None, None, None) == P.PKM_EINVAL
+    assert "16-byte" in P.pkm_last_error()
+    # T = 0 is a no-op that needs no pointers
+    assert lib.engram_hash(ctypes.byref(c), None, 0, 4, None, None, None, None) == P.PKM_OK
+    assert lib.engram_forward(ctypes.byref(c), None, None, 0, 4, None, None, None, None, None, None, None) == P.PKM_OK
