@@ -3,11 +3,13 @@
 // equation 2; residual connection) and its C entry points.
 //
 // One wave per token does the whole lookup: the token ids of the longest n-gram ending
-// at the token are read once (wave-uniform), every lane folds the hashes of the
-// (order, head) pairs its 16-byte column slices belong to, puts all the rows it needs
-// in flight at once (nontemporal: the tables are far larger than the caches), sums the
-// orders in fp32, and the wave reduces <h, e>, |h|^2 and |e|^2 for the gate before
-// writing alpha * e (+ h).  The embedding is never written to memory unless asked for,
+// at the token are read once (wave-uniform); lane p folds the hash of (order, head)
+// pair p (one hash per lane instead of one per lane and slice) and leaves the row in
+// LDS; every lane then puts all the rows of its 16-byte column slices in flight at once
+// (nontemporal: the tables are far larger than the caches), sums the orders in fp32,
+// and the wave reduces <h, e>, |h|^2 and |e|^2 for the gate before writing
+// alpha * e (+ h).  The modulus uses an fp64 reciprocal of P and an exact integer
+// correction instead of a 64-bit division.  The embedding is never written to memory unless asked for,
 // so a token costs its table rows, its hidden state and its output: for 2 orders x 8
 // heads x 128 bf16 at d = 1024, 4 KiB + 2 KiB + 2 KiB.
 #include <string>
@@ -39,6 +41,8 @@ struct EngramArgs {
   int slices;     // 16-byte slices of a token's d values
   int d, residual;
   float eps;
+  double inv_p;      // 1 / P, rounded
+  uint64_t two32_p;  // 2^32 mod P
 };
 
 // The id the hash sees (ids outside [0, vocab) read as 0; optional vocabulary map).
@@ -55,6 +59,25 @@ __device__ __forceinline__ uint64_t fold(const uint64_t (&tok)[MAX_ORDER], int n
   for (int i = 0; i < MAX_ORDER; ++i)
     if (i >= MAX_ORDER - n) hh = (hh ^ tok[i]) * m;
   return hh;
+}
+
+// x mod P for x / P < 2^40: the fp64 quotient estimate is off by at most one, which the
+// two compares correct exactly.
+__device__ __forceinline__ uint64_t mod_small(uint64_t x, uint64_t P, double inv_p) {
+  const uint64_t q = (uint64_t)((double)x * inv_p);
+  int64_t r = (int64_t)(x - q * P);
+  r = r < 0 ? r + (int64_t)P : r;
+  r = r >= (int64_t)P ? r - (int64_t)P : r;
+  return (uint64_t)r;
+}
+
+// h mod P for any 64-bit h and 1 <= P < 2^31: h = hi * 2^32 + lo, so
+// h mod P = ((hi mod P) * (2^32 mod P) + lo) mod P, whose operand is < 2^62 + 2^32 and
+// whose quotient is < 2^32 + 2^32 / P.
+__device__ __forceinline__ uint64_t mod_p(uint64_t h, const EngramArgs& a) {
+  const uint64_t P = (uint64_t)a.P;
+  const uint64_t r1 = mod_small(h >> 32, P, a.inv_p);
+  return mod_small(r1 * a.two32_p + (h & 0xFFFFFFFFull), P, a.inv_p);
 }
 
 template <int EB>
@@ -88,14 +111,23 @@ struct Elems<4> {
   }
 };
 
-// Four tokens per block, one per wave.
-template <int EB>
+// Four tokens per block, one per wave; SPL = 16-byte slices of a token per lane.
+template <int EB, int SPL>
 __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
   using EL = Elems<EB>;
   constexpr int E = EL::E;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ int32_t rows_s[4][MAX_ORDERS * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= a.T) return;
+
+  // slices of this lane and its hidden-state values (independent of the hashes)
+  u32x4 hv[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int s = lane + 64 * i;
+    hv[i] = s < a.slices ? *(const u32x4*)(a.h + ((size_t)t * a.slices + s) * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
 
   // ids of the longest n-gram ending at t, oldest first; before the sequence start: 0
   const int nmax = a.min_order + a.n_orders - 1;
@@ -107,12 +139,22 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
     tok[i] = (i >= MAX_ORDER - nmax && j >= start) ? norm_id(a, j) : 0ull;
   }
 
-  // this lane's slices: s = lane + 64 i, head s / head_vecs, column s % head_vecs
+  // lane p hashes (order, head) pair p = o * heads + k into the row of the stacked table
+  const int pairs = a.n_orders * a.heads;
+  for (int p = lane; p < pairs; p += 64) {
+    const int o = p / a.heads;
+    const uint64_t phi = mod_p(fold(tok, a.min_order + o, a.mult[p]), a);
+    rows_s[wv][p] = (int32_t)((int64_t)p * a.P + (int64_t)phi);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // every row of this lane's slices in flight at once
   const size_t row_bytes = (size_t)a.head_vecs * 16;
-  u32x4 v[MAX_ORDERS][MAX_SPL];
-  u32x4 hv[MAX_SPL];
+  u32x4 v[MAX_ORDERS][SPL];
 #pragma unroll
-  for (int i = 0; i < MAX_SPL; ++i) {
+  for (int i = 0; i < SPL; ++i) {
     const int s = lane + 64 * i;
     const bool ok = s < a.slices;
     const int k = ok ? s / a.head_vecs : 0;
@@ -121,20 +163,17 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
     for (int o = 0; o < MAX_ORDERS; ++o) {
       v[o][i] = u32x4{0u, 0u, 0u, 0u};
       if (ok && o < a.n_orders) {
-        const uint64_t m = a.mult[o * a.heads + k];
-        const uint64_t phi = fold(tok, a.min_order + o, m) % (uint64_t)a.P;
-        const int64_t row = ((int64_t)o * a.heads + k) * a.P + (int64_t)phi;
+        const int64_t row = rows_s[wv][o * a.heads + k];
         v[o][i] = __builtin_nontemporal_load((const u32x4*)(a.tables + (size_t)row * row_bytes + (size_t)col * 16));
       }
     }
-    hv[i] = ok ? *(const u32x4*)(a.h + ((size_t)t * a.slices + s) * 16) : u32x4{0u, 0u, 0u, 0u};
   }
 
   // e = sum over orders (fp32, order 0 first); the three sums of the gate
-  float e[MAX_SPL][E], hf[MAX_SPL][E];
+  float e[SPL][E], hf[SPL][E];
   float ee = 0.f, hh = 0.f, eh = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAX_SPL; ++i) {
+  for (int i = 0; i < SPL; ++i) {
 #pragma unroll
     for (int x = 0; x < E; ++x) e[i][x] = 0.f;
 #pragma unroll
@@ -160,7 +199,7 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
   const float alpha = 1.0f / (1.0f + __expf(-z));
 
 #pragma unroll
-  for (int i = 0; i < MAX_SPL; ++i) {
+  for (int i = 0; i < SPL; ++i) {
     const int s = lane + 64 * i;
     if (s >= a.slices) continue;
     float o[E];
@@ -189,7 +228,7 @@ __global__ void __launch_bounds__(256) engram_hash_kernel(EngramArgs a, int32_t*
   const uint64_t m = a.mult[o * a.heads + k];
   uint64_t hh = 0;
   for (int64_t j = t - n + 1; j <= t; ++j) hh = (hh ^ (j >= start ? norm_id(a, j) : 0ull)) * m;
-  rows[i] = (int32_t)(((int64_t)o * a.heads + k) * a.P + (int64_t)(hh % (uint64_t)a.P));
+  rows[i] = (int32_t)(((int64_t)o * a.heads + k) * a.P + (int64_t)mod_p(hh, a));
 }
 
 std::string check_engram(const engram_config* c) {
@@ -237,6 +276,8 @@ int prepare(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t seq
   a.d = cfg->n_heads * cfg->head_dim;
   a.residual = cfg->residual;
   a.eps = cfg->norm_eps;
+  a.inv_p = 1.0 / (double)cfg->table_rows;
+  a.two32_p = ((uint64_t)1 << 32) % (uint64_t)cfg->table_rows;
   return PKM_OK;
 }
 
@@ -289,10 +330,16 @@ int engram_forward(const engram_config* cfg, const void* tables, const int32_t* 
   a.e_out = e_out;
   a.alpha_out = alpha_out;
   const dim3 grid((unsigned)((T + 3) / 4));
-  if (cfg->dtype == PKM_BF16)
-    PKM_LAUNCH((pkm::engram_forward_kernel<2><<<grid, 256, 0, (hipStream_t)stream>>>(a), hipGetLastError()));
-  else
-    PKM_LAUNCH((pkm::engram_forward_kernel<4><<<grid, 256, 0, (hipStream_t)stream>>>(a), hipGetLastError()));
+  const int spl = (a.slices + 63) / 64;  // 1..4
+  hipStream_t s = (hipStream_t)stream;
+#define PKM_ENGRAM(EBV, SPLV) \
+  PKM_LAUNCH((pkm::engram_forward_kernel<EBV, SPLV><<<grid, 256, 0, s>>>(a), hipGetLastError()))
+  if (cfg->dtype == PKM_BF16) {
+    if (spl == 1) PKM_ENGRAM(2, 1); else if (spl == 2) PKM_ENGRAM(2, 2); else PKM_ENGRAM(2, 4);
+  } else {
+    if (spl == 1) PKM_ENGRAM(4, 1); else if (spl == 2) PKM_ENGRAM(4, 2); else PKM_ENGRAM(4, 4);
+  }
+#undef PKM_ENGRAM
   return PKM_OK;
 }
 
