@@ -127,3 +127,40 @@ ENGRAM_CONFIGS = {
 }
 
 ENGRAM_HEADLINE = "engram_zipf_2m_bf16"
+
+
+@dataclass(frozen=True)
+class MemoryAttentionConfig:
+    """Token-memory values of Memory Attention: a per-layer table E [vocab, d_v] read by
+    token id, normalised per key/value head and added to the keys (V = K + Norm(E)[s])."""
+    name: str
+    T: int            # tokens (batch x sequence)
+    vocab: int        # rows of the table
+    d_v: int          # value width = n_heads * head_dim
+    n_heads: int      # key/value heads; the norm runs over each head's slice of a row
+    dtype: str        # "f32" or "bf16": E, K, V
+    zipf_s: float = 1.1   # token ids follow a truncated Zipf law
+    gain: bool = True     # a per-channel RMSNorm gain (fp32, [d_v])
+    norm_eps: float = 1e-6
+
+    @property
+    def head_dim(self) -> int:
+        return self.d_v // self.n_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def with_(self, **kw) -> "MemoryAttentionConfig":
+        return replace(self, **kw)
+
+
+MA_CONFIGS = {
+    # the inference setting the page measures: hidden 2,048 with 32 key/value heads,
+    # a 32,000-token vocabulary, batch 8 x 2,048 prefill tokens
+    "ma_values_32k_bf16": MemoryAttentionConfig("ma_values_32k_bf16", T=16384, vocab=32000, d_v=2048, n_heads=32,
+                                                dtype="bf16"),
+    "ma_tiny_f32": MemoryAttentionConfig("ma_tiny_f32", T=300, vocab=700, d_v=96, n_heads=3, dtype="f32"),
+}
+
+MA_HEADLINE = "ma_values_32k_bf16"

@@ -189,3 +189,22 @@ def make_engram_inputs(cfg, seed: int = 0, T: int | None = None) -> dict:
         "compress": compress_map(seed, cfg.vocab, cfg.n_concepts) if cfg.n_concepts else None,
     }
     return d
+
+
+# ---- Memory Attention token-memory inputs ------------------------------------------
+
+TID_MA_TABLE, TID_MA_KEYS, TID_MA_GAIN = 13, 14, 15
+
+
+def make_ma_inputs(cfg, seed: int = 0, T: int | None = None) -> dict:
+    """ids [T] int32 (Zipf), E [vocab, d_v] ~ N(0, 0.02^2) (stored dtype), K [T, d_v] ~ N(0, 1),
+    gain [d_v] float32 ~ 1 + N(0, 0.1^2) (or None)."""
+    T = cfg.T if T is None else T
+    full = max(T, cfg.T)
+    return {
+        "ids": zipf_tokens(seed, full, cfg.vocab, cfg.zipf_s)[:T].copy(),
+        "E": normal_tensor(seed, TID_MA_TABLE, (cfg.vocab, cfg.d_v), 0.02, cfg.dtype),
+        "K": np.ascontiguousarray(normal_tensor(seed, TID_MA_KEYS, (full, cfg.d_v), 1.0, cfg.dtype)[:T]),
+        "gain": ((1.0 + 0.1 * np.random.default_rng([seed, TID_MA_GAIN]).standard_normal(cfg.d_v)).astype(np.float32)
+                 if cfg.gain else None),
+    }
