@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload memplus_16m_bf16]
     python bench.py --workload engram_zipf_2m_bf16     # the hashed n-gram lookup
+    python bench.py --workload ma_values_32k_bf16      # Memory Attention token-memory values
 
 A step is one whole forward (projection, qk-norm, scoring + per-half top-k,
 combine + softmax, weighted EmbeddingBag over the value table, Memory+ gate) over
@@ -255,6 +256,82 @@ def bench_engram(a):
     print(json.dumps(res), flush=True)
 
 
+def bench_ma(a):
+    """Memory Attention token-memory values: one step = ma_values over the workload's tokens
+    (the table fold runs once, before the timing)."""
+    import numpy as np
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import configs as C
+    from synth import inputs as S
+    from tests.gpu_util import TORCH_DT, to_dev
+
+    cfg = C.MA_CONFIGS[a.workload]
+    T, eb = cfg.T, cfg.elem_bytes
+    log(f"workload {cfg.name}: T={T}, vocab={cfg.vocab}, d_v={cfg.d_v}, {cfg.n_heads} heads, {cfg.dtype}")
+    d = S.make_ma_inputs(cfg, a.seed)
+    E = to_dev(d["E"], cfg.dtype)
+    gain = torch.from_numpy(d["gain"]).cuda() if d["gain"] is not None else None
+    P.ma_fold_table(E, cfg.vocab, cfg.d_v, cfg.n_heads, gain, cfg.norm_eps, cfg.dtype, E)
+    ids = torch.from_numpy(d["ids"]).cuda()
+    K = to_dev(d["K"], cfg.dtype)
+    V = torch.empty((T, cfg.d_v), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: P.ma_values(E, cfg.vocab, cfg.d_v, cfg.dtype, ids, T, K, V, stream=stream)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = e0.elapsed_time(e1) / a.steps
+    alg_b = T * (3 * cfg.d_v * eb + 4)          # K row, table row, V row, id
+    uniq = len(np.unique(d["ids"]))
+    achieved = alg_b / (launch_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        from oracle import ma as M
+        from oracle import pkm as O
+        Eh = d["E"]
+
+        def orc(n):
+            t1 = time.perf_counter()
+            Eb = M.store(M.fold_table(O.to_f64(Eh, cfg.dtype), cfg.n_heads, d["gain"], cfg.norm_eps), cfg.dtype)
+            t2 = time.perf_counter()
+            M.values(Eb, d["ids"][:n], d["K"][:n], cfg.dtype)
+            return t2 - t1, time.perf_counter() - t2
+
+        fold_s, per = orc(256)
+        n = int(max(256, min(T, a.cpu_seconds / max(per / 256, 1e-9))))
+        _, dt = orc(n)
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"first {n} of {T} tokens of {cfg.name}, float64 NumPy oracle, {dt:.2f} s "
+                         f"(the one-off table fold, {fold_s:.1f} s, not counted)"}
+
+    res = {
+        "metric": "Memory Attention token-memory values tokens/s + HBM GB/s, 1 MI355X",
+        "value": T * a.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": elapsed / a.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (Zipf(1.1) token ids, Gaussian keys and table)",
+        "config": {"workload": cfg.name, "tokens": T, "vocab": cfg.vocab, "d_v": cfg.d_v, "heads": cfg.n_heads,
+                   "table_MiB": cfg.vocab * cfg.d_v * eb / 2**20},
+        "roofline": {"bound": "hbm", "kernel": "ma_values (k = 1 lookup + add)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": launch_ms},
+        "unique_ids": uniq,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +351,8 @@ def main():
     from synth import configs as C
     if a.workload in C.ENGRAM_CONFIGS:
         return bench_engram(a)
+    if a.workload in C.MA_CONFIGS:
+        return bench_ma(a)
 
     import torch
 

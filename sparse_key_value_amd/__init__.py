@@ -3,7 +3,8 @@
 The forward ("Memory Layers at Scale": a product-key memory layer in place of an
 FFN) runs entirely in the HIP kernels of ``libpkm.so`` behind the C ABI of
 ``include/pkm.h``, and so does the hashed n-gram lookup (Engram review: multi-head
-hashing and the context-aware gate) behind ``include/engram.h``; this package only
+hashing and the context-aware gate) behind ``include/engram.h`` and the Memory
+Attention token-memory values (V = K + folded table row) behind ``include/ma.h``; this package only
 marshals arguments (``_lib``) and manages device memory with PyTorch
 (``ProductKeyMemory``).
 """
@@ -15,7 +16,7 @@ from ._lib import (  # noqa: F401
     PkmError, make_config, pkm_config, pkm_copy_normalized_subkeys, pkm_create, pkm_debug_ptrs, pkm_destroy,
     pkm_embedding_bag, pkm_enable_stage_timing, pkm_forward, pkm_forward_debug, pkm_last_error, pkm_select,
     pkm_set_pipeline_chunks, pkm_stage_times, pkm_workspace_size,
-    engram_config, engram_forward, engram_hash, make_engram_config,
+    engram_config, engram_forward, engram_hash, make_engram_config, ma_fold_table, ma_values,
 )
 
 

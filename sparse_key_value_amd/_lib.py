@@ -1,4 +1,5 @@
-"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h`` and ``include/engram.h``).
+"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h``, ``include/engram.h`` and
+``include/ma.h``).
 
 Argument marshalling only: every function has the name of the C entry point it
 calls, takes torch tensors (or raw device addresses as ints, or None for NULL)
@@ -65,6 +66,8 @@ _sig = {
     "engram_hash": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "engram_forward": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp]),
+    "ma_fold_table": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
+    "ma_values": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -186,3 +189,14 @@ def engram_forward(cfg: engram_config, tables, ids, T: int, seq_len: int, compre
                    alpha_out=None, stream=None) -> None:
     _check(_lib.engram_forward(ctypes.byref(cfg), _ptr(tables), _ptr(ids), T, seq_len, _ptr(compress), _ptr(mult),
                                _ptr(h), _ptr(out), _ptr(e_out), _ptr(alpha_out), _stream(stream)), "engram_forward")
+
+
+def ma_fold_table(E, vocab: int, d_v: int, n_heads: int, gain, eps: float, dtype, E_bar, stream=None) -> None:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    _check(_lib.ma_fold_table(_ptr(E), vocab, d_v, n_heads, _ptr(gain), eps, dt, _ptr(E_bar), _stream(stream)),
+           "ma_fold_table")
+
+
+def ma_values(E_bar, vocab: int, d_v: int, dtype, ids, T: int, K, V, stream=None) -> None:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    _check(_lib.ma_values(_ptr(E_bar), vocab, d_v, dt, _ptr(ids), T, _ptr(K), _ptr(V), _stream(stream)), "ma_values")

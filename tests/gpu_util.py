@@ -39,14 +39,17 @@ class Workload:
     """Inputs of one workload on the GPU plus a handle over them."""
 
     def __init__(self, cfg, seed: int = 0, T: int | None = None, max_tokens: int | None = None,
-                 values: torch.Tensor | None = None, host_inputs: dict | None = None):
+                 values: torch.Tensor | None = None, host_inputs: dict | None = None, value_seed: int | None = None):
+        """``values`` (with the ``value_seed`` it was filled from) shares one value table
+        between several workloads (a shared memory pool)."""
         import sparse_key_value_amd as P
 
         self.cfg, self.seed = cfg, seed
+        self.value_seed = seed if value_seed is None else value_seed
         self.T = cfg.T if T is None else T
         self.inp = host_inputs if host_inputs is not None else S.make_inputs(cfg, seed, T=self.T)
         self.dev = {k: to_dev(v, cfg.dtype) for k, v in self.inp.items()}
-        self.values = values if values is not None else make_value_table(cfg, seed)
+        self.values = values if values is not None else make_value_table(cfg, self.value_seed)
         self.pkm = P.ProductKeyMemory(
             d_model=cfg.d_model, n_heads=cfg.H, d_query=cfg.d_q, n_sub=cfg.n_sub, k=cfg.k, d_value=cfg.d_v,
             dtype=cfg.dtype, qk_norm=cfg.qk_norm, memory_plus=cfg.memory_plus,
@@ -55,7 +58,7 @@ class Workload:
 
     def host_rows(self, rows) -> np.ndarray:
         """Stored value rows as generated on the host (float32 or bf16 bits)."""
-        return S.value_rows(self.seed, rows, self.cfg.d_v, self.cfg.dtype)
+        return S.value_rows(self.value_seed, rows, self.cfg.d_v, self.cfg.dtype)
 
     def forward_debug(self, x: torch.Tensor | None = None):
         import sparse_key_value_amd as P

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared(header):
     txt = open(os.path.join(ROOT, "include", header)).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:pkm|engram)_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b((?:pkm|engram|ma)_[a-z_]+)\s*\(", txt)))
 
 
 @pytest.fixture(scope="module")
@@ -25,9 +25,10 @@ def P():
 def test_library_exports_every_declared_symbol(P):
     lib = ctypes.CDLL(P.LIB_PATH)
     headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
-    assert headers == ["engram.h", "pkm.h"]
+    assert headers == ["engram.h", "ma.h", "pkm.h"]
     names = sorted(set(n for hd in headers for n in _declared(hd)))
-    assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag", "engram_hash", "engram_forward"} <= set(names)
+    assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag", "engram_hash", "engram_forward",
+            "ma_fold_table", "ma_values"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/pkm.h but not exported"
     assert set(names) == set(P.EXPORTED), "binding and header disagree"
@@ -164,3 +165,21 @@ def test_engram_argument_errors_before_any_device_call(P):
     # T = 0 is a no-op that needs no pointers
     assert lib.engram_hash(ctypes.byref(c), None, 0, 4, None, None, None, None) == P.PKM_OK
     assert lib.engram_forward(ctypes.byref(c), None, None, 0, 4, None, None, None, None, None, None, None) == P.PKM_OK
+
+
+def test_ma_argument_errors_before_any_device_call(P):
+    lib = P._lib._lib
+    f, v = lib.ma_fold_table, lib.ma_values
+    assert f(256, 10, 64, 4, None, 1e-6, 2, 256, None) == P.PKM_EINVAL and "dtype" in P.pkm_last_error()
+    assert f(256, 10, 12, 1, None, 1e-6, 1, 256, None) == P.PKM_EINVAL and "d_v" in P.pkm_last_error()
+    assert f(256, 10, 64, 3, None, 1e-6, 1, 256, None) == P.PKM_EINVAL and "n_heads" in P.pkm_last_error()
+    assert f(256, 10, 64, 16, None, 1e-6, 1, 256, None) == P.PKM_EINVAL   # 4 bf16 per head = 8 bytes
+    assert f(256, 10, 64, 4, None, -1.0, 1, 256, None) == P.PKM_EINVAL and "eps" in P.pkm_last_error()
+    assert f(None, 10, 64, 4, None, 1e-6, 1, 256, None) == P.PKM_EINVAL
+    assert f(8, 10, 64, 4, None, 1e-6, 1, 256, None) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
+    assert f(None, 0, 64, 4, None, 1e-6, 1, None, None) == P.PKM_OK
+    assert v(256, 0, 64, 1, 256, 4, 256, 256, None) == P.PKM_EINVAL and "vocab" in P.pkm_last_error()
+    assert v(256, 10, 64, 1, None, 4, 256, 256, None) == P.PKM_EINVAL
+    assert v(256, 10, 64, 1, 256, -1, 256, 256, None) == P.PKM_EINVAL
+    assert v(256, 10, 64, 1, 256, 4, 264, 256, None) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
+    assert v(None, 10, 64, 1, None, 0, None, None, None) == P.PKM_OK
