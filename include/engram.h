@@ -78,6 +78,29 @@ int engram_forward(const engram_config* cfg, const void* tables, const int32_t* 
                    const int32_t* compress, const uint64_t* mult, const void* h, void* out, float* e_out,
                    float* alpha_out, void* stream);
 
+/* Host-resident tables with prefetch (review of "Conditional Memory via Scalable
+ * Lookup" (Engram): the tables can live in host memory at a small cost in throughput;
+ * summary of "Memory Attention", how it is used: the lookup addresses depend only on
+ * token ids, so the rows can be fetched before the hidden state that needs them).
+ *
+ * engram_prefetch computes the rows of every (token, order, head) exactly as
+ * engram_forward does and copies them, in their stored type, to
+ *   staged [T, n_orders, d] dtype (device memory): staged[t, o, k*head_dim + i] =
+ *          tables[row_{t,k,o}][i]
+ * `tables` may be device memory or pinned host memory (allocated with hipHostMalloc,
+ * or a pinned torch tensor): the kernel then reads it over the host link.  Pageable
+ * host memory is refused (PKM_EINVAL).  Launch it early on a side stream and order
+ * engram_forward_staged after it with an event.
+ *
+ * engram_forward_staged computes e_t (the sum over orders of staged[t, o, :]), the gate
+ * and the output exactly as engram_forward does (same arithmetic in the same order, so
+ * the results are bitwise equal); h, out, e_out, alpha_out as for engram_forward.
+ * T = 0 is a no-op for both. */
+int engram_prefetch(const engram_config* cfg, const void* tables, const int32_t* ids, int64_t T, int64_t seq_len,
+                    const int32_t* compress, const uint64_t* mult, void* staged, void* stream);
+int engram_forward_staged(const engram_config* cfg, const void* staged, const void* h, int64_t T, void* out,
+                          float* e_out, float* alpha_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,8 @@ _sig = {
     "engram_hash": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "engram_forward": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp]),
+    "engram_prefetch": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "engram_forward_staged": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
     "ma_fold_table": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
     "ma_values": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -189,6 +191,16 @@ def engram_forward(cfg: engram_config, tables, ids, T: int, seq_len: int, compre
                    alpha_out=None, stream=None) -> None:
     _check(_lib.engram_forward(ctypes.byref(cfg), _ptr(tables), _ptr(ids), T, seq_len, _ptr(compress), _ptr(mult),
                                _ptr(h), _ptr(out), _ptr(e_out), _ptr(alpha_out), _stream(stream)), "engram_forward")
+
+
+def engram_prefetch(cfg: engram_config, tables, ids, T: int, seq_len: int, compress, mult, staged, stream=None) -> None:
+    _check(_lib.engram_prefetch(ctypes.byref(cfg), _ptr(tables), _ptr(ids), T, seq_len, _ptr(compress), _ptr(mult),
+                                _ptr(staged), _stream(stream)), "engram_prefetch")
+
+
+def engram_forward_staged(cfg: engram_config, staged, h, T: int, out, e_out=None, alpha_out=None, stream=None) -> None:
+    _check(_lib.engram_forward_staged(ctypes.byref(cfg), _ptr(staged), _ptr(h), T, _ptr(out), _ptr(e_out),
+                                      _ptr(alpha_out), _stream(stream)), "engram_forward_staged")
 
 
 def ma_fold_table(E, vocab: int, d_v: int, n_heads: int, gain, eps: float, dtype, E_bar, stream=None) -> None:

@@ -43,6 +43,14 @@ struct EngramArgs {
   float eps;
   double inv_p;      // 1 / P, rounded
   uint64_t two32_p;  // 2^32 mod P
+  uint8_t* staged;   // [T, n_orders, d] rows copied ahead of use (prefetch / staged modes)
+};
+
+// What one launch of the token kernel does.
+enum Mode {
+  FULL = 0,      // hash, read the table rows, gate, write the output
+  PREFETCH = 1,  // hash, read the table rows (e.g. from host memory), write them to `staged`
+  STAGED = 2,    // read the rows from `staged`, gate, write the output
 };
 
 // The id the hash sees (ids outside [0, vocab) read as 0; optional vocabulary map).
@@ -112,7 +120,7 @@ struct Elems<4> {
 };
 
 // Four tokens per block, one per wave; SPL = 16-byte slices of a token per lane.
-template <int EB, int SPL>
+template <int EB, int SPL, int MODE>
 __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
   using EL = Elems<EB>;
   constexpr int E = EL::E;
@@ -126,9 +134,22 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
     const int s = lane + 64 * i;
-    hv[i] = s < a.slices ? *(const u32x4*)(a.h + ((size_t)t * a.slices + s) * 16) : u32x4{0u, 0u, 0u, 0u};
+    hv[i] = (MODE != PREFETCH && s < a.slices) ? *(const u32x4*)(a.h + ((size_t)t * a.slices + s) * 16)
+                                               : u32x4{0u, 0u, 0u, 0u};
   }
 
+  u32x4 v[MAX_ORDERS][SPL];
+  if constexpr (MODE == STAGED) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int s = lane + 64 * i;
+#pragma unroll
+      for (int o = 0; o < MAX_ORDERS; ++o)
+        v[o][i] = (s < a.slices && o < a.n_orders)
+                      ? __builtin_nontemporal_load((const u32x4*)(a.staged + (((size_t)t * a.n_orders + o) * a.slices + s) * 16))
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
   // ids of the longest n-gram ending at t, oldest first; before the sequence start: 0
   const int nmax = a.min_order + a.n_orders - 1;
   const int64_t start = t - t % a.seq_len;
@@ -152,7 +173,6 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
 
   // every row of this lane's slices in flight at once
   const size_t row_bytes = (size_t)a.head_vecs * 16;
-  u32x4 v[MAX_ORDERS][SPL];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
     const int s = lane + 64 * i;
@@ -167,6 +187,19 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
         v[o][i] = __builtin_nontemporal_load((const u32x4*)(a.tables + (size_t)row * row_bytes + (size_t)col * 16));
       }
     }
+  }
+  if constexpr (MODE == PREFETCH) {
+    // the rows of order o, head k land where the staged mode reads them: [t, o, slice]
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int s = lane + 64 * i;
+#pragma unroll
+      for (int o = 0; o < MAX_ORDERS; ++o)
+        if (s < a.slices && o < a.n_orders)
+          __builtin_nontemporal_store(v[o][i], (u32x4*)(a.staged + (((size_t)t * a.n_orders + o) * a.slices + s) * 16));
+    }
+    return;
+  }
   }
 
   // e = sum over orders (fp32, order 0 first); the three sums of the gate
@@ -281,6 +314,51 @@ int prepare(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t seq
   return PKM_OK;
 }
 
+// One launch of the token kernel: four tokens per block, instantiated per element size,
+// slices per lane (1, 2 or 4) and mode.
+template <int MODE>
+int launch_mode(int dtype, const EngramArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + 3) / 4));
+  const int spl = (a.slices + 63) / 64;  // 1..4
+#define PKM_ENGRAM(EBV, SPLV) \
+  PKM_LAUNCH((engram_forward_kernel<EBV, SPLV, MODE><<<grid, 256, 0, s>>>(a), hipGetLastError()))
+  if (dtype == PKM_BF16) {
+    if (spl == 1) PKM_ENGRAM(2, 1); else if (spl == 2) PKM_ENGRAM(2, 2); else PKM_ENGRAM(2, 4);
+  } else {
+    if (spl == 1) PKM_ENGRAM(4, 1); else if (spl == 2) PKM_ENGRAM(4, 2); else PKM_ENGRAM(4, 4);
+  }
+#undef PKM_ENGRAM
+  return PKM_OK;
+}
+
+int launch_tokens(int dtype, int mode, const EngramArgs& a, hipStream_t s) {
+  if (mode == PREFETCH) return launch_mode<PREFETCH>(dtype, a, s);
+  if (mode == STAGED) return launch_mode<STAGED>(dtype, a, s);
+  return launch_mode<FULL>(dtype, a, s);
+}
+
+// The address at which kernels read `p`: device memory as is, pinned host memory through
+// its device mapping; anything else (pageable host memory) is refused.
+int device_view(const void* p, const void** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return pkm_abi::fail(PKM_EINVAL, "tables are neither device memory nor pinned host memory");
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PKM_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    PKM_HIP(hipHostGetDevicePointer(&d, const_cast<void*>(p), 0));
+    if (!d) return pkm_abi::fail(PKM_EINVAL, "pinned host tables have no device mapping");
+    *out = d;
+    return PKM_OK;
+  }
+  return pkm_abi::fail(PKM_EINVAL, "tables must be device memory or pinned host memory (e.g. hipHostMalloc)");
+}
+
 // The device check once per device and process.
 int device_ok() {
   static int state[64] = {};  // 0 unknown, 1 gfx950
@@ -329,18 +407,47 @@ int engram_forward(const engram_config* cfg, const void* tables, const int32_t* 
   a.out = (uint8_t*)out;
   a.e_out = e_out;
   a.alpha_out = alpha_out;
-  const dim3 grid((unsigned)((T + 3) / 4));
-  const int spl = (a.slices + 63) / 64;  // 1..4
-  hipStream_t s = (hipStream_t)stream;
-#define PKM_ENGRAM(EBV, SPLV) \
-  PKM_LAUNCH((pkm::engram_forward_kernel<EBV, SPLV><<<grid, 256, 0, s>>>(a), hipGetLastError()))
-  if (cfg->dtype == PKM_BF16) {
-    if (spl == 1) PKM_ENGRAM(2, 1); else if (spl == 2) PKM_ENGRAM(2, 2); else PKM_ENGRAM(2, 4);
-  } else {
-    if (spl == 1) PKM_ENGRAM(4, 1); else if (spl == 2) PKM_ENGRAM(4, 2); else PKM_ENGRAM(4, 4);
-  }
-#undef PKM_ENGRAM
-  return PKM_OK;
+  return pkm::launch_tokens(cfg->dtype, pkm::FULL, a, (hipStream_t)stream);
+}
+
+int engram_prefetch(const engram_config* cfg, const void* tables, const int32_t* ids, int64_t T, int64_t seq_len,
+                    const int32_t* compress, const uint64_t* mult, void* staged, void* stream) {
+  pkm::EngramArgs a;
+  int rc = pkm::prepare(cfg, ids, T, seq_len, compress, mult, a);
+  if (rc != PKM_OK) return rc;
+  if (T == 0) return PKM_OK;
+  if (!tables || !staged) return pkm_abi::fail(PKM_EINVAL, "tables and staged must not be NULL");
+  if ((((uintptr_t)tables | (uintptr_t)staged) & 15) != 0)
+    return pkm_abi::fail(PKM_EINVAL, "tables and staged must be 16-byte aligned");
+  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
+  const void* view = nullptr;
+  if ((rc = pkm::device_view(tables, &view)) != PKM_OK) return rc;
+  a.tables = (const uint8_t*)view;
+  a.staged = (uint8_t*)staged;
+  return pkm::launch_tokens(cfg->dtype, pkm::PREFETCH, a, (hipStream_t)stream);
+}
+
+int engram_forward_staged(const engram_config* cfg, const void* staged, const void* h, int64_t T, void* out,
+                          float* e_out, float* alpha_out, void* stream) {
+  pkm::EngramArgs a;
+  // the hash inputs are not read in this mode: any non-NULL placeholders pass the checks
+  static const int32_t dummy_ids = 0;
+  static const uint64_t dummy_mult = 1;
+  int rc = pkm::prepare(cfg, &dummy_ids, T, 1, nullptr, &dummy_mult, a);
+  if (rc != PKM_OK) return rc;
+  if (T == 0) return PKM_OK;
+  if (!staged || !h || !out) return pkm_abi::fail(PKM_EINVAL, "staged, h and out must not be NULL");
+  if ((((uintptr_t)staged | (uintptr_t)h | (uintptr_t)out | (uintptr_t)e_out) & 15) != 0)
+    return pkm_abi::fail(PKM_EINVAL, "staged, h, out and e_out must be 16-byte aligned");
+  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
+  a.ids = nullptr;
+  a.mult = nullptr;
+  a.staged = (uint8_t*)staged;
+  a.h = (const uint8_t*)h;
+  a.out = (uint8_t*)out;
+  a.e_out = e_out;
+  a.alpha_out = alpha_out;
+  return pkm::launch_tokens(cfg->dtype, pkm::STAGED, a, (hipStream_t)stream);
 }
 
 }  // extern "C"

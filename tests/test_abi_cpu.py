@@ -162,6 +162,13 @@ def test_engram_argument_errors_before_any_device_call(P):
     assert lib.engram_forward(ctypes.byref(c), None, 256, 4, 4, None, 256, 256, 256, None, None, None) == P.PKM_EINVAL
     assert lib.engram_forward(ctypes.byref(c), 256, 256, 4, 4, None, 256, 264, 256, None, None, None) == P.PKM_EINVAL
     assert "16-byte" in P.pkm_last_error()
+    pf, st = lib.engram_prefetch, lib.engram_forward_staged
+    assert pf(ctypes.byref(c), None, 256, 4, 4, None, 256, 256, None) == P.PKM_EINVAL
+    assert pf(ctypes.byref(c), 256, 256, 4, 4, None, 256, 8, None) == P.PKM_EINVAL and "16-byte" in P.pkm_last_error()
+    assert st(ctypes.byref(c), None, 256, 4, 256, None, None, None) == P.PKM_EINVAL
+    assert st(ctypes.byref(c), 256, 256, 4, 256, 8, None, None) == P.PKM_EINVAL and "16-byte" in P.pkm_last_error()
+    assert pf(ctypes.byref(c), None, None, 0, 4, None, None, None, None) == P.PKM_OK
+    assert st(ctypes.byref(c), None, None, 0, None, None, None, None) == P.PKM_OK
     # T = 0 is a no-op that needs no pointers
     assert lib.engram_hash(ctypes.byref(c), None, 0, 4, None, None, None, None) == P.PKM_OK
     assert lib.engram_forward(ctypes.byref(c), None, None, 0, 4, None, None, None, None, None, None, None) == P.PKM_OK

@@ -185,3 +185,66 @@ def test_engram_full_size_as_benchmarked():
     out, e, a = L.forward()
     assert np.all((a > 0) & (a < 1)) and np.isfinite(e).all()
     del L
+
+
+def _staged(L, tables):
+    from tests.gpu_util import TORCH_DT
+    cfg = L.cfg
+    st = torch.full((L.T, cfg.n_orders, cfg.d), float("nan"), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    L.P.engram_prefetch(L.ecfg, tables, L.ids, L.T, cfg.seq_len, L.compress, L.mult, st)
+    out = torch.empty((L.T, cfg.d), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    e = torch.empty((L.T, cfg.d), dtype=torch.float32, device="cuda")
+    a = torch.empty((L.T,), dtype=torch.float32, device="cuda")
+    L.P.engram_forward_staged(L.ecfg, st, L.h, L.T, out, e, a)
+    torch.cuda.synchronize()
+    return _to_host(st), _to_host(out), e.cpu().numpy(), a.cpu().numpy()
+
+
+def _check_staged(L, staged, out, e, a):
+    """Staged rows are the oracle's table rows bitwise; the staged lookup equals the direct one bitwise."""
+    cfg = L.cfg
+    rows = E.hash_rows(L.inp["ids"], cfg.seq_len, L.inp["mult"], cfg.table_rows, cfg.min_order, cfg.vocab,
+                       L.inp["compress"])                                      # [T, heads, orders]
+    want = S.engram_table_rows(L.seed, rows.transpose(0, 2, 1).reshape(-1), cfg.head_dim, cfg.dtype)
+    np.testing.assert_array_equal(np.asarray(staged).reshape(L.T, cfg.n_orders, cfg.heads, cfg.head_dim),
+                                  want.reshape(L.T, cfg.n_orders, cfg.heads, cfg.head_dim), err_msg="staged rows")
+    o2, e2, a2 = L.forward()
+    for x, y, n in ((out, o2, "out"), (e, e2, "e"), (a, a2, "alpha")):
+        np.testing.assert_array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8), err_msg=n)
+
+
+@pytest.mark.parametrize("name", ["engram_tiny_f32", "engram_compress_bf16"])
+def test_engram_prefetch_from_device_tables(name):
+    cfg = C.ENGRAM_CONFIGS[name]
+    say(f"engram prefetch (device tables) {name}")
+    L = Lookup(cfg, seed=3)
+    _check_staged(L, *_staged(L, L.tables))
+
+
+@pytest.mark.parametrize("name", ["engram_compress_bf16", "engram_zipf_2m_bf16"])
+def test_engram_prefetch_from_pinned_host_tables(name):
+    """Tables in pinned host memory, read by the kernel over the host link."""
+    cfg = C.ENGRAM_CONFIGS[name]
+    say(f"engram prefetch (pinned host tables) {name}")
+    L = Lookup(cfg, seed=0)
+    host = torch.empty(L.tables.shape, dtype=L.tables.dtype, pin_memory=True)
+    host.copy_(L.tables)
+    torch.cuda.synchronize()
+    dev = L.tables
+    L.tables = None
+    del dev
+    torch.cuda.empty_cache()
+    staged, out, e, a = _staged(L, host)
+    L.tables = host.cuda()
+    _check_staged(L, staged, out, e, a)
+
+
+def test_engram_prefetch_refuses_pageable_host_memory():
+    import sparse_key_value_amd as P
+    cfg = C.ENGRAM_CONFIGS["engram_tiny_f32"]
+    L = Lookup(cfg, seed=1, T=8)
+    pageable = torch.empty(L.tables.shape, dtype=L.tables.dtype)          # plain host memory
+    st = torch.empty((L.T, cfg.n_orders, cfg.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(P.PkmError) as ex:
+        P.engram_prefetch(L.ecfg, pageable, L.ids, L.T, cfg.seq_len, None, L.mult, st)
+    assert ex.value.code == P.PKM_EINVAL and "pinned" in str(ex.value)
