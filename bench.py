@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload memplus_16m_bf16]
     python bench.py --workload engram_zipf_2m_bf16     # the hashed n-gram lookup
     python bench.py --workload ma_values_32k_bf16      # Memory Attention token-memory values
+    python bench.py --workload engram_zipf_2m_bf16 --tables host   # tables in host memory, prefetched
 
 A step is one whole forward (projection, qk-norm, scoring + per-half top-k,
 combine + softmax, weighted EmbeddingBag over the value table, Memory+ gate) over
@@ -256,6 +257,106 @@ def bench_engram(a):
     print(json.dumps(res), flush=True)
 
 
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction, published
+
+
+def bench_engram_host(a):
+    """Hashed n-gram lookup with the tables in pinned host memory: each step prefetches the
+    next batch's rows over the host link on a side stream while the current batch is gated
+    from its staged rows (two staging buffers)."""
+    import numpy as np
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import configs as C
+    from synth import device as SD
+    from synth import inputs as S
+    from tests.gpu_util import TORCH_DT, to_dev
+
+    cfg = C.ENGRAM_CONFIGS[a.workload]
+    T, eb = cfg.T, cfg.elem_bytes
+    log(f"workload {cfg.name} with host-resident tables: T={T}, {cfg.n_tables} tables x {cfg.table_rows} rows")
+    inp = S.make_engram_inputs(cfg, a.seed)
+    dev_tables = torch.empty((cfg.total_rows, cfg.head_dim), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    SD.fill_values(dev_tables, a.seed, tid=S.TID_ENGRAM)
+    tables = torch.empty(dev_tables.shape, dtype=dev_tables.dtype, pin_memory=True)
+    tables.copy_(dev_tables)
+    torch.cuda.synchronize()
+    del dev_tables
+    torch.cuda.empty_cache()
+    ids = torch.from_numpy(inp["ids"]).cuda()
+    h = to_dev(inp["h"], cfg.dtype)
+    mult = torch.from_numpy(inp["mult"].view(np.int64)).cuda()
+    comp = torch.from_numpy(inp["compress"]).cuda() if inp["compress"] is not None else None
+    out = torch.empty((T, cfg.d), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    staged = [torch.empty((T, cfg.n_orders, cfg.d), dtype=TORCH_DT[cfg.dtype], device="cuda") for _ in range(2)]
+    ec = P.make_engram_config(cfg.min_order, cfg.n_orders, cfg.heads, cfg.head_dim, cfg.table_rows, cfg.vocab,
+                              cfg.dtype, cfg.residual, cfg.norm_eps)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    prefetch = lambda buf, st: P.engram_prefetch(ec, tables, ids, T, cfg.seq_len, comp, mult, buf, stream=st)
+    gate = lambda buf: P.engram_forward_staged(ec, buf, h, T, out, stream=main)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # each part alone, timed with events on the stream it runs on
+    for _ in range(a.warmup):
+        prefetch(staged[0], main)
+        gate(staged[0])
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(main)
+    for _ in range(a.steps):
+        prefetch(staged[0], main)
+    e1.record(main)
+    torch.cuda.synchronize()
+    pf_ms = e0.elapsed_time(e1) / a.steps
+    e0.record(main)
+    for _ in range(a.steps):
+        gate(staged[0])
+    e1.record(main)
+    torch.cuda.synchronize()
+    gate_ms = e0.elapsed_time(e1) / a.steps
+
+    # the pipeline: prefetch of step i + 1 on the side stream beside the gate of step i
+    ready = [torch.cuda.Event(), torch.cuda.Event()]
+    free = [torch.cuda.Event(), torch.cuda.Event()]
+    with torch.cuda.stream(side):
+        prefetch(staged[0], side)
+        ready[0].record(side)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        cur, nxt = i % 2, (i + 1) % 2
+        side.wait_event(free[nxt]) if i > 0 else None
+        prefetch(staged[nxt], side)
+        ready[nxt].record(side)
+        main.wait_event(ready[cur])
+        gate(staged[cur])
+        free[cur].record(main)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    link_b = T * cfg.n_orders * cfg.d * eb           # rows read from host memory per step
+    achieved = link_b / (pf_ms * 1e-3) / 1e9
+    res = {
+        "metric": "Engram hashed n-gram lookup tokens/s, tables in host memory + host-link GB/s, 1 MI355X",
+        "value": T * a.steps / elapsed, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": elapsed / a.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (Zipf(1.1) token ids, Gaussian hidden states, tables generated on the GPU, kept in "
+                "pinned host memory)",
+        "config": {"workload": cfg.name, "tables": "host (pinned)", "tokens": T, "table_GiB":
+                   cfg.total_rows * cfg.head_dim * eb / 2**30, "staging_MiB": link_b / 2**20},
+        "roofline": {"bound": "host-link", "kernel": "engram_prefetch (hash + row copy from host memory)",
+                     "achieved": achieved, "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HOST_LINK_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": link_b,
+                     "avg_launch_ms": pf_ms},
+        "prefetch_ms": pf_ms, "staged_gate_ms": gate_ms,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_ma(a):
     """Memory Attention token-memory values: one step = ma_values over the workload's tokens
     (the table fold runs once, before the timing)."""
@@ -342,6 +443,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
+    ap.add_argument("--tables", choices=["device", "host"], default="device",
+                    help="Engram workloads: keep the tables in HBM or in pinned host memory (prefetched)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the forward has no multi-GPU path "
@@ -350,7 +453,7 @@ def main():
 
     from synth import configs as C
     if a.workload in C.ENGRAM_CONFIGS:
-        return bench_engram(a)
+        return bench_engram_host(a) if a.tables == "host" else bench_engram(a)
     if a.workload in C.MA_CONFIGS:
         return bench_ma(a)
 

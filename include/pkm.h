@@ -122,11 +122,15 @@ size_t pkm_workspace_size(const pkm_config* cfg);
  * valid and unchanged while the handle is used.
  *   W_q      [d_model, H*d_q]   (head h = columns h*d_q .. h*d_q + d_q - 1)
  *   subkeys  [H, 2, n_sub, d_h] (index 0 scores the first query half)
- *   values   [n_sub^2, d_value]
+ *   values   [n_sub^2, d_value]: device memory, or pinned host memory (hipHostMalloc,
+ *            a pinned torch tensor) read by the gather over the host link (a
+ *            host-resident table: the roofline becomes the host link's bandwidth);
+ *            pageable host memory is refused (PKM_EINVAL)
  *   W1       [d_model, d_value], W2 [d_value, d_model]  (NULL unless memory_plus)
  *   workspace: device buffer of ws_bytes >= pkm_workspace_size(cfg), 256-byte
  *            aligned, owned by the caller, used exclusively by this handle.
- * Errors: PKM_EINVAL (bad config or NULL pointer), PKM_EWORKSPACE,
+ * W_q, subkeys, W1, W2 and the workspace must be device memory (checked).
+ * Errors: PKM_EINVAL (bad config, NULL or non-device pointer), PKM_EWORKSPACE,
  * PKM_EUNSUPPORTED (device not gfx950), PKM_EHIP. */
 int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, const void* values,
                const void* W1, const void* W2, void* workspace, size_t ws_bytes, void* stream,
@@ -166,7 +170,8 @@ int pkm_copy_normalized_subkeys(pkm_handle* h, void* dst, void* stream);
  *   y[b, :] = sum over j < bag_size of w[b, j] * table[idx[b, j], :]     (fp32)
  * idx [n_bags, bag_size] int32, w [n_bags, bag_size] fp32, y [n_bags, dim] fp32.
  * Indices outside [0, n_rows) contribute nothing.  dim * sizeof(dtype) must be
- * a multiple of 16 and the table 16-byte aligned.  n_bags = 0 enqueues nothing. */
+ * a multiple of 16 and the table 16-byte aligned; the table may be device memory or
+ * pinned host memory (as `values` of pkm_create).  n_bags = 0 enqueues nothing. */
 int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dtype,
                       const int32_t* idx, const float* w, int64_t n_bags, int32_t bag_size, float* y,
                       void* stream);

@@ -27,7 +27,9 @@ class ProductKeyMemory:
     Tensors (torch, on the GPU, row-major, dtype matching ``dtype``):
       W_q [d_model, H*d_q], subkeys [H, 2, n_sub, d_q/2], values [n_sub^2, d_value],
       W1 [d_model, d_value] and W2 [d_value, d_model] when ``memory_plus``.
-    ``values`` is borrowed: keep it alive and unchanged while this object is used.
+    ``values`` is borrowed: keep it alive and unchanged while this object is used.  It may
+    live in pinned host memory (a host-resident table, read over the host link); the
+    workspace is allocated on W_q's device.
     """
 
     def __init__(self, *, d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
@@ -37,7 +39,7 @@ class ProductKeyMemory:
         self.cfg = make_config(d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
                                norm_eps)
         self.ws_bytes = pkm_workspace_size(self.cfg)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=values.device)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=W_q.device)
         self._keep = (W_q, subkeys, values, W1, W2)
         self.handle = pkm_create(self.cfg, W_q, subkeys, values, W1, W2, self.workspace, self.ws_bytes, stream)
 

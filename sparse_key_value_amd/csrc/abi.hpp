@@ -19,6 +19,14 @@ const char* last_error();
 // PKM_OK if the current device is a gfx950, else PKM_EUNSUPPORTED / PKM_EHIP.
 int check_device();
 
+// The address at which kernels read a table `p`: device memory as is, pinned host
+// memory through its device mapping (the kernels then read it over the host link);
+// anything else (pageable host memory) is refused with PKM_EINVAL naming `what`.
+int device_view(const void* p, const char* what, const void** out);
+
+// PKM_OK if `p` is device memory, else PKM_EINVAL naming `what`.
+int require_device(const void* p, const char* what);
+
 }  // namespace pkm_abi
 
 #define PKM_HIP(call)                                                                                \

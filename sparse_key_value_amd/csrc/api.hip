@@ -41,6 +41,36 @@ int check_device() {
 
 const char* last_error() { return g_err.c_str(); }
 
+int device_view(const void* p, const char* what, const void** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKM_EINVAL, "%s: neither device memory nor pinned host memory", what);
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PKM_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    PKM_HIP(hipHostGetDevicePointer(&d, const_cast<void*>(p), 0));
+    if (!d) return fail(PKM_EINVAL, "%s: pinned host memory without a device mapping", what);
+    *out = d;
+    return PKM_OK;
+  }
+  return fail(PKM_EINVAL, "%s must be device memory or pinned host memory (e.g. hipHostMalloc)", what);
+}
+
+int require_device(const void* p, const char* what) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKM_EINVAL, "%s is not device memory", what);
+  }
+  if (at.type != hipMemoryTypeDevice) return fail(PKM_EINVAL, "%s must be device memory", what);
+  return PKM_OK;
+}
+
 }  // namespace pkm_abi
 
 using pkm_abi::check_device;
@@ -352,12 +382,24 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
     return fail(PKM_EWORKSPACE, "workspace has %zu bytes, the config needs %zu", ws_bytes, L.total);
   int rc = check_device();
   if (rc) return rc;
+  if ((rc = pkm_abi::require_device(workspace, "workspace")) != PKM_OK) return rc;
+  if ((rc = pkm_abi::require_device(W_q, "W_q")) != PKM_OK) return rc;
+  if ((rc = pkm_abi::require_device(subkeys, "subkeys")) != PKM_OK) return rc;
+  if (cfg->memory_plus) {
+    if ((rc = pkm_abi::require_device(W1, "W1")) != PKM_OK) return rc;
+    if ((rc = pkm_abi::require_device(W2, "W2")) != PKM_OK) return rc;
+  }
 
   pkm_handle* h = new (std::nothrow) pkm_handle();
   if (!h) return fail(PKM_EINVAL, "out of host memory");
   h->cfg = *cfg;
   h->d_h = cfg->d_query / 2;
-  h->values = values;
+  const void* vview = nullptr;
+  if ((rc = pkm_abi::device_view(values, "values", &vview)) != PKM_OK) {
+    delete h;
+    return rc;
+  }
+  h->values = vview;
   h->ws = (uint8_t*)workspace;
   h->L = L;
   hipStream_t s = (hipStream_t)stream;
@@ -428,7 +470,10 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
   if (n_bags == 0) return PKM_OK;
   if (!table || !idx || !w || !y) return fail(PKM_EINVAL, "table, idx, w and y must not be NULL");
   if (((uintptr_t)table & 15) != 0) return fail(PKM_EINVAL, "table must be 16-byte aligned");
-  PKM_LAUNCH(pkm::launch_gather(table, n_rows, dim, dtype, idx, w, n_bags, bag_size, y, 0, (hipStream_t)stream));
+  const void* tview = nullptr;
+  const int rc = pkm_abi::device_view(table, "table", &tview);
+  if (rc != PKM_OK) return rc;
+  PKM_LAUNCH(pkm::launch_gather(tview, n_rows, dim, dtype, idx, w, n_bags, bag_size, y, 0, (hipStream_t)stream));
   return PKM_OK;
 }
 

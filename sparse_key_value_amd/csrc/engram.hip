@@ -337,28 +337,6 @@ int launch_tokens(int dtype, int mode, const EngramArgs& a, hipStream_t s) {
   return launch_mode<FULL>(dtype, a, s);
 }
 
-// The address at which kernels read `p`: device memory as is, pinned host memory through
-// its device mapping; anything else (pageable host memory) is refused.
-int device_view(const void* p, const void** out) {
-  hipPointerAttribute_t at;
-  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
-    (void)hipGetLastError();
-    return pkm_abi::fail(PKM_EINVAL, "tables are neither device memory nor pinned host memory");
-  }
-  if (at.type == hipMemoryTypeDevice) {
-    *out = p;
-    return PKM_OK;
-  }
-  if (at.type == hipMemoryTypeHost) {
-    void* d = nullptr;
-    PKM_HIP(hipHostGetDevicePointer(&d, const_cast<void*>(p), 0));
-    if (!d) return pkm_abi::fail(PKM_EINVAL, "pinned host tables have no device mapping");
-    *out = d;
-    return PKM_OK;
-  }
-  return pkm_abi::fail(PKM_EINVAL, "tables must be device memory or pinned host memory (e.g. hipHostMalloc)");
-}
-
 // The device check once per device and process.
 int device_ok() {
   static int state[64] = {};  // 0 unknown, 1 gfx950
@@ -421,7 +399,7 @@ int engram_prefetch(const engram_config* cfg, const void* tables, const int32_t*
     return pkm_abi::fail(PKM_EINVAL, "tables and staged must be 16-byte aligned");
   if ((rc = pkm::device_ok()) != PKM_OK) return rc;
   const void* view = nullptr;
-  if ((rc = pkm::device_view(tables, &view)) != PKM_OK) return rc;
+  if ((rc = pkm_abi::device_view(tables, "tables", &view)) != PKM_OK) return rc;
   a.tables = (const uint8_t*)view;
   a.staged = (uint8_t*)staged;
   return pkm::launch_tokens(cfg->dtype, pkm::PREFETCH, a, (hipStream_t)stream);

@@ -127,3 +127,45 @@ def test_shared_pool_three_layers_over_one_table():
     assert not np.array_equal(outs[0], outs[1])
     for wl in layers:
         wl.close()
+
+
+def test_host_resident_value_table():
+    """The value table in pinned host memory: the gather reads it over the host link; the
+    forward and the EmbeddingBag give the same bytes as with the table in HBM."""
+    import sparse_key_value_amd as P
+    from tests import gpu_util as G
+
+    cfg = CONFIGS["pkm_1m_bf16"].with_(memory_plus=True)
+    T = 96
+    dev = G.Workload(cfg, seed=0, T=T)
+    host_v = torch.empty(dev.values.shape, dtype=dev.values.dtype, pin_memory=True)
+    host_v.copy_(dev.values)
+    torch.cuda.synchronize()
+    hwl = G.Workload(cfg, seed=0, T=T, values=host_v, value_seed=0)
+    x = dev.dev["x"]
+    outs = []
+    for wl in (dev, hwl):
+        o = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
+        wl.pkm.forward(x, out=o)
+        outs.append(G.to_host(o))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    full_rows = [G.to_host(t) for t in (dev.values[:4], host_v[:4])]
+    np.testing.assert_array_equal(full_rows[0], full_rows[1])
+    # the EmbeddingBag over the host table, uniform indices
+    idx, w = S.uniform_bags(3, 500, 16, cfg.N)
+    idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    ys = []
+    for table in (dev.values, host_v):
+        y = torch.empty((500, cfg.d_v), dtype=torch.float32, device="cuda")
+        P.pkm_embedding_bag(table, cfg.N, cfg.d_v, cfg.dtype, idx_d, w_d, 500, 16, y)
+        ys.append(y.cpu().numpy())
+    np.testing.assert_array_equal(ys[0], ys[1])
+    ref = O.weighted_bag(lambda r: O.to_f64(S.value_rows(0, r, cfg.d_v, cfg.dtype), cfg.dtype),
+                         idx.astype(np.int64), w.astype(np.float64))
+    PAR.check_rows(ys[1], ref, 1e-4, "EmbeddingBag over the host table")
+    # pageable host memory is refused
+    with pytest.raises(P.PkmError):
+        P.pkm_embedding_bag(torch.empty(16, cfg.d_v, dtype=dev.values.dtype), 16, cfg.d_v, cfg.dtype, idx_d, w_d,
+                            1, 1, y)
+    hwl.close()
+    dev.close()
