@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
 FP32_MFMA_PEAK_TFLOPS = 157.3
+HOST_LINK_PEAK_GBPS = 64.0    # PCIe 5.0 x16 host link, one direction, published
 METRIC = "PKM fwd tokens/s + value-gather GB/s (% of HBM peak) at 16M keys, 1 MI355X"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gather_memplus_16m_bf16_counters.json")
 GATHER_SRC = os.path.join(ROOT, "sparse_key_value_amd", "csrc", "gather.hip")
@@ -257,9 +258,6 @@ def bench_engram(a):
     print(json.dumps(res), flush=True)
 
 
-HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction, published
-
-
 def bench_engram_host(a):
     """Hashed n-gram lookup with the tables in pinned host memory: each step prefetches the
     next batch's rows over the host link on a side stream while the current batch is gated
@@ -467,31 +465,48 @@ def main():
     cfg = CONFIGS[a.workload]
     T = cfg.T
     log(f"workload {cfg.name}: T={T}, N={cfg.N}, d_v={cfg.d_v}, {cfg.dtype}; filling the value table")
-    wl = Workload(cfg, seed=a.seed)
+    host = a.tables == "host"
+    if host:
+        # a host-resident table: generated on the GPU, moved to pinned host memory in 1 GiB pieces
+        from tests.gpu_util import TORCH_DT
+        hv = torch.empty((cfg.N, cfg.d_v), dtype=TORCH_DT[cfg.dtype], pin_memory=True)
+        step = max(1, (1 << 30) // (cfg.d_v * cfg.elem_bytes))
+        piece = torch.empty((step, cfg.d_v), dtype=hv.dtype, device="cuda")
+        for r0 in range(0, cfg.N, step):
+            n = min(step, cfg.N - r0)
+            SD.fill_rows(piece, a.seed, r0, n)
+            hv[r0:r0 + n].copy_(piece[:n])
+        torch.cuda.synchronize()
+        del piece
+        wl = Workload(cfg, seed=a.seed, values=hv, value_seed=a.seed)
+    else:
+        wl = Workload(cfg, seed=a.seed)
     h = wl.pkm.handle
     P.pkm_set_pipeline_chunks(h, a.chunks)
     x = wl.dev["x"]
     out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # streaming-read ceiling over the value table itself (one pass, after a warm pass)
-    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    SD.stream_read(wl.values, sink)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    SD.stream_read(wl.values, sink)
-    ev1.record()
-    torch.cuda.synchronize()
     tbytes = wl.values.numel() * wl.values.element_size()
-    stream_gbps = tbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
-    log(f"streaming read of the table: {stream_gbps:.0f} GB/s")
-    # a plain copy of known size (1 GiB read + 1 GiB written): the reference that scales the
-    # HBM byte counters of a profiler run to bytes
-    cal_src = wl.values.view(torch.uint8).view(-1)[: 1 << 30]
-    cal_dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    SD.copy(cal_dst, cal_src)
-    torch.cuda.synchronize()
-    del cal_dst
+    stream_gbps = None
+    if not host:
+        # streaming-read ceiling over the value table itself (one pass, after a warm pass)
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        SD.stream_read(wl.values, sink)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        SD.stream_read(wl.values, sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        stream_gbps = tbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+        log(f"streaming read of the table: {stream_gbps:.0f} GB/s")
+        # a plain copy of known size (1 GiB read + 1 GiB written): the reference that scales the
+        # HBM byte counters of a profiler run to bytes
+        cal_src = wl.values.view(torch.uint8).view(-1)[: 1 << 30]
+        cal_dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        SD.copy(cal_dst, cal_src)
+        torch.cuda.synchronize()
+        del cal_dst
 
     for _ in range(a.warmup):
         P.pkm_forward(h, x, T, out, stream=stream)
@@ -515,10 +530,10 @@ def main():
     log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
 
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not host:
         cpu = cpu_baseline(wl, cfg, a.cpu_seconds)
 
-    traffic = counter_traffic()
+    traffic = counter_traffic() if not host else None
     res = {
         "metric": METRIC,
         "value": tok_s,
@@ -534,14 +549,16 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights; value table generated on the GPU)",
         "config": {"workload": cfg.name, "tokens": T, "pipeline_chunks": a.chunks or "auto", "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
                    "n_sub": cfg.n_sub, "n_keys": cfg.N, "d_value": cfg.d_v, "k": cfg.k, "qk_norm": cfg.qk_norm,
-                   "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30},
-        "roofline": {"bound": "hbm", "kernel": "gather (weighted EmbeddingBag)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                   "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30,
+                   "table_memory": "host (pinned)" if host else "device"},
+        "roofline": {"bound": "host-link" if host else "hbm", "kernel": "gather (weighted EmbeddingBag)",
+                     "achieved": achieved, "peak": HOST_LINK_PEAK_GBPS if host else HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / (HOST_LINK_PEAK_GBPS if host else HBM_PEAK_GBPS),
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": g_ms},
         "gather_value_GBps": rows_b / (g_ms * 1e-3) / 1e9,
         "gather_value_frac_hbm": rows_b / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stream_read_GBps": stream_gbps,
-        "gather_frac_of_stream_read": achieved / stream_gbps,
+        "gather_frac_of_stream_read": achieved / stream_gbps if stream_gbps else None,
         "stages_ms": stages,
         "score_TFLOPs": tf(score, stages["score"]),
         "score_mfma_frac": (tf(score, stages["score"]) or 0) / peak_t,

@@ -35,6 +35,21 @@ def fill_values(table, seed: int, row0: int = 0, n_rows: int | None = None, tid:
         raise RuntimeError(f"synth_fill_table failed: hip error {rc}")
 
 
+def fill_rows(buf, seed: int, row0: int, n_rows: int, tid: int = 6) -> None:
+    """Fill buf[0:n_rows] with rows row0 .. row0 + n_rows - 1 of the table of tensor id ``tid``
+    (a piece of a table too large to keep on the GPU)."""
+    import torch
+    assert 0 <= n_rows <= buf.shape[0]
+    dt = 1 if buf.dtype == torch.bfloat16 else 0
+    row_bytes = buf.shape[1] * buf.element_size()
+    # the generator addresses rows from the table's row 0; only rows row0 .. row0 + n_rows - 1,
+    # i.e. buf[0:n_rows], are written
+    rc = _lib.synth_fill_table(buf.data_ptr() - row0 * row_bytes, row0, n_rows, buf.shape[1], dt, seed, tid,
+                               _stream())
+    if rc:
+        raise RuntimeError(f"synth_fill_table failed: hip error {rc}")
+
+
 def stream_read(buf, sink, grid: int = 2048) -> None:
     rc = _lib.synth_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), grid, _stream())
     if rc:
