@@ -4,7 +4,8 @@ The forward ("Memory Layers at Scale": a product-key memory layer in place of an
 FFN) runs entirely in the HIP kernels of ``libpkm.so`` behind the C ABI of
 ``include/pkm.h``, and so does the hashed n-gram lookup (Engram review: multi-head
 hashing and the context-aware gate) behind ``include/engram.h`` and the Memory
-Attention token-memory values (V = K + folded table row) behind ``include/ma.h``; this package only
+Attention token-memory values (V = K + folded table row) behind ``include/ma.h`` and the
+EmbeddingBag backward with the sparse update behind ``include/bag_backward.h``; this package only
 marshals arguments (``_lib``) and manages device memory with PyTorch
 (``ProductKeyMemory``).
 """
@@ -17,7 +18,7 @@ from ._lib import (  # noqa: F401
     pkm_embedding_bag, pkm_enable_stage_timing, pkm_forward, pkm_forward_debug, pkm_last_error, pkm_select,
     pkm_set_pipeline_chunks, pkm_stage_times, pkm_workspace_size,
     engram_config, engram_forward, engram_forward_staged, engram_hash, engram_prefetch, make_engram_config,
-    ma_fold_table, ma_values,
+    ma_fold_table, ma_values, pkm_bag_backward, pkm_bag_backward_args, pkm_bag_backward_workspace_size,
 )
 
 

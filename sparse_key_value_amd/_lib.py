@@ -1,5 +1,5 @@
-"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h``, ``include/engram.h`` and
-``include/ma.h``).
+"""ctypes binding of ``libpkm.so`` (the C ABI in ``include/pkm.h``, ``include/engram.h``,
+``include/ma.h`` and ``include/bag_backward.h``).
 
 Argument marshalling only: every function has the name of the C entry point it
 calls, takes torch tensors (or raw device addresses as ints, or None for NULL)
@@ -49,6 +49,16 @@ class engram_config(ctypes.Structure):
     ]
 
 
+class pkm_bag_backward_args(ctypes.Structure):
+    _fields_ = [
+        ("table", ctypes.c_void_p), ("n_rows", ctypes.c_int64), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("n_bags", ctypes.c_int64),
+        ("bag_size", ctypes.c_int32), ("dw", ctypes.c_void_p), ("ds", ctypes.c_void_p),
+        ("softmax_group", ctypes.c_int32), ("rows", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+        ("n_unique", ctypes.c_void_p), ("update", ctypes.c_int32), ("lr", ctypes.c_float),
+    ]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _sig = {
     "pkm_workspace_size": (_sz, [ctypes.POINTER(pkm_config)]),
@@ -68,6 +78,8 @@ _sig = {
                                       _vp, _vp]),
     "engram_prefetch": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "engram_forward_staged": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "pkm_bag_backward_workspace_size": (_sz, [_i64, _i32, _i64]),
+    "pkm_bag_backward": (ctypes.c_int, [ctypes.POINTER(pkm_bag_backward_args), _vp, _sz, _vp]),
     "ma_fold_table": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
     "ma_values": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -212,3 +224,22 @@ def ma_fold_table(E, vocab: int, d_v: int, n_heads: int, gain, eps: float, dtype
 def ma_values(E_bar, vocab: int, d_v: int, dtype, ids, T: int, K, V, stream=None) -> None:
     dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
     _check(_lib.ma_values(_ptr(E_bar), vocab, d_v, dt, _ptr(ids), T, _ptr(K), _ptr(V), _stream(stream)), "ma_values")
+
+
+def pkm_bag_backward_workspace_size(n_bags: int, bag_size: int, n_rows: int) -> int:
+    n = _lib.pkm_bag_backward_workspace_size(n_bags, bag_size, n_rows)
+    if n == 0:
+        raise PkmError(PKM_EINVAL, "pkm_bag_backward_workspace_size")
+    return n
+
+
+def pkm_bag_backward(table, n_rows: int, dim: int, dtype, idx, w, dy, n_bags: int, bag_size: int, dw=None, ds=None,
+                     softmax_group: int = 0, rows=None, grad=None, n_unique=None, update: bool = False,
+                     lr: float = 0.0, workspace=None, ws_bytes=None, stream=None) -> None:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    a = pkm_bag_backward_args(_ptr(table), int(n_rows), int(dim), int(dt), _ptr(idx), _ptr(w), _ptr(dy), int(n_bags),
+                              int(bag_size), _ptr(dw), _ptr(ds), int(softmax_group), _ptr(rows), _ptr(grad),
+                              _ptr(n_unique), int(bool(update)), float(lr))
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pkm_bag_backward(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)), "pkm_bag_backward")

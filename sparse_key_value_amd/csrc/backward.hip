@@ -1,0 +1,372 @@
+// Backward of the weighted EmbeddingBag and the sparse update of the touched rows
+// ("Memory Layers at Scale" digest, parallel EmbeddingBag: the forward sum whose chain
+// rule this is; "Memory inside the model" overview, learning without forgetting: only
+// the slots that were read are edited), and their C entry point.
+//
+//  * dw (and ds): one block of four waves per bag; each wave keeps the bag's dy row in
+//    registers (dim <= 2048 floats: at most 32 per lane) and takes every fourth entry,
+//    with four entries' table slices in flight per lane; a wave reduction gives each
+//    dot product.  The table rows are read once, like the forward gather.
+//  * the per-row gradient: the (row, position) pairs are sorted by row with a stable
+//    radix sort, run-length encoded and scanned (rocPRIM device primitives); one block
+//    per distinct row then sums w * dy over the row's positions in position order (the
+//    result does not depend on scheduling, and no atomics are used) and writes the
+//    gradient and/or applies the update in place.
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_run_length_encode.hpp>
+#include <rocprim/device/device_scan.hpp>
+
+#include "../../include/bag_backward.h"
+#include "abi.hpp"
+#include "common.hpp"
+
+namespace pkm {
+
+namespace {
+
+constexpr int MAX_BAG = 2048;
+
+template <int EB>
+struct BV;
+template <>
+struct BV<2> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = bf16_lo(v[e]);
+      f[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* f) {
+    u32x4 p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = (uint32_t)f32_to_bf16(f[2 * e]) | ((uint32_t)f32_to_bf16(f[2 * e + 1]) << 16);
+    return p;
+  }
+};
+template <>
+struct BV<4> {
+  static constexpr int E = 4;
+  __device__ static __forceinline__ void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+  }
+  __device__ static __forceinline__ u32x4 pack(const float* f) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  }
+};
+
+// dy[b] slice s (E floats, 16-byte aligned).
+template <int E>
+__device__ __forceinline__ void load_dy(const float* p, float* d) {
+#pragma unroll
+  for (int x = 0; x < E; x += 4) {
+    const f32x4 q = *(const f32x4*)(p + x);
+    d[x] = q[0];
+    d[x + 1] = q[1];
+    d[x + 2] = q[2];
+    d[x + 3] = q[3];
+  }
+}
+
+// One block per bag.  SPL = 16-byte table slices per lane.
+template <int EB, int SPL>
+__global__ void __launch_bounds__(256) bag_dw_kernel(const uint8_t* __restrict__ table, int64_t n_rows, int slices,
+                                                     int dim, const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ w, const float* __restrict__ dy,
+                                                     int bag, float* __restrict__ dw, float* __restrict__ ds,
+                                                     int group) {
+  using V = BV<EB>;
+  constexpr int E = V::E, U = 4;
+  __shared__ float dws[MAX_BAG];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = blockIdx.x;
+
+  float d[SPL][E];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int s = lane + 64 * i;
+    if (s < slices) {
+      load_dy<E>(dy + b * dim + (int64_t)s * E, d[i]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < E; ++x) d[i][x] = 0.f;
+    }
+  }
+
+  const int32_t* bi = idx + b * bag;
+  const size_t row_bytes = (size_t)slices * 16;
+  for (int j0 = wv; j0 < bag; j0 += 4 * U) {
+    u32x4 v[U][SPL];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 4 * u;
+      const int32_t r = j < bag ? bi[j] : -1;
+      ok[u] = r >= 0 && (int64_t)r < n_rows;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int s = lane + 64 * i;
+        v[u][i] = (ok[u] && s < slices)
+                      ? __builtin_nontemporal_load((const u32x4*)(table + (size_t)r * row_bytes + (size_t)s * 16))
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        float f[E];
+        V::unpack(v[u][i], f);
+#pragma unroll
+        for (int x = 0; x < E; ++x) p = __builtin_fmaf(d[i][x], f[x], p);
+      }
+      p = wave_sum_f32(p);
+      const int j = j0 + 4 * u;
+      if (lane == 0 && j < bag) dws[j] = ok[u] ? p : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < bag; j += 256) {
+    const float g = dws[j];
+    if (dw) dw[b * bag + j] = g;
+    if (ds) {
+      const int g0 = j - j % group;
+      float sum = 0.f;
+      for (int q = g0; q < g0 + group; ++q) sum = __builtin_fmaf(w[b * bag + q], dws[q], sum);
+      ds[b * bag + j] = w[b * bag + j] * (g - sum);
+    }
+  }
+}
+
+// Sort keys: the row, or n_rows for an index that read nothing (those sort last).
+__global__ void __launch_bounds__(256) bag_keys_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t n_rows,
+                                                       uint32_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t r = idx[i];
+  keys[i] = (r >= 0 && (int64_t)r < n_rows) ? (uint32_t)r : (uint32_t)n_rows;
+  vals[i] = (uint32_t)i;
+}
+
+// One block per distinct row (grid-strided): the row's gradient in position order.
+template <int EB>
+__global__ void __launch_bounds__(256) bag_grad_kernel(const uint32_t* __restrict__ unique,
+                                                       const uint32_t* __restrict__ counts,
+                                                       const uint32_t* __restrict__ offsets,
+                                                       const uint32_t* __restrict__ runs,
+                                                       const uint32_t* __restrict__ pos_sorted,
+                                                       const float* __restrict__ w, const float* __restrict__ dy,
+                                                       int bag, int dim, int slices, uint32_t n_rows,
+                                                       int32_t* __restrict__ rows, float* __restrict__ grad,
+                                                       int32_t* __restrict__ n_unique, uint8_t* __restrict__ table,
+                                                       int update, float lr) {
+  using V = BV<EB>;
+  constexpr int E = V::E;
+  const uint32_t R = *runs;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n_unique)
+    n_unique[0] = (int32_t)((R > 0 && unique[R - 1] >= n_rows) ? R - 1 : R);
+  for (uint32_t u = blockIdx.x; u < R; u += gridDim.x) {
+    const uint32_t key = unique[u];
+    if (key >= n_rows) continue;  // the run of indices that read nothing (always the last)
+    const uint32_t off = offsets[u], cnt = counts[u];
+    if (rows && threadIdx.x == 0) rows[u] = (int32_t)key;
+    for (int s = threadIdx.x; s < slices; s += 256) {
+      float acc[E];
+#pragma unroll
+      for (int x = 0; x < E; ++x) acc[x] = 0.f;
+      for (uint32_t e = 0; e < cnt; ++e) {
+        const uint32_t p = pos_sorted[off + e];
+        const float wt = w[p];
+        float dd[E];
+        load_dy<E>(dy + (int64_t)(p / (uint32_t)bag) * dim + (int64_t)s * E, dd);
+#pragma unroll
+        for (int x = 0; x < E; ++x) acc[x] = __builtin_fmaf(wt, dd[x], acc[x]);
+      }
+      if (grad) {
+        float* go = grad + (int64_t)u * dim + (int64_t)s * E;
+#pragma unroll
+        for (int x = 0; x < E; x += 4) *(f32x4*)(go + x) = f32x4{acc[x], acc[x + 1], acc[x + 2], acc[x + 3]};
+      }
+      if (update) {
+        u32x4* tp = (u32x4*)(table + ((size_t)key * slices + s) * 16);
+        float t[E];
+        V::unpack(*tp, t);
+#pragma unroll
+        for (int x = 0; x < E; ++x) t[x] = __builtin_fmaf(-lr, acc[x], t[x]);
+        *tp = V::pack(t);
+      }
+    }
+  }
+}
+
+struct SortSpace {
+  size_t keys = 0, keys_sorted = 0, vals = 0, vals_sorted = 0, unique = 0, counts = 0, offsets = 0, runs = 0,
+         temp = 0, temp_bytes = 0, total = 0;
+};
+
+unsigned key_bits(int64_t n_rows) {
+  unsigned b = 1;
+  while (b < 32 && ((uint64_t)1 << b) <= (uint64_t)n_rows) ++b;  // n_rows itself (the sentinel) must fit
+  return b;
+}
+
+// Buffers of the sort and their rocPRIM temporary storage (sizes from rocPRIM's own queries).
+int sort_space(int64_t n, int64_t n_rows, SortSpace& S) {
+  auto a = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = a(off + bytes);
+    return o;
+  };
+  S.keys = take(n * 4);
+  S.keys_sorted = take(n * 4);
+  S.vals = take(n * 4);
+  S.vals_sorted = take(n * 4);
+  S.unique = take(n * 4);
+  S.counts = take(n * 4);
+  S.offsets = take(n * 4);
+  S.runs = take(4);
+  size_t t1 = 0, t2 = 0, t3 = 0;
+  const unsigned bits = key_bits(n_rows);
+  PKM_HIP(rocprim::radix_sort_pairs(nullptr, t1, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+                                    (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t)n, 0u, bits));
+  PKM_HIP(rocprim::run_length_encode(nullptr, t2, (const uint32_t*)nullptr, (unsigned)n, (uint32_t*)nullptr,
+                                     (uint32_t*)nullptr, (uint32_t*)nullptr));
+  PKM_HIP(rocprim::exclusive_scan(nullptr, t3, (const uint32_t*)nullptr, (uint32_t*)nullptr, 0u, (size_t)n,
+                                  rocprim::plus<uint32_t>()));
+  S.temp_bytes = t1 > t2 ? (t1 > t3 ? t1 : t3) : (t2 > t3 ? t2 : t3);
+  S.temp = take(S.temp_bytes);
+  S.total = off;
+  return PKM_OK;
+}
+
+int check_sizes(int64_t n_bags, int32_t bag_size, int64_t n_rows) {
+  using pkm_abi::fail;
+  if (n_bags < 0) return fail(PKM_EINVAL, "n_bags must be >= 0");
+  if (bag_size < 1 || bag_size > MAX_BAG) return fail(PKM_EINVAL, "bag_size must be in [1, 2048]");
+  if (n_bags * bag_size >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_bags * bag_size must be < 2^31");
+  if (n_rows < 1 || n_rows >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_rows must be in [1, 2^31)");
+  return PKM_OK;
+}
+
+int device_ok() {
+  static int state[64] = {};
+  int dev = 0;
+  PKM_HIP(hipGetDevice(&dev));
+  if (dev >= 0 && dev < 64 && state[dev] == 1) return PKM_OK;
+  const int rc = pkm_abi::check_device();
+  if (rc == PKM_OK && dev >= 0 && dev < 64) state[dev] = 1;
+  return rc;
+}
+
+template <int EB>
+int launch_dw(const pkm_bag_backward_args* a, const uint8_t* table, int slices, hipStream_t s) {
+  const int spl = (slices + 63) / 64;
+  const dim3 grid((unsigned)a->n_bags);
+#define PKM_DW(SPLV)                                                                                            \
+  PKM_LAUNCH((bag_dw_kernel<EB, SPLV><<<grid, 256, 0, s>>>(table, a->n_rows, slices, a->dim, a->idx, a->w, a->dy, \
+                                                           a->bag_size, a->dw, a->ds, a->softmax_group),         \
+              hipGetLastError()))
+  if (spl == 1) PKM_DW(1);
+  else if (spl == 2) PKM_DW(2);
+  else if (spl <= 4) PKM_DW(4);
+  else PKM_DW(8);
+#undef PKM_DW
+  return PKM_OK;
+}
+
+}  // namespace
+
+}  // namespace pkm
+
+extern "C" {
+
+size_t pkm_bag_backward_workspace_size(int64_t n_bags, int32_t bag_size, int64_t n_rows) {
+  if (pkm::check_sizes(n_bags, bag_size, n_rows) != PKM_OK) return 0;
+  pkm::SortSpace S;
+  if (pkm::sort_space(n_bags * bag_size > 0 ? n_bags * bag_size : 1, n_rows, S) != PKM_OK) return 0;
+  return S.total;
+}
+
+int pkm_bag_backward(const pkm_bag_backward_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  using pkm_abi::fail;
+  if (!a) return fail(PKM_EINVAL, "args is NULL");
+  int rc = pkm::check_sizes(a->n_bags, a->bag_size, a->n_rows);
+  if (rc != PKM_OK) return rc;
+  if (a->dtype != PKM_F32 && a->dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
+  const int eb = a->dtype == PKM_BF16 ? 2 : 4;
+  if (a->dim < 1 || a->dim > 2048 || ((int64_t)a->dim * eb) % 16 != 0)
+    return fail(PKM_EINVAL, "dim must be in [1, 2048] with dim * sizeof(dtype) a multiple of 16");
+  if (a->ds && (a->softmax_group < 1 || a->bag_size % a->softmax_group != 0))
+    return fail(PKM_EINVAL, "softmax_group must divide bag_size");
+  if (a->update != 0 && a->update != 1) return fail(PKM_EINVAL, "update must be 0 or 1");
+  if (a->n_bags == 0) return PKM_OK;
+  if (!a->table || !a->idx || !a->w || !a->dy) return fail(PKM_EINVAL, "table, idx, w and dy must not be NULL");
+  if ((((uintptr_t)a->table | (uintptr_t)a->dy | (uintptr_t)a->grad) & 15) != 0)
+    return fail(PKM_EINVAL, "table, dy and grad must be 16-byte aligned");
+  const bool need_sort = a->rows || a->grad || a->n_unique || a->update;
+  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
+  const void* tview = nullptr;
+  if ((rc = pkm_abi::device_view(a->table, "table", &tview)) != PKM_OK) return rc;
+  const int slices = a->dim * eb / 16;
+  hipStream_t s = (hipStream_t)stream;
+
+  // dw and ds read the table before any update
+  if (a->dw || a->ds) {
+    if (a->dtype == PKM_BF16) rc = pkm::launch_dw<2>(a, (const uint8_t*)tview, slices, s);
+    else rc = pkm::launch_dw<4>(a, (const uint8_t*)tview, slices, s);
+    if (rc != PKM_OK) return rc;
+  }
+  if (!need_sort) return PKM_OK;
+
+  const int64_t n = a->n_bags * a->bag_size;
+  pkm::SortSpace S;
+  if ((rc = pkm::sort_space(n, a->n_rows, S)) != PKM_OK) return rc;
+  if (!workspace || ws_bytes < S.total)
+    return fail(PKM_EWORKSPACE, "workspace has %zu bytes, these sizes need %zu", workspace ? ws_bytes : (size_t)0,
+                S.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(PKM_EINVAL, "workspace must be 256-byte aligned");
+  if ((rc = pkm_abi::require_device(workspace, "workspace")) != PKM_OK) return rc;
+  uint8_t* ws = (uint8_t*)workspace;
+  auto U = [&](size_t o) { return (uint32_t*)(ws + o); };
+  PKM_LAUNCH((pkm::bag_keys_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a->idx, n, a->n_rows,
+                                                                                   U(S.keys), U(S.vals)),
+              hipGetLastError()));
+  size_t tb = S.temp_bytes;
+  PKM_HIP(rocprim::radix_sort_pairs(ws + S.temp, tb, (const uint32_t*)U(S.keys), U(S.keys_sorted),
+                                    (const uint32_t*)U(S.vals), U(S.vals_sorted), (uint32_t)n, 0u,
+                                    pkm::key_bits(a->n_rows), s));
+  tb = S.temp_bytes;
+  PKM_HIP(rocprim::run_length_encode(ws + S.temp, tb, (const uint32_t*)U(S.keys_sorted), (unsigned)n, U(S.unique),
+                                     U(S.counts), U(S.runs), s));
+  tb = S.temp_bytes;
+  PKM_HIP(rocprim::exclusive_scan(ws + S.temp, tb, (const uint32_t*)U(S.counts), U(S.offsets), 0u, (size_t)n,
+                                  rocprim::plus<uint32_t>(), s));
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int64_t want = (int64_t)cus * 16;
+  const dim3 grid((unsigned)(n < want ? n : want));
+  uint8_t* tw = a->update ? (uint8_t*)tview : nullptr;
+#define PKM_GRAD(EBV)                                                                                          \
+  PKM_LAUNCH((pkm::bag_grad_kernel<EBV><<<grid, 256, 0, s>>>(U(S.unique), U(S.counts), U(S.offsets), U(S.runs), \
+                                                             U(S.vals_sorted), a->w, a->dy, a->bag_size, a->dim, \
+                                                             slices, (uint32_t)a->n_rows, a->rows, a->grad,      \
+                                                             a->n_unique, tw, a->update, a->lr),                 \
+              hipGetLastError()))
+  if (a->dtype == PKM_BF16) PKM_GRAD(2);
+  else PKM_GRAD(4);
+#undef PKM_GRAD
+  return PKM_OK;
+}
+
+}  // extern "C"

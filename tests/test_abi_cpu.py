@@ -25,10 +25,10 @@ def P():
 def test_library_exports_every_declared_symbol(P):
     lib = ctypes.CDLL(P.LIB_PATH)
     headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
-    assert headers == ["engram.h", "ma.h", "pkm.h"]
+    assert headers == ["bag_backward.h", "engram.h", "ma.h", "pkm.h"]
     names = sorted(set(n for hd in headers for n in _declared(hd)))
     assert {"pkm_create", "pkm_forward", "pkm_destroy", "pkm_embedding_bag", "engram_hash", "engram_forward",
-            "ma_fold_table", "ma_values"} <= set(names)
+            "ma_fold_table", "ma_values", "pkm_bag_backward", "pkm_bag_backward_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/pkm.h but not exported"
     assert set(names) == set(P.EXPORTED), "binding and header disagree"
@@ -190,3 +190,28 @@ def test_ma_argument_errors_before_any_device_call(P):
     assert v(256, 10, 64, 1, 256, -1, 256, 256, None) == P.PKM_EINVAL
     assert v(256, 10, 64, 1, 256, 4, 264, 256, None) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
     assert v(None, 10, 64, 1, None, 0, None, None, None) == P.PKM_OK
+
+
+def test_bag_backward_argument_errors_before_any_device_call(P):
+    lib = P._lib._lib
+    assert lib.pkm_bag_backward(None, None, 0, None) == P.PKM_EINVAL
+    assert lib.pkm_bag_backward_workspace_size(-1, 4, 100) == 0
+    assert lib.pkm_bag_backward_workspace_size(10, 0, 100) == 0 and "bag_size" in P.pkm_last_error()
+    assert lib.pkm_bag_backward_workspace_size(10, 4096, 100) == 0
+    assert lib.pkm_bag_backward_workspace_size(1 << 30, 4, 100) == 0 and "2^31" in P.pkm_last_error()
+    assert lib.pkm_bag_backward_workspace_size(10, 4, 0) == 0 and "n_rows" in P.pkm_last_error()
+
+    def args(**kw):
+        base = dict(table=256, n_rows=100, dim=64, dtype=1, idx=256, w=256, dy=256, n_bags=4, bag_size=8)
+        base.update(kw)
+        return P.pkm_bag_backward_args(**base)
+
+    bb = lambda a: lib.pkm_bag_backward(ctypes.byref(a), None, 0, None)
+    assert bb(args(dtype=3)) == P.PKM_EINVAL and "dtype" in P.pkm_last_error()
+    assert bb(args(dim=4)) == P.PKM_EINVAL and "dim" in P.pkm_last_error()
+    assert bb(args(dim=4096)) == P.PKM_EINVAL
+    assert bb(args(ds=256, softmax_group=3)) == P.PKM_EINVAL and "softmax_group" in P.pkm_last_error()
+    assert bb(args(update=2)) == P.PKM_EINVAL
+    assert bb(args(table=None)) == P.PKM_EINVAL
+    assert bb(args(dy=8)) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
+    assert bb(args(n_bags=0, table=None, idx=None, w=None, dy=None)) == P.PKM_OK

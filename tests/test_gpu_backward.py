@@ -1,0 +1,176 @@
+"""GPU parity of the EmbeddingBag backward and the sparse update, through the C ABI.
+
+Integer results (the distinct rows, their count) are compared exactly; dw, ds and the
+row gradients (fp32 sums of fp32 products) to 1e-4 of each row's largest magnitude
+against the float64 oracle; the updated table stage-wise (the oracle applies the GPU's
+own gradient) to one storage ulp, with every untouched row bitwise unchanged.
+"""
+
+from __future__ import annotations
+
+import gc
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from oracle import backward as B  # noqa: E402
+from oracle import pkm as O  # noqa: E402
+from synth import CONFIGS  # noqa: E402
+from synth import inputs as S  # noqa: E402
+from tests import parity as PAR  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _run(table, n_rows, dim, dt, idx, w, dy, group, update=False, lr=0.0, want_grad=True, grad_to_host=True):
+    import sparse_key_value_amd as P
+    n_bags, bag = idx.shape
+    n = n_bags * bag
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    idx_d, w_d, dy_d = dev(idx.astype(np.int32)), dev(w.astype(np.float32)), dev(dy.astype(np.float32))
+    dw = torch.full((n_bags, bag), float("nan"), device="cuda")
+    ds = torch.full((n_bags, bag), float("nan"), device="cuda")
+    rows = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    grad = torch.full((n, dim), float("nan"), device="cuda") if want_grad else None
+    nu = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    ws_bytes = P.pkm_bag_backward_workspace_size(n_bags, bag, n_rows)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    P.pkm_bag_backward(table, n_rows, dim, dt, idx_d, w_d, dy_d, n_bags, bag, dw=dw, ds=ds, softmax_group=group,
+                       rows=rows, grad=grad, n_unique=nu, update=update, lr=lr, workspace=ws)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    g = None
+    if want_grad:
+        g = grad[:U].cpu().numpy() if grad_to_host else grad[:U]
+    return {"dw": dw.cpu().numpy(), "ds": ds.cpu().numpy(), "U": U, "rows": rows[:U].cpu().numpy(), "grad": g}
+
+
+def _check(got, table_rows_of, n_rows, idx, w, dy, group, tokens=None):
+    sel = np.arange(idx.shape[0]) if tokens is None else np.asarray(tokens)
+    dw_ref = B.grad_weights(table_rows_of, idx[sel], dy[sel], n_rows)
+    PAR.check_rows(got["dw"][sel], dw_ref, 1e-4, "dw")
+    ds_ref = B.softmax_backward(w[sel].astype(np.float64), got["dw"][sel].astype(np.float64), group)
+    np.testing.assert_allclose(got["ds"][sel], ds_ref, rtol=1e-5, atol=1e-6 * np.abs(ds_ref).max())
+    if tokens is None:
+        rows_ref, grad_ref = B.grad_rows(idx, w, dy, n_rows)
+        np.testing.assert_array_equal(got["rows"], rows_ref)
+        assert got["U"] == len(rows_ref)
+        if got["grad"] is not None:
+            PAR.check_rows(got["grad"], grad_ref, 1e-4, "row gradients")
+
+
+def _one_ulp(got_stored, ref64, dt):
+    g = O.to_f64(got_stored, dt)
+    mag = np.maximum(np.abs(ref64), 1e-30)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - (7 if dt == "bf16" else 23))
+    assert np.all(np.abs(g - ref64) <= ulp), f"update beyond one ulp: {np.abs(g - ref64).max():.3e}"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_small_with_duplicates_and_out_of_range(dt):
+    from tests.gpu_util import TORCH_DT, to_dev, to_host
+    rng = np.random.default_rng(0)
+    n_rows, dim, n_bags, k, H = 400, 64, 120, 8, 2
+    bag = H * k
+    idx = rng.integers(-3, n_rows + 3, size=(n_bags, bag))          # some out of range
+    idx[:5, :4] = 17                                               # a row many times, also within a bag
+    s = rng.standard_normal((n_bags, H, k))
+    w = np.exp(s - s.max(-1, keepdims=True))
+    w = (w / w.sum(-1, keepdims=True)).reshape(n_bags, bag).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(9, np.arange(n_rows), dim, dt)
+    table = to_dev(host, dt)
+    say(f"bag backward small {dt}")
+    got = _run(table, n_rows, dim, dt, idx, w, dy, k)
+    rows_of = lambda r: O.to_f64(host[np.asarray(r)], dt)
+    _check(got, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), k)
+    # the update, stage-wise from the GPU's gradient; untouched rows unchanged
+    before = to_host(table).copy()
+    lr = 0.125
+    got2 = _run(table, n_rows, dim, dt, idx, w, dy, k, update=True, lr=lr)
+    after = to_host(table)
+    np.testing.assert_array_equal(got2["rows"], got["rows"])
+    ref = O.to_f64(before[got["rows"]], dt) - lr * got2["grad"].astype(np.float64)
+    _one_ulp(after[got["rows"]], ref, dt)
+    untouched = np.setdiff1d(np.arange(n_rows), got["rows"])
+    np.testing.assert_array_equal(np.asarray(after[untouched]).view(np.uint8),
+                                  np.asarray(before[untouched]).view(np.uint8))
+
+
+def test_deterministic():
+    from tests.gpu_util import to_dev
+    rng = np.random.default_rng(1)
+    n_rows, dim, n_bags, bag = 50, 128, 400, 32                   # heavy reuse: ~256 entries per row
+    idx = rng.integers(0, n_rows, size=(n_bags, bag))
+    w = rng.random((n_bags, bag)).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    table = to_dev(S.value_rows(2, np.arange(n_rows), dim, "bf16"), "bf16")
+    a = _run(table, n_rows, dim, "bf16", idx, w, dy, 8)
+    b = _run(table, n_rows, dim, "bf16", idx, w, dy, 8)
+    for k in ("dw", "ds", "rows", "grad"):
+        np.testing.assert_array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8))
+
+
+def test_forward_indices_pkm_1m():
+    """The backward of a real forward's gather (1M-key table, 4 heads x k = 32)."""
+    from tests import gpu_util as G
+    cfg = CONFIGS["pkm_1m_bf16"]
+    T = 256
+    wl = G.Workload(cfg, seed=0, T=T)
+    o = wl.forward_debug()
+    idx = o["idx"].cpu().numpy().reshape(T, cfg.H * cfg.k)
+    w = o["w"].cpu().numpy().reshape(T, cfg.H * cfg.k)
+    dy = np.random.default_rng(3).standard_normal((T, cfg.d_v)).astype(np.float32)
+    say("bag backward on pkm_1m forward indices")
+    got = _run(wl.values, cfg.N, cfg.d_v, cfg.dtype, idx, w, dy, cfg.k)
+    _check(got, lambda r: O.to_f64(wl.host_rows(r), cfg.dtype), cfg.N, idx, w.astype(np.float64),
+           dy.astype(np.float64), cfg.k)
+    wl.close()
+
+
+def test_full_size_sampled():
+    """16,384 tokens x 128 entries over the 16M-key, 64 GiB table, as benchmarked: the
+    distinct rows exactly, dw/ds on sampled tokens, gradients of sampled rows."""
+    from tests import gpu_util as G
+    cfg = CONFIGS["memplus_16m_bf16"]
+    T = cfg.T
+    wl = G.Workload(cfg, seed=0, T=T)
+    o = wl.forward_debug()
+    bag = cfg.H * cfg.k
+    idx = o["idx"].cpu().numpy().reshape(T, bag)
+    w = o["w"].cpu().numpy().reshape(T, bag)
+    del o
+    dy = np.random.default_rng(4).standard_normal((T, cfg.d_v)).astype(np.float32)
+    say("bag backward full size")
+    got = _run(wl.values, cfg.N, cfg.d_v, cfg.dtype, idx, w, dy, cfg.k, grad_to_host=False)
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(T, 24, replace=False))
+    rows_of = lambda r: O.to_f64(wl.host_rows(r), cfg.dtype)
+    _check(got, rows_of, cfg.N, idx, w.astype(np.float64), dy.astype(np.float64), cfg.k, tokens=tokens)
+    uniq = np.unique(idx)
+    np.testing.assert_array_equal(got["rows"], uniq)
+    # sampled rows: the most repeated ones and random ones
+    vals, counts = np.unique(idx, return_counts=True)
+    pick = np.concatenate([vals[np.argsort(-counts)[:8]], rng.choice(vals, 24, replace=False)])
+    flat_i, flat_w = idx.reshape(-1), w.reshape(-1).astype(np.float64)
+    for r in pick:
+        pos = np.nonzero(flat_i == r)[0]
+        ref = np.sum(flat_w[pos, None] * dy[pos // bag].astype(np.float64), axis=0)
+        u = int(np.searchsorted(got["rows"], r))
+        PAR.check_rows(got["grad"][u].cpu().numpy()[None], ref[None], 1e-4, f"gradient of row {r}")
+    wl.close()
