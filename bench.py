@@ -4,6 +4,7 @@
     python bench.py --workload engram_zipf_2m_bf16     # the hashed n-gram lookup
     python bench.py --workload ma_values_32k_bf16      # Memory Attention token-memory values
     python bench.py --workload engram_zipf_2m_bf16 --tables host   # tables in host memory, prefetched
+    python bench.py --backward                         # value-table backward + sparse update
 
 A step is one whole forward (projection, qk-norm, scoring + per-half top-k,
 combine + softmax, weighted EmbeddingBag over the value table, Memory+ gate) over
@@ -355,6 +356,78 @@ def bench_engram_host(a):
     print(json.dumps(res), flush=True)
 
 
+def bench_backward(a):
+    """The sparse training step of the value table behind the forward's gather: dw and the
+    softmax ds for every token, then the per-row sums and the in-place update of every touched
+    row (pkm_bag_backward), on the indices and weights of a real forward."""
+    import numpy as np
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import CONFIGS
+    from tests.gpu_util import Workload
+
+    cfg = CONFIGS[a.workload]
+    T, bag, eb = cfg.T, cfg.H * cfg.k, cfg.elem_bytes
+    log(f"backward of {cfg.name}: T={T}, {bag} entries per token, N={cfg.N}, d_v={cfg.d_v}")
+    wl = Workload(cfg, seed=a.seed)
+    x = wl.dev["x"]
+    out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
+    idx = torch.empty((T, bag), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, bag), dtype=torch.float32, device="cuda")
+    P.pkm_forward(wl.pkm.handle, x, T, out, idx, w)
+    dy = torch.randn((T, cfg.d_v), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(a.seed))
+    dw = torch.empty((T, bag), dtype=torch.float32, device="cuda")
+    ds = torch.empty_like(dw)
+    rows = torch.empty(T * bag, dtype=torch.int32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_bytes = P.pkm_bag_backward_workspace_size(T, bag, cfg.N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    common = dict(table=wl.values, n_rows=cfg.N, dim=cfg.d_v, dtype=cfg.dtype, idx=idx, w=w, dy=dy, n_bags=T,
+                  bag_size=bag, workspace=ws, stream=stream)
+    run_dw = lambda: P.pkm_bag_backward(**common, dw=dw, ds=ds, softmax_group=cfg.k)
+    run_upd = lambda: P.pkm_bag_backward(**common, rows=rows, n_unique=nu, update=True, lr=1e-4)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    dw_ms = timed(run_dw)
+    upd_ms = timed(run_upd)
+    U = int(nu.item())
+    n = T * bag
+    dw_bytes = n * cfg.d_v * eb + T * cfg.d_v * 4 + n * 16          # rows, dy, idx/w/dw/ds
+    upd_bytes = 2 * U * cfg.d_v * eb + T * cfg.d_v * 4 + n * 8        # touched rows read + written, dy, idx/w
+    step_ms = dw_ms + upd_ms
+    res = {
+        "metric": "PKM value-table backward (dw, ds, sparse update of the touched rows) tokens/s, 1 MI355X",
+        "value": T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (indices and weights of a real forward over the generated table; "
+                                    "dy ~ N(0, 1))",
+        "config": {"workload": cfg.name, "tokens": T, "entries_per_token": bag, "n_keys": cfg.N, "d_value": cfg.d_v,
+                   "distinct_rows": U},
+        "roofline": {"bound": "hbm", "kernel": "bag_dw_kernel (dw + ds)", "achieved": dw_bytes / (dw_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dw_bytes / (dw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dw_bytes, "avg_launch_ms": dw_ms},
+        "update": {"ms": upd_ms, "algorithmic_bytes": upd_bytes, "GBps": upd_bytes / (upd_ms * 1e-3) / 1e9,
+                   "frac_hbm": upd_bytes / (upd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_ma(a):
     """Memory Attention token-memory values: one step = ma_values over the workload's tokens
     (the table fold runs once, before the timing)."""
@@ -441,6 +514,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the value-table backward and sparse update instead of the forward")
     ap.add_argument("--tables", choices=["device", "host"], default="device",
                     help="Engram workloads: keep the tables in HBM or in pinned host memory (prefetched)")
     a = ap.parse_args()
@@ -454,6 +529,8 @@ def main():
         return bench_engram_host(a) if a.tables == "host" else bench_engram(a)
     if a.workload in C.MA_CONFIGS:
         return bench_ma(a)
+    if a.backward:
+        return bench_backward(a)
 
     import torch
 
