@@ -40,11 +40,13 @@ def log(msg):
 
 
 def gather_bytes(cfg, T):
-    """Algorithmic bytes one gather launch must move: value rows + (idx, w) + y (fp32)."""
+    """Algorithmic bytes one gather launch must move: value rows + (idx, w) + its output --
+    with the Memory+ gate, z = x W1 read (fp32) and g = y * silu(z) written (dtype); else y
+    written (dtype)."""
     rows = T * cfg.H * cfg.k * cfg.d_v * cfg.elem_bytes
     sel = T * cfg.H * cfg.k * 8
-    y = T * cfg.d_v * 4 if cfg.memory_plus else T * cfg.d_v * cfg.elem_bytes
-    return rows, rows + sel + y
+    out = T * cfg.d_v * (4 + cfg.elem_bytes) if cfg.memory_plus else T * cfg.d_v * cfg.elem_bytes
+    return rows, rows + sel + out
 
 
 def flops(cfg, T):

@@ -203,7 +203,7 @@ int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream
   uint8_t* qhat = h->at<uint8_t>(L.qhat) + (size_t)t0 * H * dq * eb;
   // a1: q = x W_q (fp32)
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.wqT), q, nullptr, tc, H * dq, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
+  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.wqT), q, tc, H * dq, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 1, sa));
   // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 0, sa));
@@ -211,14 +211,22 @@ int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 1, sa));
   // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
   const size_t sel = (size_t)t0 * H * k;
-  return run_select(h, qhat, tc, scratch_at(h, t0), h->at<int32_t>(L.hidx) + 2 * sel, h->at<float>(L.hsc) + 2 * sel,
-                    h->at<int32_t>(L.idx) + sel, h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
+  int rc = run_select(h, qhat, tc, scratch_at(h, t0), h->at<int32_t>(L.hidx) + 2 * sel, h->at<float>(L.hsc) + 2 * sel,
+                      h->at<int32_t>(L.idx) + sel, h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
+  if (rc || !c.memory_plus) return rc;
+  // a8, first product: z = x W1 (fp32), consumed by the gather's fused gate
+  float* z = h->at<float>(L.z) + (size_t)t0 * c.d_value;
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 0, sa));
+  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.w1T), z, tc, c.d_value, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
+  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 1, sa));
+  return PKM_OK;
 }
 
-// Gather (a7) for tokens [t0, t0 + tc) on stream sb: into y (fp32) with the gate, else
-// straight into out.
+// Gather (a7) for tokens [t0, t0 + tc) on stream sb: with the gate, fused with its
+// elementwise part into g = y * silu(z) (dtype); else straight into out.  A debug y
+// (fp32) comes from one more plain gather, whose arithmetic is the fused one's.
 int chunk_gather(pkm_handle* h, int64_t t0, int64_t tc, void* out, float* ydbg, hipStream_t sb, Timer& tm,
-                 int chunk) {
+                 int chunk, bool shared) {
   const pkm_config& c = h->cfg;
   const pkm::Layout& L = h->L;
   const int H = c.n_heads, k = c.k;
@@ -229,37 +237,35 @@ int chunk_gather(pkm_handle* h, int64_t t0, int64_t tc, void* out, float* ydbg, 
   const float* w = h->at<float>(L.w) + sel;
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATHER, chunk, 0, sb));
   if (c.memory_plus) {
-    float* y = (ydbg ? ydbg : h->at<float>(L.y)) + (size_t)t0 * c.d_value;
-    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, y, 0, sb));
+    const float* z = h->at<float>(L.z) + (size_t)t0 * c.d_value;
+    uint8_t* g = h->at<uint8_t>(L.g) + (size_t)t0 * c.d_value * eb;
+    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, g, 1, sb, z, shared));
+    if (ydbg)
+      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k,
+                                    ydbg + (size_t)t0 * c.d_value, 0, sb, nullptr, shared));
   } else {
     uint8_t* o = (uint8_t*)out + (size_t)t0 * c.d_value * eb;
     if (ydbg) {
       float* y = ydbg + (size_t)t0 * c.d_value;
-      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, y, 0, sb));
+      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, y, 0, sb, nullptr, shared));
       PKM_LAUNCH(pkm::launch_convert_f32(y, o, tc * c.d_value, c.dtype, sb));
     } else {
-      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, o, 1, sb));
+      PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, o, 1, sb, nullptr, shared));
     }
   }
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATHER, chunk, 1, sb));
   return PKM_OK;
 }
 
-// Memory+ gate (a8) for tokens [t0, t0 + tc) on stream sa: g = y * silu(x W1) in dtype, out = g W2.
-int chunk_gate(pkm_handle* h, const void* x, int64_t t0, int64_t tc, void* out, float* ydbg, hipStream_t sa,
-               Timer& tm, int chunk) {
+// Memory+ gate (a8), second product, for tokens [t0, t0 + tc) on stream sa: out = g W2.
+int chunk_gate(pkm_handle* h, int64_t t0, int64_t tc, void* out, hipStream_t sa, Timer& tm, int chunk) {
   const pkm_config& c = h->cfg;
   const pkm::Layout& L = h->L;
   const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
-  const uint8_t* xc = (const uint8_t*)x + (size_t)t0 * c.d_model * eb;
-  const float* y = (ydbg ? ydbg : h->at<float>(L.y)) + (size_t)t0 * c.d_value;
-  uint8_t* g = h->at<uint8_t>(L.g) + (size_t)t0 * c.d_value * eb;
+  const uint8_t* g = h->at<uint8_t>(L.g) + (size_t)t0 * c.d_value * eb;
   uint8_t* o = (uint8_t*)out + (size_t)t0 * c.d_model * eb;
-  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.w1T), g, y, tc, c.d_value, c.d_model, c.dtype, pkm::EPI_GATE, sa));
-  PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 1, sa));
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATE2, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_gemm(g, h->at(L.w2T), o, nullptr, tc, c.d_model, c.d_value, c.dtype,
+  PKM_LAUNCH(pkm::launch_gemm(g, h->at(L.w2T), o, tc, c.d_model, c.d_value, c.dtype,
                               c.dtype == PKM_BF16 ? pkm::EPI_STORE_DT : pkm::EPI_STORE_F32, sa));
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATE2, chunk, 1, sa));
   return PKM_OK;
@@ -284,8 +290,8 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   const bool gated = c.memory_plus != 0;
   if (nch == 1) {
     int rc = chunk_select(h, x, 0, T, s, tm, 0);
-    if (!rc) rc = chunk_gather(h, 0, T, out, ydbg, s, tm, 0);
-    if (!rc && gated) rc = chunk_gate(h, x, 0, T, out, ydbg, s, tm, 0);
+    if (!rc) rc = chunk_gather(h, 0, T, out, ydbg, s, tm, 0, false);
+    if (!rc && gated) rc = chunk_gate(h, 0, T, out, s, tm, 0);
     if (rc) return rc;
   } else {
     // fork: both internal streams start after the work already queued on `s`.
@@ -308,14 +314,14 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
       if (rc) return rc;
       PKM_HIP(hipEventRecord(h->ev_sel[ch], h->sA));
       PKM_HIP(hipStreamWaitEvent(h->sB, h->ev_sel[ch], 0));
-      rc = chunk_gather(h, t0, tc, out, ydbg, h->sB, tm, ch);
+      rc = chunk_gather(h, t0, tc, out, ydbg, h->sB, tm, ch, true);
       if (rc) return rc;
       PKM_HIP(hipEventRecord(h->ev_gat[ch], h->sB));
       if (gated && ch > 0) {
         int64_t p0, pc;
         span(ch - 1, p0, pc);
         PKM_HIP(hipStreamWaitEvent(h->sA, h->ev_gat[ch - 1], 0));
-        rc = chunk_gate(h, x, p0, pc, out, ydbg, h->sA, tm, ch - 1);
+        rc = chunk_gate(h, p0, pc, out, h->sA, tm, ch - 1);
         if (rc) return rc;
       }
       last = ch;
@@ -324,7 +330,7 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
       int64_t p0, pc;
       span(last, p0, pc);
       PKM_HIP(hipStreamWaitEvent(h->sA, h->ev_gat[last], 0));
-      int rc = chunk_gate(h, x, p0, pc, out, ydbg, h->sA, tm, last);
+      int rc = chunk_gate(h, p0, pc, out, h->sA, tm, last);
       if (rc) return rc;
     }
     // join: `s` continues after both internal streams

@@ -1,14 +1,15 @@
 // Dense GEMMs of the forward: the query projection q = x W_q, and the two Memory+
-// products ("Memory Layers at Scale" digest, Memory+ block: out = (y * silu(x W1)) W2),
-// with the gate y * silu(.) fused into the epilogue of x W1.
+// products ("Memory Layers at Scale" digest, Memory+ block: out = (y * silu(x W1)) W2):
+// z = x W1 in fp32 (the gate's elementwise part y * silu(z) is fused into the gather,
+// which writes g) and out = g W2.
 //
 // C[M, N] = A[M, K] * Bt[N, K]^T: both operands are K-contiguous (the weights are
 // transposed once at create), fp32 accumulation.
-//  * bf16: matrix cores, v_mfma_f32_32x32x16_bf16.  Block tile 256 x 128 x 64 (128 x 128
-//    for small problems), four waves in a 2 x 2 arrangement, each wave 128 x 64 (4 x 2
-//    MFMA tiles, so each 16-byte LDS operand read feeds 1.33 MFMAs on average).  Tiles
-//    are staged through padded LDS rows; the next K-tile is prefetched into registers
-//    while the current one is multiplied; two blocks share a CU.
+//  * bf16: matrix cores, v_mfma_f32_32x32x16_bf16.  Block tile 256 x 128 (128 x 128 for
+//    small problems) with K-tiles of 32, four waves in a 2 x 2 arrangement, each wave
+//    (BM/2) x (BN/2) (4 x 2 MFMA tiles at 256 x 128, so each 16-byte LDS operand read
+//    feeds 1.33 MFMAs on average).  K-tiles reach padded LDS rows by direct global->LDS
+//    loads into a double buffer; two blocks share a CU.
 //  * fp32: a plain SIMT tile (64 x 64 x 16, 4 x 4 per thread) for the fp32 workloads.
 #include "kernels.hpp"
 
@@ -19,13 +20,13 @@ namespace {
 // Block tile BM x BN, four waves in a 2 x 2 grid, each wave (BM/2) x (BN/2) made of
 // 32 x 32 MFMA tiles.  A and B K-tiles reach LDS by direct global->LDS loads
 // (global_load_lds_dwordx4: each wave instruction fills 64 consecutive 16-byte LDS
-// units) into a double buffer of padded rows (9 units of 16 bytes per 8 data units, so
+// units) into a double buffer of padded rows (5 units of 16 bytes per 4 data units, so
 // the MFMA operand reads are free of bank conflicts); a lane whose unit is padding
 // loads a harmless in-bounds address.  One barrier per K-tile.
 template <int BM, int BN, int EPI>
 __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ Bt, void* __restrict__ C,
-                                                           const float* __restrict__ aux, int64_t M, int N, int K) {
+                                                           int64_t M, int N, int K) {
   constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;    // MFMA tiles per wave
   constexpr int BKT = 32;                      // K per LDS tile
@@ -119,20 +120,16 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(const uint16_t* __res
         const int64_t o = m * N + n;
         if (EPI == EPI_STORE_F32) {
           ((float*)C)[o] = v;
-        } else if (EPI == EPI_STORE_DT) {
-          ((uint16_t*)C)[o] = f32_to_bf16(v);
         } else {
-          ((uint16_t*)C)[o] = f32_to_bf16(aux[o] * silu_f32(v));
+          ((uint16_t*)C)[o] = f32_to_bf16(v);
         }
       }
     }
   }
 }
 
-template <int EPI>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ Bt,
-                                                       float* __restrict__ C, const float* __restrict__ aux, int64_t M,
-                                                       int N, int K) {
+                                                       float* __restrict__ C, int64_t M, int N, int K) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
   const int tid = threadIdx.x;
@@ -176,15 +173,15 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
       const int64_t o = m * N + n;
-      C[o] = EPI == EPI_GATE ? aux[o] * silu_f32(acc[i][j]) : acc[i][j];
+      C[o] = acc[i][j];
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const void* A, const void* Bt, void* C, const float* aux, int64_t M, int N, int K, int dtype,
-                       int epi, hipStream_t s) {
+hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N, int K, int dtype, int epi,
+                       hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (dtype == DT_BF16) {
     const uint16_t* a = (const uint16_t*)A;
@@ -193,27 +190,20 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, const float* aux,
     const bool big = M >= 4096 && N >= 512;
 #define PKM_GEMM(BMV, BNV, E)                                                                            \
   gemm_bf16_kernel<BMV, BNV, E><<<dim3((unsigned)((N + BNV - 1) / BNV), (unsigned)((M + BMV - 1) / BMV)), 256, 0, s>>>( \
-      a, b, C, aux, M, N, K)
+      a, b, C, M, N, K)
     if (big) {
-      switch (epi) {
-        case EPI_STORE_F32: PKM_GEMM(256, 128, EPI_STORE_F32); break;
-        case EPI_STORE_DT: PKM_GEMM(256, 128, EPI_STORE_DT); break;
-        default: PKM_GEMM(256, 128, EPI_GATE); break;
-      }
+      if (epi == EPI_STORE_F32) PKM_GEMM(256, 128, EPI_STORE_F32);
+      else PKM_GEMM(256, 128, EPI_STORE_DT);
     } else {
-      switch (epi) {
-        case EPI_STORE_F32: PKM_GEMM(128, 128, EPI_STORE_F32); break;
-        case EPI_STORE_DT: PKM_GEMM(128, 128, EPI_STORE_DT); break;
-        default: PKM_GEMM(128, 128, EPI_GATE); break;
-      }
+      if (epi == EPI_STORE_F32) PKM_GEMM(128, 128, EPI_STORE_F32);
+      else PKM_GEMM(128, 128, EPI_STORE_DT);
     }
 #undef PKM_GEMM
   } else {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     const float* a = (const float*)A;
     const float* b = (const float*)Bt;
-    if (epi == EPI_GATE) gemm_f32_kernel<EPI_GATE><<<grid, 256, 0, s>>>(a, b, (float*)C, aux, M, N, K);
-    else gemm_f32_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(a, b, (float*)C, aux, M, N, K);
+    gemm_f32_kernel<<<grid, 256, 0, s>>>(a, b, (float*)C, M, N, K);
   }
   return hipGetLastError();
 }

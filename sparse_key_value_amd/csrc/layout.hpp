@@ -15,7 +15,7 @@ struct Layout {
   size_t wqT = 0, khat = 0, w1T = 0, w2T = 0;        // create-time copies
   size_t q = 0, qhat = 0, hidx = 0, hsc = 0;          // per-forward intermediates
   size_t gmax = 0, theta = 0, cand = 0, count = 0;    // selection scratch
-  size_t idx = 0, sc = 0, w = 0, y = 0, g = 0;
+  size_t idx = 0, sc = 0, w = 0, z = 0, g = 0;
   size_t total = 0;
 };
 
@@ -78,8 +78,8 @@ inline Layout make_layout(const pkm_config* c) {
   L.sc = take(T * H * k * 4);
   L.w = take(T * H * k * 4);
   if (c->memory_plus) {
-    L.y = take(T * dv * 4);
-    L.g = take(T * dv * eb);
+    L.z = take(T * dv * 4);    // x W1 (fp32), read by the gather's fused gate
+    L.g = take(T * dv * eb);   // y * silu(x W1), the input of the W2 product
   }
   L.total = off;
   return L;
