@@ -5,6 +5,7 @@
     python bench.py --workload ma_values_32k_bf16      # Memory Attention token-memory values
     python bench.py --workload engram_zipf_2m_bf16 --tables host   # tables in host memory, prefetched
     python bench.py --backward                         # value-table backward + sparse update
+    python bench.py --uniform                          # the gather alone, uniform indices
 
 A step is one whole forward (projection, qk-norm, scoring + per-half top-k,
 combine + softmax, weighted EmbeddingBag over the value table, Memory+ gate) over
@@ -430,6 +431,55 @@ def bench_backward(a):
     print(json.dumps(res), flush=True)
 
 
+def bench_uniform(a):
+    """The gather alone (pkm_embedding_bag) over the workload's table with i.i.d. uniform
+    row indices and random normalised weights: the no-reuse floor of the value read."""
+    import numpy as np
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import CONFIGS
+    from synth import inputs as S
+    from tests.gpu_util import make_value_table
+
+    cfg = CONFIGS[a.workload]
+    T, bag, eb = cfg.T, cfg.H * cfg.k, cfg.elem_bytes
+    log(f"uniform-index gather over {cfg.name}'s table: {T} bags of {bag}, N={cfg.N}, d_v={cfg.d_v}")
+    values = make_value_table(cfg, a.seed)
+    idx, w = S.uniform_bags(a.seed, T, bag, cfg.N)
+    uniq = len(np.unique(idx))
+    idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    y = torch.empty((T, cfg.d_v), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: P.pkm_embedding_bag(values, cfg.N, cfg.d_v, cfg.dtype, idx_d, w_d, T, bag, y, stream=stream)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    rows_b = T * bag * cfg.d_v * eb
+    alg_b = rows_b + T * bag * 8 + T * cfg.d_v * 4
+    res = {
+        "metric": "value-gather GB/s with uniform indices (no-reuse floor), 1 MI355X",
+        "value": alg_b / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (i.i.d. uniform row indices, random normalised weights, table generated on the GPU)",
+        "config": {"workload": cfg.name + " (uniform indices)", "bags": T, "bag_size": bag, "n_keys": cfg.N,
+                   "d_value": cfg.d_v, "unique_rows": uniq, "unique_row_bytes": uniq * cfg.d_v * eb},
+        "roofline": {"bound": "hbm", "kernel": "gather (weighted EmbeddingBag)", "achieved": alg_b / (ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": ms},
+        "value_rows_GBps": rows_b / (ms * 1e-3) / 1e9,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_ma(a):
     """Memory Attention token-memory values: one step = ma_values over the workload's tokens
     (the table fold runs once, before the timing)."""
@@ -516,6 +566,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
+    ap.add_argument("--uniform", action="store_true",
+                    help="time the gather alone with uniform random indices over the workload's table")
     ap.add_argument("--backward", action="store_true",
                     help="time the value-table backward and sparse update instead of the forward")
     ap.add_argument("--tables", choices=["device", "host"], default="device",
@@ -533,6 +585,8 @@ def main():
         return bench_ma(a)
     if a.backward:
         return bench_backward(a)
+    if a.uniform:
+        return bench_uniform(a)
 
     import torch
 
