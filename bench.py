@@ -119,7 +119,7 @@ def cpu_baseline(wl, cfg, target_s, max_tokens=None):
     n = int(max(16, min(max_tokens or wl.T, target_s / max(per_tok, 1e-9))))
     log(f"oracle: {per_tok * 1e3:.1f} ms/token estimated, timing {n} tokens")
     dt = run(n)
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {n} of {wl.T} tokens of {cfg.name}, float64 NumPy oracle, {dt:.1f} s" + note}
 
 
@@ -136,6 +136,16 @@ def host_copy(t):
     for r0 in range(0, t.shape[0], step):
         ht[r0:r0 + step].copy_(dv[r0:r0 + step])
     return host
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def blas_threads():
