@@ -9,7 +9,9 @@
 //    dot product.  The table rows are read once, like the forward gather.
 //  * the per-row gradient: the (row, position) pairs are sorted by row with a stable
 //    radix sort, run-length encoded and scanned (rocPRIM device primitives); one block
-//    per distinct row then sums w * dy over the row's positions in position order (the
+//    per distinct row (a grid as large as the entry count, so that enough blocks are
+//    resident to hide each row's chain of dependent loads) then sums w * dy over the
+//    row's positions in position order (the
 //    result does not depend on scheduling, and no atomics are used) and writes the
 //    gradient and/or applies the update in place.
 #include <rocprim/device/device_radix_sort.hpp>
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__(256) bag_keys_kernel(const int32_t* __restrict
   vals[i] = (uint32_t)i;
 }
 
-// One block per distinct row (grid-strided): the row's gradient in position order.
+// One block per distinct row (grid-strided when the grid is smaller): the row's gradient in position order.
 template <int EB>
 __global__ void __launch_bounds__(256) bag_grad_kernel(const uint32_t* __restrict__ unique,
                                                        const uint32_t* __restrict__ counts,
@@ -347,15 +349,9 @@ int pkm_bag_backward(const pkm_bag_backward_args* a, void* workspace, size_t ws_
   tb = S.temp_bytes;
   PKM_HIP(rocprim::exclusive_scan(ws + S.temp, tb, (const uint32_t*)U(S.counts), U(S.offsets), 0u, (size_t)n,
                                   rocprim::plus<uint32_t>(), s));
-  int cus = 256;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  const int64_t want = (int64_t)cus * 16;
-  const dim3 grid((unsigned)(n < want ? n : want));
+  // one block per possible run (at most n): a block's rows form a chain of dependent loads,
+  // so many resident blocks are what hides the latency; blocks past the run count exit
+  const dim3 grid((unsigned)n);
   uint8_t* tw = a->update ? (uint8_t*)tview : nullptr;
 #define PKM_GRAD(EBV)                                                                                          \
   PKM_LAUNCH((pkm::bag_grad_kernel<EBV><<<grid, 256, 0, s>>>(U(S.unique), U(S.counts), U(S.offsets), U(S.runs), \
