@@ -308,17 +308,29 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
     const bool full = (ch + 1) * CHUNK <= n;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      // bit r: score r reaches the bound (and its sub-key exists).  Building the mask is
+      // branch-free; the appends then loop over the set bits only, so the wave runs as
+      // many append rounds as its busiest lane has candidates in this chunk (usually 0-2)
+      // instead of one masked round for every position that any lane hit.
+      uint32_t m = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float s = acc[g][r];
-        if (s >= thr[g]) {
-          const int sub = sub_of(ch * CHUNK, r, hi);
-          bool take = full || sub < n;
-          if (take && s == thr[g]) take = eq[g]++ < k;  // exact ties with the bound: the first k suffice
-          if (take) {
-            if (cnt[g] < HALF) dst[g][cnt[g]] = make_key(s, (uint32_t)sub);
-            ++cnt[g];
-          }
+      for (int r = 0; r < 16; ++r) m |= (acc[g][r] >= thr[g] ? 1u : 0u) << r;
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m &= (sub_of(ch * CHUNK, r, hi) < n) ? ~0u : ~(1u << r);
+      }
+      while (m) {
+        const int r = __builtin_ctz(m);  // ascending positions: the same order as a scan
+        m &= m - 1;
+        float s = acc[g][0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) s = r == q ? acc[g][q] : s;
+        const int sub = sub_of(ch * CHUNK, r, hi);
+        bool take = true;
+        if (s == thr[g]) take = eq[g]++ < k;  // exact ties with the bound: the first k suffice
+        if (take) {
+          if (cnt[g] < HALF) dst[g][cnt[g]] = make_key(s, (uint32_t)sub);
+          ++cnt[g];
         }
       }
     }
