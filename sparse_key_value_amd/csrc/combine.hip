@@ -18,9 +18,10 @@
 // "staircase" (i + 1)(j + 1) <= k can reach the top-k (119 pairs for k = 32 instead of
 // 1,024).  The staircase is sorted with a bitonic network over two keys per lane.  The
 // fp32 rounding of a sum can merge two distinct sums into a tie that the flat index
-// then breaks the other way, so every one of the k*k pairs is checked against the
-// k-th key found; if any pair off the staircase beats it (a rounding tie, about never
-// with real data) the wave redoes the selection over all k*k pairs.
+// then breaks the other way, so the cells off the staircase are checked against the
+// k-th key found (one check per row of the grid, by monotonicity); if any could reach
+// it (a rounding tie, about never with real data) the wave redoes the selection over
+// all k*k pairs.
 #include "kernels.hpp"
 
 namespace pkm {
@@ -112,16 +113,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   // element e = 2 * lane + slot; the k-th best is element k - 1
   const uint64_t kth = shfl_u64((k - 1) & 1 ? x1 : x0, (k - 1) >> 1);
 
-  // check every pair: nothing off the staircase may beat the k-th key
-  const int kk = k * k;
+  // nothing off the staircase may beat the k-th key.  Both lists are sorted and an fp32
+  // add is monotone, so the largest off-staircase sum of row a is at its first
+  // off-staircase column b0 = floor(k / (a + 1)): if that sum is below the k-th score, no
+  // cell of the row reaches it (a cell can only beat the k-th key by a larger sum, or by
+  // an equal sum with a lower flat index).  Lane a checks row a; a row that fails is
+  // settled by the exhaustive selection below.
+  const float kth_score = key_score(kth);
   bool beaten = false;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int cidx = lane + 64 * r;
-    if (cidx < kk) {
-      const int a = cidx / k, b = cidx - a * k;
-      if ((a + 1) * (b + 1) > k && cell_key(a, b) > kth) beaten = true;
-    }
+  if (lane < k) {
+    const int b0 = k / (lane + 1);
+    if (b0 < k) beaten = key_score(L0[lane]) + key_score(L1[b0]) >= kth_score;
   }
   uint64_t mine;  // lane j < k ends up with the j-th best key
   if (__ballot(beaten) == 0) {
@@ -130,6 +132,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
     mine = (lane & 1) ? a1 : a0;
   } else {
     // exhaustive: k rounds of a wave-wide maximum over all k*k keys
+    const int kk = k * k;
     uint64_t key[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
