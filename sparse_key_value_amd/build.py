@@ -26,6 +26,10 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+ROCM_LIB = "/opt/rocm/lib"
+# hipBLASLt for the plain bf16 GEMMs of the forward
+LINK_LIBS = {"pkm": [f"-L{ROCM_LIB}", "-lhipblaslt", f"-Wl,-rpath,{ROCM_LIB}"]}
+
 TARGETS = {
     "pkm": (os.path.join(ROOT, "sparse_key_value_amd", "csrc"), os.path.join(ROOT, "sparse_key_value_amd", "libpkm.so")),
     "synth": (os.path.join(ROOT, "synth", "csrc"), os.path.join(ROOT, "synth", "libpkm_synth.so")),
@@ -57,7 +61,8 @@ def build_target(name: str, jobs: int = 8, verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
     tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    libs = LINK_LIBS.get(name, [])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *libs])
     os.replace(tmp, out)
     return out
 
