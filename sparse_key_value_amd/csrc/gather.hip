@@ -119,26 +119,28 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         pk[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
-      *(u32x4*)((uint16_t*)y + o) = pk;
+      __builtin_nontemporal_store(pk, (u32x4*)((uint16_t*)y + o));
     } else {
-      *(f32x4*)((float*)y + o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)((float*)y + o));
     }
     return;
   }
+  // outputs are streamed (nontemporal stores): they are not read again by this kernel
   if (y_f32) {
     float* yo = (float*)y + o;
 #pragma unroll
-    for (int e = 0; e < E; e += 4) *(f32x4*)(yo + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    for (int e = 0; e < E; e += 4)
+      __builtin_nontemporal_store(f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]}, (f32x4*)(yo + e));
   } else if (EB == 2) {
     uint16_t* yo = (uint16_t*)y + o;
     u32x4 pk;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       pk[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
-    *(u32x4*)yo = pk;
+    __builtin_nontemporal_store(pk, (u32x4*)yo);
   } else {
     float* yo = (float*)y + o;
-    *(f32x4*)yo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)yo);
   }
 }
 
