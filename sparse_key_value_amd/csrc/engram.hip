@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
     float o[E];
 #pragma unroll
     for (int x = 0; x < E; ++x) o[x] = a.residual ? __builtin_fmaf(alpha, e[i][x], hf[i][x]) : alpha * e[i][x];
-    *(u32x4*)(a.out + ((size_t)t * a.slices + s) * 16) = EL::pack(o);
+    __builtin_nontemporal_store(EL::pack(o), (u32x4*)(a.out + ((size_t)t * a.slices + s) * 16));
     if (a.e_out) {
       float* eo = a.e_out + (size_t)t * a.d + (size_t)s * E;
 #pragma unroll
