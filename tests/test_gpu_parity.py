@@ -237,6 +237,27 @@ def test_edge_shapes(case, dt):
     wl.close()
 
 
+@pytest.mark.parametrize("case", [
+    # bf16 without qk-norm; 96-wide values (12 slices of 16 bytes: lanes not a multiple of 64)
+    dict(name="bf16_no_norm_dv96", dtype="bf16", qk_norm=False, n_sub=128, k=16, H=2, d_q=256, d_model=128, d_v=96,
+         T=90),
+    # fp32 with qk-norm and the gate
+    dict(name="f32_norm_gate", dtype="f32", qk_norm=True, memory_plus=True, n_sub=150, k=8, H=3, d_q=128, d_model=96,
+         d_v=96, T=77),
+    # eight heads, gated bf16
+    dict(name="h8_gate", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=256, k=32, H=8, d_q=128, d_model=256,
+         d_v=256, T=65),
+])
+def test_flag_combinations(case):
+    case = dict(case)
+    name = case.pop("name")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=name, memory_plus=case.pop("memory_plus", False), **case)
+    say(f"flags {cfg.name}")
+    wl = _G().Workload(cfg, seed=7)
+    full_check(wl, run_debug(wl))
+    wl.close()
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_exact_ties_resolve_to_lowest_index(dt):
     """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
