@@ -33,7 +33,7 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 HOST_LINK_PEAK_GBPS = 64.0    # PCIe 5.0 x16 host link, one direction, published
 METRIC = "PKM fwd tokens/s + value-gather GB/s (% of HBM peak) at 16M keys, 1 MI355X"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gather_memplus_16m_bf16_counters.json")
-GATHER_SRC = os.path.join(ROOT, "sparse_key_value_amd", "csrc", "gather.hip")
+ENGRAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "engram_zipf_2m_bf16_counters.json")
 
 
 def log(msg):
@@ -57,15 +57,20 @@ def flops(cfg, T):
     return proj, score, gate
 
 
-def counter_traffic():
-    """HBM bytes per gather launch from the committed rocprofv3 counter runs, if the kernel is unchanged."""
+def counter_traffic(counters_file=COUNTERS_FILE):
+    """HBM bytes per launch from a committed rocprofv3 counter run, if its kernel source is unchanged.
+
+    The counter file records the kernel's source file and that file's sha256; a source that
+    has changed since the counters were taken gives None.
+    """
     try:
-        rec = json.load(open(COUNTERS_FILE))
-        sha = hashlib.sha256(open(GATHER_SRC, "rb").read()).hexdigest()
-        if rec.get("gather_source_sha256") != sha:
+        rec = json.load(open(counters_file))
+        src = os.path.join(ROOT, rec["source"])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
             return None
         return rec.get("traffic_bytes_per_launch")
-    except (OSError, ValueError):
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -223,6 +228,7 @@ def bench_engram(a):
     except Exception as ex:  # pragma: no cover - reporting only
         log(f"unique-row count failed: {ex}")
     achieved = alg_b / (launch_ms * 1e-3) / 1e9
+    traffic = counter_traffic(ENGRAM_COUNTERS_FILE) if cfg.name == "engram_zipf_2m_bf16" else None
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -262,7 +268,7 @@ def bench_engram(a):
                    "orders": list(range(cfg.min_order, cfg.min_order + cfg.n_orders)), "heads": cfg.heads,
                    "head_dim": cfg.head_dim, "table_rows": cfg.table_rows, "d": cfg.d, "table_GiB": tbytes / 2**30},
         "roofline": {"bound": "hbm", "kernel": "engram_forward (hash + row gather + gate)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": launch_ms},
         "unique_rows": uniq,
         "unique_row_bytes": uniq * cfg.head_dim * eb if uniq is not None else None,
@@ -676,7 +682,8 @@ def main():
     if not a.no_cpu_baseline and not host:
         cpu = cpu_baseline(wl, cfg, a.cpu_seconds)
 
-    traffic = counter_traffic() if not host else None
+    # the committed counters were taken at the headline workload with device-resident tables
+    traffic = counter_traffic() if (not host and cfg.name == "memplus_16m_bf16") else None
     res = {
         "metric": METRIC,
         "value": tok_s,
