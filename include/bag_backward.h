@@ -16,7 +16,9 @@
  * An index outside [0, n_rows) read nothing and receives nothing (dw = 0).
  *
  * Deterministic: the (row, position) pairs are sorted by row with a stable radix sort
- * and every row's gradient is summed in position order; no atomics.
+ * and every row's gradient is summed in position order; no atomics.  dw and ds always
+ * use the table as it was before the call, also when the update is applied in the same
+ * call (dw then comes from the rows the update reads, before they are written).
  *
  * Conventions as in pkm.h (caller-owned DEVICE pointers unless stated, row-major,
  * `stream` a hipStream_t as void*, nothing allocated, PKM_OK or a negative code with
@@ -59,8 +61,10 @@ typedef struct {
  * 0 and sets pkm_last_error() on bad sizes. */
 size_t pkm_bag_backward_workspace_size(int64_t n_bags, int32_t bag_size, int64_t n_rows);
 
-/* Enqueue the backward on `stream`: dw and ds first (they read the table before any
- * update), then the sort, the per-row sums and the outputs asked for.  The workspace
+/* Enqueue the backward on `stream`: without the update, dw and ds from their own pass
+ * over the rows; the sort when rows, grad, n_unique or the update are asked for; with
+ * the update, one pass per token that updates every touched row once and takes dw from
+ * the old rows on the way, then ds; the distinct rows and gradients last.  The workspace
  * (device, 256-byte aligned, ws_bytes >= the size above) is used exclusively by this
  * call until the stream reaches its end. */
 int pkm_bag_backward(const pkm_bag_backward_args* args, void* workspace, size_t ws_bytes, void* stream);

@@ -105,11 +105,85 @@ def test_small_with_duplicates_and_out_of_range(dt):
     got2 = _run(table, n_rows, dim, dt, idx, w, dy, k, update=True, lr=lr)
     after = to_host(table)
     np.testing.assert_array_equal(got2["rows"], got["rows"])
+    # with the update, dw and ds come from the rows the update reads: still the old rows
+    _check(got2, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), k)
     ref = O.to_f64(before[got["rows"]], dt) - lr * got2["grad"].astype(np.float64)
     _one_ulp(after[got["rows"]], ref, dt)
     untouched = np.setdiff1d(np.arange(n_rows), got["rows"])
     np.testing.assert_array_equal(np.asarray(after[untouched]).view(np.uint8),
                                   np.asarray(before[untouched]).view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_update_alone_matches_update_with_outputs(dt):
+    """The update with no other output asked for (no sort outputs, no gradient) leaves the
+    same table, bit for bit, as the update that also writes the gradients, and that table
+    is one storage ulp from the stage-wise oracle; rows repeated within and across bags."""
+    import sparse_key_value_amd as P
+    from tests.gpu_util import to_dev, to_host
+    rng = np.random.default_rng(7)
+    n_rows, dim, n_bags, bag = 300, 96 if dt == "bf16" else 64, 200, 24
+    idx = rng.integers(-2, n_rows + 2, size=(n_bags, bag))
+    idx[:9, :6] = 5                                                # one row 54 times
+    idx[20, 3] = idx[20, 11] = 299                                 # a row twice in one bag, last row
+    w = rng.random((n_bags, bag)).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(11, np.arange(n_rows), dim, dt)
+    t1, t2 = to_dev(host, dt), to_dev(host, dt)
+    lr = 0.25
+    say(f"bag update alone {dt}")
+    ref = _run(t1, n_rows, dim, dt, idx, w, dy, 8, update=True, lr=lr)
+    ws = torch.empty(P.pkm_bag_backward_workspace_size(n_bags, bag, n_rows), dtype=torch.uint8, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    P.pkm_bag_backward(t2, n_rows, dim, dt, dev(idx.astype(np.int32)), dev(w), dev(dy), n_bags, bag, update=True,
+                       lr=lr, workspace=ws)
+    torch.cuda.synchronize()
+    # ds alone with the update: dw goes to the workspace
+    t3 = to_dev(host, dt)
+    ds3 = torch.full((n_bags, bag), float("nan"), device="cuda")
+    P.pkm_bag_backward(t3, n_rows, dim, dt, dev(idx.astype(np.int32)), dev(w), dev(dy), n_bags, bag, ds=ds3,
+                       softmax_group=8, update=True, lr=lr, workspace=ws)
+    torch.cuda.synchronize()
+    a1, a2 = to_host(t1), to_host(t2)
+    np.testing.assert_array_equal(np.asarray(a2).view(np.uint8), np.asarray(a1).view(np.uint8))
+    np.testing.assert_array_equal(np.asarray(to_host(t3)).view(np.uint8), np.asarray(a1).view(np.uint8))
+    np.testing.assert_array_equal(ds3.cpu().numpy(), ref["ds"])
+    rows_ref, grad_ref = B.grad_rows(idx, w.astype(np.float64), dy.astype(np.float64), n_rows)
+    np.testing.assert_array_equal(ref["rows"], rows_ref)
+    PAR.check_rows(ref["grad"], grad_ref, 1e-4, "row gradients")
+    _one_ulp(a2[rows_ref], O.to_f64(host[rows_ref], dt) - lr * ref["grad"].astype(np.float64), dt)
+    untouched = np.setdiff1d(np.arange(n_rows), rows_ref)
+    np.testing.assert_array_equal(np.asarray(a2[untouched]).view(np.uint8), np.asarray(host[untouched]).view(np.uint8))
+
+
+@pytest.mark.parametrize("dt,dim", [("bf16", 64), ("f32", 96), ("bf16", 1024), ("bf16", 1280), ("f32", 1536),
+                                    ("f32", 2048), ("bf16", 2048)])
+def test_fused_step_shapes(dt, dim):
+    """dw, ds, gradients and the update in one call, for widths that give one, two and
+    four waves per token and one or two 16-byte slices per lane (some lanes idle)."""
+    from tests.gpu_util import to_dev, to_host
+    rng = np.random.default_rng(dim)
+    n_rows, n_bags, k, H = 700, 64, 8, 4
+    bag = H * k
+    idx = rng.integers(-1, n_rows + 1, size=(n_bags, bag))
+    idx[:6, :5] = 3                                                # a shared row, also within bags
+    idx[40, 7] = idx[41, 7] = n_rows - 1
+    s_ = rng.standard_normal((n_bags, H, k))
+    w = np.exp(s_ - s_.max(-1, keepdims=True))
+    w = (w / w.sum(-1, keepdims=True)).reshape(n_bags, bag).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(13, np.arange(n_rows), dim, dt)
+    table = to_dev(host, dt)
+    lr = 0.5
+    say(f"bag fused step {dt} dim {dim}")
+    got = _run(table, n_rows, dim, dt, idx, w, dy, k, update=True, lr=lr)
+    rows_of = lambda r: O.to_f64(host[np.asarray(r)], dt)
+    _check(got, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), k)
+    after = to_host(table)
+    _one_ulp(after[got["rows"]], O.to_f64(host[got["rows"]], dt) - lr * got["grad"].astype(np.float64), dt)
+    untouched = np.setdiff1d(np.arange(n_rows), got["rows"])
+    np.testing.assert_array_equal(np.asarray(after[untouched]).view(np.uint8),
+                                  np.asarray(host[untouched]).view(np.uint8))
 
 
 def test_deterministic():
@@ -173,4 +247,36 @@ def test_full_size_sampled():
         ref = np.sum(flat_w[pos, None] * dy[pos // bag].astype(np.float64), axis=0)
         u = int(np.searchsorted(got["rows"], r))
         PAR.check_rows(got["grad"][u].cpu().numpy()[None], ref[None], 1e-4, f"gradient of row {r}")
+    del got
+    # the update alone, as benchmarked (distinct rows and their count, no gradients): sampled
+    # touched rows against the float64 oracle's step, sampled untouched rows unchanged
+    import sparse_key_value_amd as P
+    from tests.gpu_util import to_host
+    lr = 1e-2
+    n = T * bag
+    rows = torch.empty(n, dtype=torch.int32, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(P.pkm_bag_backward_workspace_size(T, bag, cfg.N), dtype=torch.uint8, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    say("bag update full size")
+    dw2 = torch.full((T, bag), float("nan"), device="cuda")
+    ds2 = torch.full((T, bag), float("nan"), device="cuda")
+    P.pkm_bag_backward(wl.values, cfg.N, cfg.d_v, cfg.dtype, dev(idx.astype(np.int32)), dev(w), dev(dy), T, bag,
+                       dw=dw2, ds=ds2, softmax_group=cfg.k, rows=rows, n_unique=nu, update=True, lr=lr, workspace=ws)
+    torch.cuda.synchronize()
+    _check({"dw": dw2.cpu().numpy(), "ds": ds2.cpu().numpy()}, rows_of, cfg.N, idx, w.astype(np.float64),
+           dy.astype(np.float64), cfg.k, tokens=tokens)
+    assert int(nu.item()) == len(uniq)
+    np.testing.assert_array_equal(rows[:len(uniq)].cpu().numpy(), uniq)
+    for r in pick:
+        pos = np.nonzero(flat_i == r)[0]
+        g = np.sum(flat_w[pos, None] * dy[pos // bag].astype(np.float64), axis=0)
+        ref = O.to_f64(wl.host_rows(np.array([r])), cfg.dtype)[0] - lr * g
+        after = O.to_f64(to_host(wl.values[int(r)])[None], cfg.dtype)[0]
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert np.all(np.abs(after - ref) <= ulp + lr * 1e-4 * np.abs(g).max()), f"update of row {r}"
+    untouched = np.setdiff1d(rng.integers(0, cfg.N, 64), uniq)
+    got_u = to_host(wl.values[torch.from_numpy(untouched).cuda()])
+    np.testing.assert_array_equal(np.asarray(got_u).view(np.uint8),
+                                  np.asarray(wl.host_rows(untouched)).view(np.uint8))
     wl.close()
