@@ -500,6 +500,69 @@ def bench_uniform(a):
     print(json.dumps(res), flush=True)
 
 
+def bench_shard(a):
+    """One GPU's share of a column-sharded value table: the gather (pkm_embedding_bag) of the
+    forward's own indices and weights over a [N, d_v / G] slice, as each of G GPUs would run
+    it after the replicated selection.  The exchange between GPUs is not part of it."""
+    import numpy as np
+    import torch
+
+    import sparse_key_value_amd as P
+    from synth import CONFIGS
+    from synth import device as SD
+    from tests.gpu_util import TORCH_DT, Workload
+
+    cfg = CONFIGS[a.workload]
+    G = a.shard_columns
+    T, bag, eb = cfg.T, cfg.H * cfg.k, cfg.elem_bytes
+    if cfg.d_v % G or (cfg.d_v // G * eb) % 16:
+        raise SystemExit(f"d_v = {cfg.d_v} does not split into {G} slices of a multiple of 16 bytes")
+    dv = cfg.d_v // G
+    log(f"column shard of {cfg.name}: {G} shards, slice [{cfg.N}, {dv}], {T} bags of {bag}")
+    wl = Workload(cfg, seed=a.seed)
+    out = torch.empty((T, cfg.d_out), dtype=wl.dev["x"].dtype, device="cuda")
+    idx = torch.empty((T, bag), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, bag), dtype=torch.float32, device="cuda")
+    P.pkm_forward(wl.pkm.handle, wl.dev["x"], T, out, idx, w)
+    torch.cuda.synchronize()
+    uniq = int(torch.unique(idx).numel())
+    wl.close()
+    del wl, out
+    torch.cuda.empty_cache()
+    table = torch.empty((cfg.N, dv), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    SD.fill_values(table, a.seed)
+    y = torch.empty((T, dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda: P.pkm_embedding_bag(table, cfg.N, dv, cfg.dtype, idx, w, T, bag, y, stream=stream)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    rows_b = T * bag * dv * eb
+    alg_b = rows_b + T * bag * 8 + T * dv * 4
+    res = {
+        "metric": f"value-gather GB/s of one GPU's column shard (d_v / {G}) with the forward's indices, 1 MI355X",
+        "value": alg_b / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (indices and weights of a real forward; slice generated on the GPU)",
+        "config": {"workload": f"{cfg.name} column shard 1 of {G}", "bags": T, "bag_size": bag, "n_keys": cfg.N,
+                   "d_value_slice": dv, "row_bytes": dv * eb, "unique_rows": uniq},
+        "roofline": {"bound": "hbm", "kernel": "gather (weighted EmbeddingBag) over the slice",
+                     "achieved": alg_b / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": ms},
+        "value_rows_GBps": rows_b / (ms * 1e-3) / 1e9,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_ma(a):
     """Memory Attention token-memory values: one step = ma_values over the workload's tokens
     (the table fold runs once, before the timing)."""
@@ -588,14 +651,16 @@ def main():
     ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
     ap.add_argument("--uniform", action="store_true",
                     help="time the gather alone with uniform random indices over the workload's table")
+    ap.add_argument("--shard-columns", type=int, default=0,
+                    help="time one GPU's gather over a d_v / G column slice of the table (G > 1)")
     ap.add_argument("--backward", action="store_true",
                     help="time the value-table backward and sparse update instead of the forward")
     ap.add_argument("--tables", choices=["device", "host"], default="device",
                     help="Engram workloads: keep the tables in HBM or in pinned host memory (prefetched)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the forward has no multi-GPU path "
-              "in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the path has no multi-GPU execution; "
+              "--shard-columns G times one GPU's share of a column-sharded table", file=sys.stderr)
         sys.exit(2)
 
     from synth import configs as C
@@ -607,6 +672,8 @@ def main():
         return bench_backward(a)
     if a.uniform:
         return bench_uniform(a)
+    if a.shard_columns > 1:
+        return bench_shard(a)
 
     import torch
 

@@ -163,6 +163,7 @@ def test_device_value_generator_is_bit_identical_to_host():
 @pytest.mark.parametrize("dt,dim,n_rows,n_bags,bag", [
     ("bf16", 2048, 5000, 37, 128), ("bf16", 1024, 3000, 130, 33), ("f32", 256, 4000, 65, 32),
     ("bf16", 64, 700, 300, 5), ("f32", 12, 99, 17, 3), ("bf16", 4096, 257, 9, 16),
+    ("bf16", 256, 6000, 80, 128),     # one GPU's column shard of the 2048-wide table over 8 GPUs
 ])
 def test_embedding_bag_matches_oracle(dt, dim, n_rows, n_bags, bag):
     import sparse_key_value_amd as P
