@@ -124,8 +124,12 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
       const int row = p / U16, col = (p % U16) ^ (row % U16);
       int sub = ch * CHUNK + row;
       sub = sub < n ? sub : 0;
+      // a 32-bit offset from the wave-uniform base (one pair's sub-keys: n_sub * RB < 2^32
+      // bytes) keeps one VGPR per address; 64-bit per-lane addresses made pass 2 spill
+      // them, and every reload from scratch waited for all loads in flight
+      const uint32_t off = (uint32_t)sub * RB + (uint32_t)col * 16;
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kbase + (size_t)sub * RB + col * 16),
+          (const void __attribute__((address_space(1)))*)(kbase + off),
           (void __attribute__((address_space(3)))*)(ks + buf * CHUNK * RB + (wv * DPW + i) * 64 * 16), 16, 0, 0);
     }
   };
@@ -140,11 +144,34 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
     if (ch + 1 < nch) fetch(ch + 1, buf ^ 1);
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
     f32x16 acc[2] = {f32x16{}, f32x16{}};
+    if constexpr (M::EB == 2) {
+      // bf16: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling groups
+      // below keep the compiler from pulling the reads back next to their use (it
+      // otherwise waits for the LDS every two k-steps).  (fp32 keeps the plain loop: with
+      // one-register operands the groups only lengthen live ranges and cause spills.)
+      constexpr int PD = 4;
+      typename M::frag a[M::NK];
 #pragma unroll
-    for (int kk = 0; kk < M::NK; ++kk) {
-      const typename M::frag a = M::lds_k(myrow, swz, kk, hi);
-      acc[0] = M::mma(a, qf[0][kk], acc[0]);
-      acc[1] = M::mma(a, qf[1][kk], acc[1]);
+      for (int kk = 0; kk < PD && kk < M::NK; ++kk) a[kk] = M::lds_k(myrow, swz, kk, hi);
+#pragma unroll
+      for (int kk = 0; kk < M::NK; ++kk) {
+        if (kk + PD < M::NK) a[kk + PD] = M::lds_k(myrow, swz, kk + PD, hi);
+        acc[0] = M::mma(a[kk], qf[0][kk], acc[0]);
+        acc[1] = M::mma(a[kk], qf[1][kk], acc[1]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PD < M::NK ? PD : M::NK, 0);  // DS reads
+#pragma unroll
+      for (int kk = 0; kk < M::NK; ++kk) {
+        if (kk + PD < M::NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                      // MFMAs
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < M::NK; ++kk) {
+        const typename M::frag a = M::lds_k(myrow, swz, kk, hi);
+        acc[0] = M::mma(a, qf[0][kk], acc[0]);
+        acc[1] = M::mma(a, qf[1][kk], acc[1]);
+      }
     }
     on_tile(ch, acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);
