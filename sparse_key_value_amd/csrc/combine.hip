@@ -63,7 +63,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
                                                       float* __restrict__ half_score, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, float* __restrict__ w) {
   __shared__ uint64_t lists[4][2][32];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index made explicitly uniform: the row, its counts and the ranking loops
+  // below are then scalar (a per-lane count made each loop divergent, with exec-mask
+  // updates in every iteration)
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;  // row = t * H + h
   if (row >= rows) return;
 
@@ -76,17 +79,36 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
     const uint64_t* cr = cand + r2 * CAND;
     const uint64_t x0 = lane < na ? cr[lane] : 0ull;
     const uint64_t x1 = lane < nb ? cr[CAND / 2 + lane] : 0ull;
-    int r0 = 0, r1 = 0;
-    for (int i = 0; i < na; ++i) {
+    // rank = the number of candidates with a larger key; two broadcasts per step so that
+    // the compares of one step do not wait on each other's carry
+    int r0 = 0, r1 = 0, q0 = 0, q1 = 0;
+    int i = 0;
+    for (; i + 1 < na; i += 2) {
+      const uint64_t y = readlane_u64(x0, i), z = readlane_u64(x0, i + 1);
+      r0 += y > x0;
+      r1 += y > x1;
+      q0 += z > x0;
+      q1 += z > x1;
+    }
+    if (i < na) {
       const uint64_t y = readlane_u64(x0, i);
       r0 += y > x0;
       r1 += y > x1;
     }
-    for (int i = 0; i < nb; ++i) {
+    for (i = 0; i + 1 < nb; i += 2) {
+      const uint64_t y = readlane_u64(x1, i), z = readlane_u64(x1, i + 1);
+      r0 += y > x0;
+      r1 += y > x1;
+      q0 += z > x0;
+      q1 += z > x1;
+    }
+    if (i < nb) {
       const uint64_t y = readlane_u64(x1, i);
       r0 += y > x0;
       r1 += y > x1;
     }
+    r0 += q0;
+    r1 += q1;
     if (lane < na && r0 < k) lists[wv][c][r0] = x0;
     if (lane < nb && r1 < k) lists[wv][c][r1] = x1;
   }

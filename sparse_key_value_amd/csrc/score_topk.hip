@@ -331,20 +331,30 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
     thr[g] = t < T ? theta[row[g]] : __builtin_inff();
     dst[g] = cand + row[g] * CAND + hi * HALF;
   }
+  // thz: the bound with a zero bound taken as -0, so that the sign of (score - thz) is
+  // set exactly when score < bound, -0 scores included (x - x is +0; finite values)
+  float thz[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
   sweep<DT, DH>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      // bit r: score r reaches the bound (and its sub-key exists).  Building the mask is
-      // branch-free; the appends then loop over the set bits only, so the wave runs as
-      // many append rounds as its busiest lane has candidates in this chunk (usually 0-2)
-      // instead of one masked round for every position that any lane hit.
-      uint32_t m = 0;
+      // bit r: score r reaches the bound.  The sign bits of the differences are shifted in
+      // with v_alignbit: two VALU ops per score and no lane masks (a compare and select
+      // per score costs twice that, with a wait state after every compare).  The appends
+      // then loop over the set bits only, so the wave runs as many append rounds as its
+      // busiest lane has candidates in this chunk (usually 0-2).
+      uint32_t miss = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m |= (acc[g][r] >= thr[g] ? 1u : 0u) << r;
-      if (!full) {
+      for (int r = 15; r >= 0; --r) miss = __builtin_amdgcn_alignbit(miss, __float_as_uint(acc[g][r] - thz[g]), 31);
+      uint32_t m = ~miss & 0xFFFFu;
+      if (!full) {  // the last chunk: only sub-keys < n exist
+        const int nv = n - ch * CHUNK;
+        uint32_t valid = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m &= (sub_of(ch * CHUNK, r, hi) < n) ? ~0u : ~(1u << r);
+        for (int r = 0; r < 16; ++r) valid |= (8 * (r >> 2) + 4 * hi + (r & 3) < nv ? 1u : 0u) << r;
+        m &= valid;
       }
       while (m) {
         const int r = __builtin_ctz(m);  // ascending positions: the same order as a scan

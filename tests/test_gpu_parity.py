@@ -248,6 +248,9 @@ def test_edge_shapes(case, dt):
     # eight heads, gated bf16
     dict(name="h8_gate", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=256, k=32, H=8, d_q=128, d_model=256,
          d_v=256, T=65),
+    # 256-wide sub-keys (the 16M-key kernels) with a partial last chunk of sub-keys
+    dict(name="dh256_partial_chunk", dtype="bf16", qk_norm=True, n_sub=77, k=8, H=2, d_q=512, d_model=128, d_v=64,
+         T=70),
 ])
 def test_flag_combinations(case):
     case = dict(case)
