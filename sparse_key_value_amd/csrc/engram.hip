@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
   using EL = Elems<EB>;
   constexpr int E = EL::E;
   __shared__ int32_t rows_s[4][MAX_ORDERS * 64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= a.T) return;
 

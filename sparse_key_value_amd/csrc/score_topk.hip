@@ -98,7 +98,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), hi = lane >> 5;
 
   typename M::frag qf[2][M::NK];
 #pragma unroll
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qh
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   float run[2] = {-__builtin_inff(), -__builtin_inff()};
   float buf[2][8];
   int nbuf = 0;  // groups in buf (wave-uniform)
@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hi = lane >> 5;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   float thr[2];
   int cnt[2] = {0, 0}, eq[2] = {0, 0};
   uint64_t* dst[2];
@@ -389,7 +389,7 @@ __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qh
                                                        int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
                                                        int32_t* __restrict__ count) {
   __shared__ float qs[4][DH];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t waves = (int64_t)gridDim.x * 4;
   for (int64_t base = ((int64_t)blockIdx.x * 4 + wv) * 64; base < rows2; base += waves * 64) {
     const int64_t r = base + lane;
