@@ -79,12 +79,12 @@ typedef struct {
 
 /* Stage ids for the optional per-stage timing. */
 enum {
-  PKM_STAGE_PROJECT = 0,  /* q = x W_q */
+  PKM_STAGE_PROJECT = 0,  /* q = x W_q (Memory+: with z = x W1 in the same GEMM) */
   PKM_STAGE_QNORM = 1,    /* qk-norm + split */
   PKM_STAGE_SCORE = 2,    /* sub-key scoring fused with the per-half top-k */
   PKM_STAGE_COMBINE = 3,  /* k x k combine, final top-k, softmax */
   PKM_STAGE_GATHER = 4,   /* weighted EmbeddingBag over the value table (Memory+: with y * silu(z)) */
-  PKM_STAGE_GATE1 = 5,    /* z = x W1, before the gather (Memory+ only) */
+  PKM_STAGE_GATE1 = 5,    /* empty: z = x W1 is computed with the projection */
   PKM_STAGE_GATE2 = 6,    /* (.) W2 (Memory+ only) */
   PKM_STAGE_TOTAL = 7,    /* the whole forward */
   PKM_NUM_STAGES = 8

@@ -199,25 +199,26 @@ int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream
   const int H = c.n_heads, dq = c.d_query, k = c.k;
   const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
   const uint8_t* xc = (const uint8_t*)x + (size_t)t0 * c.d_model * eb;
-  float* q = h->at<float>(L.q) + (size_t)t0 * H * dq;
+  float* q = h->at<float>(L.q) + (size_t)t0 * L.qz_cols;
   uint8_t* qhat = h->at<uint8_t>(L.qhat) + (size_t)t0 * H * dq * eb;
-  // a1: q = x W_q (fp32)
+  // a1: q = x W_q (fp32); with the Memory+ gate the same GEMM also computes z = x W1 (the
+  // first product of a8) into the next d_v columns: one 16,384 x 4,096 product runs
+  // faster than two of 16,384 x 2,048 on MI355X
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.wqT), q, tc, H * dq, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
+  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.wqT), q, tc, (int)L.qz_cols, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, chunk, 1, sa));
   // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_rownorm(q, 1, qhat, c.dtype, tc * H, dq, c.qk_norm, c.norm_eps, sa));
+  PKM_LAUNCH(pkm::launch_rownorm(q, 1, qhat, c.dtype, tc * H, dq, c.qk_norm, c.norm_eps, sa, H, L.qz_cols));
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 1, sa));
   // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
   const size_t sel = (size_t)t0 * H * k;
   int rc = run_select(h, qhat, tc, scratch_at(h, t0), h->at<int32_t>(L.hidx) + 2 * sel, h->at<float>(L.hsc) + 2 * sel,
                       h->at<int32_t>(L.idx) + sel, h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
   if (rc || !c.memory_plus) return rc;
-  // a8, first product: z = x W1 (fp32), consumed by the gather's fused gate
-  float* z = h->at<float>(L.z) + (size_t)t0 * c.d_value;
+  // z = x W1 came with the projection: the stage is kept, empty, so that stage records
+  // keep their shape
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 0, sa));
-  PKM_LAUNCH(pkm::launch_gemm(xc, h->at(L.w1T), z, tc, c.d_value, c.d_model, c.dtype, pkm::EPI_STORE_F32, sa));
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATE1, chunk, 1, sa));
   return PKM_OK;
 }
@@ -237,9 +238,9 @@ int chunk_gather(pkm_handle* h, int64_t t0, int64_t tc, void* out, float* ydbg, 
   const float* w = h->at<float>(L.w) + sel;
   PKM_LAUNCH(tm.stage(PKM_STAGE_GATHER, chunk, 0, sb));
   if (c.memory_plus) {
-    const float* z = h->at<float>(L.z) + (size_t)t0 * c.d_value;
+    const float* z = h->at<float>(L.q) + (size_t)t0 * L.qz_cols + (size_t)H * c.d_query;  // columns of x W1
     uint8_t* g = h->at<uint8_t>(L.g) + (size_t)t0 * c.d_value * eb;
-    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, g, 1, sb, z, shared));
+    PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k, g, 1, sb, z, shared, L.qz_cols));
     if (ydbg)
       PKM_LAUNCH(pkm::launch_gather(h->values, N, c.d_value, c.dtype, idx, w, tc, H * k,
                                     ydbg + (size_t)t0 * c.d_value, 0, sb, nullptr, shared));

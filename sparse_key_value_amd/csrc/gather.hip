@@ -45,7 +45,8 @@ struct VecTraits<4> {  // fp32: 4 elements per 16 bytes
 template <int EB, int UNROLL, bool GATE>
 __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
                                            const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
-                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z);
+                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z,
+                                           int64_t z_ld);
 
 // Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bags blockIdx.x*BPB+g,
 // then + gridDim.x*BPB, ... (one block per group of bags, or, beside other kernels, a
@@ -56,19 +57,20 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
                                                      int row_vecs, int tpr, int bags_per_block,
                                                      const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                      int64_t n_bags, int bag, void* __restrict__ y, int y_f32,
-                                                     const float* __restrict__ z) {
+                                                     const float* __restrict__ z, int64_t z_ld) {
   int g = threadIdx.x / tpr;
   if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
   const int col = blockIdx.y * tpr + (threadIdx.x - g * tpr);  // 16-byte slice index in the row
   if (g >= bags_per_block || col >= row_vecs) return;
   for (int64_t b = (int64_t)blockIdx.x * bags_per_block + g; b < n_bags; b += (int64_t)gridDim.x * bags_per_block)
-    gather_bag<EB, UNROLL, GATE>(table, n_rows, row_vecs, col, idx, w, b, bag, y, y_f32, z);
+    gather_bag<EB, UNROLL, GATE>(table, n_rows, row_vecs, col, idx, w, b, bag, y, y_f32, z, z_ld);
 }
 
 template <int EB, int UNROLL, bool GATE>
 __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
                                            const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
-                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z) {
+                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z,
+                                           int64_t z_ld) {
   using VT = VecTraits<EB>;
   constexpr int E = VT::E;
   const int32_t* bi = idx + b * bag;
@@ -110,7 +112,7 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
     // g = y * silu(z), stored in the table's type
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
-      const f32x4 zz = __builtin_nontemporal_load((const f32x4*)(z + o + e));
+      const f32x4 zz = __builtin_nontemporal_load((const f32x4*)(z + b * z_ld + (int64_t)col * E + e));
 #pragma unroll
       for (int x = 0; x < 4; ++x) acc[e + x] = acc[e + x] * silu_f32(zz[x]);
     }
@@ -146,7 +148,7 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
 
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s,
-                         const float* z, bool persistent) {
+                         const float* z, bool persistent, int64_t z_ld) {
   if (n_bags == 0) return hipSuccess;
   // persistent: two blocks per CU loop over the bags, leaving room on every CU for kernels
   // running beside the gather; otherwise one block per group of bags (on its own the
@@ -161,6 +163,7 @@ hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, 
   const int64_t max_blocks = persistent ? cu_blocks : ((int64_t)1 << 31) - 1;
   const int eb = dtype == DT_BF16 ? 2 : 4;
   const int row_vecs = (int)((int64_t)dim * eb / 16);
+  if (z_ld == 0) z_ld = dim;
   const int tpr = row_vecs < 256 ? row_vecs : 256;
   const int bpb = 256 / tpr;
   const int threads = bpb * tpr;
@@ -172,7 +175,7 @@ hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, 
   const bool uniform = (tpr % 64) == 0;
 #define PKM_GATHER(EBV, UNI, GT)                                                                              \
   gather_kernel<EBV, 16, UNI, GT><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, \
-                                                           w, n_bags, bag, y, y_f32, z)
+                                                           w, n_bags, bag, y, y_f32, z, z_ld)
   if (z) {
     if (eb == 2) {
       if (uniform) PKM_GATHER(2, true, true); else PKM_GATHER(2, false, true);

@@ -12,10 +12,14 @@
 namespace pkm {
 
 struct Layout {
+  // With the Memory+ gate, W1^T follows W_q^T in one [H d_q + d_v, d_model] matrix and one
+  // GEMM computes x [W_q | W1] into the rows of q: columns [0, H d_q) are the query,
+  // [H d_q, H d_q + d_v) are z = x W1 (qz_cols columns per token).
   size_t wqT = 0, khat = 0, w1T = 0, w2T = 0;        // create-time copies
+  int64_t qz_cols = 0;
   size_t q = 0, qhat = 0, hidx = 0, hsc = 0;          // per-forward intermediates
   size_t gmax = 0, theta = 0, cand = 0, count = 0;    // selection scratch
-  size_t idx = 0, sc = 0, w = 0, z = 0, g = 0;
+  size_t idx = 0, sc = 0, w = 0, g = 0;
   size_t total = 0;
 };
 
@@ -60,13 +64,12 @@ inline Layout make_layout(const pkm_config* c) {
     off = align256(off + bytes);
     return o;
   };
-  L.wqT = take(H * dq * dm * eb);
+  L.qz_cols = (int64_t)(H * dq + (c->memory_plus ? dv : 0));
+  L.wqT = take((size_t)L.qz_cols * dm * eb);
+  if (c->memory_plus) L.w1T = L.wqT + H * dq * dm * eb;
   L.khat = take(H * 2 * n * (dq / 2) * eb);
-  if (c->memory_plus) {
-    L.w1T = take(dv * dm * eb);
-    L.w2T = take(dm * dv * eb);
-  }
-  L.q = take(T * H * dq * 4);
+  if (c->memory_plus) L.w2T = take(dm * dv * eb);
+  L.q = take(T * (size_t)L.qz_cols * 4);
   L.qhat = take(T * H * dq * eb);
   L.gmax = take(T * H * 2 * 128 * 4);   // MAX_GROUPS group maxima per row
   L.theta = take(T * H * 2 * 4);
@@ -77,10 +80,7 @@ inline Layout make_layout(const pkm_config* c) {
   L.idx = take(T * H * k * 4);
   L.sc = take(T * H * k * 4);
   L.w = take(T * H * k * 4);
-  if (c->memory_plus) {
-    L.z = take(T * dv * 4);    // x W1 (fp32), read by the gather's fused gate
-    L.g = take(T * dv * eb);   // y * silu(x W1), the input of the W2 product
-  }
+  if (c->memory_plus) L.g = take(T * dv * eb);   // y * silu(x W1), the input of the W2 product
   L.total = off;
   return L;
 }

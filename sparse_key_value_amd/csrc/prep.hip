@@ -53,43 +53,76 @@ template <>
 __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
 // One wave per row of `width` elements: out = norm ? v / sqrt(mean(v^2) + eps) : v.
-// Input element type TI (fp32 accumulator or stored dtype), output type TO.
-template <typename TI, typename TO>
+// Input element type TI (fp32 accumulator or stored dtype), output type TO.  Row r is
+// element (r % per_tok) of token r / per_tok: it starts at (r / per_tok) * in_ld +
+// (r % per_tok) * width in the input (in_ld elements per token) and at r * width in the
+// output.  VEC: fp32 input read four elements (16 bytes) per lane at a time.
+template <typename TI, typename TO, bool VEC>
 __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in, TO* __restrict__ out,
-                                                      int64_t rows, int width, int norm, float eps) {
+                                                      int64_t rows, int width, int per_tok, int64_t in_ld, int norm,
+                                                      float eps) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
-  const TI* src = in + row * width;
+  const TI* src = in + (row / per_tok) * in_ld + (row % per_tok) * (int64_t)width;
   TO* dst = out + row * width;
   float scale = 1.0f;
-  if (norm) {
+  if constexpr (VEC) {
+    // width is a multiple of 256: every lane holds width / 256 groups of four
+    constexpr int MAXV = 4;  // width <= 1024
+    f32x4 v[MAXV];
+    const int nv = width / 256;
     float ss = 0.f;
-    for (int i = lane; i < width; i += 64) {
-      float v = load_elem<TI>(src, i);
-      ss += v * v;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      if (i < nv) {
+        v[i] = *(const f32x4*)((const float*)src + i * 256 + lane * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += v[i][e] * v[i][e];
+      }
     }
-    ss = wave_sum_f32(ss);
-    scale = 1.0f / __fsqrt_rn(ss / (float)width + eps);
+    if (norm) {
+      ss = wave_sum_f32(ss);
+      scale = 1.0f / __fsqrt_rn(ss / (float)width + eps);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i < nv)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_elem<TO>(dst, i * 256 + lane * 4 + e, v[i][e] * scale);
+  } else {
+    if (norm) {
+      float ss = 0.f;
+      for (int i = lane; i < width; i += 64) {
+        float v = load_elem<TI>(src, i);
+        ss += v * v;
+      }
+      ss = wave_sum_f32(ss);
+      scale = 1.0f / __fsqrt_rn(ss / (float)width + eps);
+    }
+    for (int i = lane; i < width; i += 64) store_elem<TO>(dst, i, load_elem<TI>(src, i) * scale);
   }
-  for (int i = lane; i < width; i += 64) store_elem<TO>(dst, i, load_elem<TI>(src, i) * scale);
 }
 
 hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtype, int64_t rows, int width,
-                          int norm, float eps, hipStream_t s) {
+                          int norm, float eps, hipStream_t s, int per_tok, int64_t in_ld) {
   if (rows == 0) return hipSuccess;
+  if (in_ld == 0) in_ld = (int64_t)per_tok * width;
   dim3 grid((unsigned)((rows + 3) / 4));
+  const bool vec = in_is_f32 && width % 256 == 0 && width <= 1024 && in_ld % 4 == 0 && ((uintptr_t)in & 15) == 0;
+#define PKM_RN(TI, TO, V) \
+  rownorm_kernel<TI, TO, V><<<grid, 256, 0, s>>>((const TI*)in, (TO*)out, rows, width, per_tok, in_ld, norm, eps)
   if (in_is_f32) {
-    if (out_dtype == DT_BF16)
-      rownorm_kernel<float, uint16_t><<<grid, 256, 0, s>>>((const float*)in, (uint16_t*)out, rows, width, norm, eps);
-    else
-      rownorm_kernel<float, float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, rows, width, norm, eps);
+    if (out_dtype == DT_BF16) {
+      if (vec) PKM_RN(float, uint16_t, true); else PKM_RN(float, uint16_t, false);
+    } else {
+      if (vec) PKM_RN(float, float, true); else PKM_RN(float, float, false);
+    }
   } else {
-    if (out_dtype == DT_BF16)
-      rownorm_kernel<uint16_t, uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, (uint16_t*)out, rows, width, norm, eps);
-    else
-      rownorm_kernel<uint16_t, float><<<grid, 256, 0, s>>>((const uint16_t*)in, (float*)out, rows, width, norm, eps);
+    if (out_dtype == DT_BF16) PKM_RN(uint16_t, uint16_t, false);
+    else PKM_RN(uint16_t, float, false);
   }
+#undef PKM_RN
   return hipGetLastError();
 }
 
