@@ -375,6 +375,43 @@ def bench_engram_host(a):
     print(json.dumps(res), flush=True)
 
 
+def backward_cpu_baseline(a, cfg, wl, idx, w, dy):
+    """The oracle's backward step (dw, ds, the per-row sums and the SGD update of the touched
+    rows) on the first n tokens of the workload, taken as a batch of their own, on the host
+    cores.  The rows it reads are fetched from the device beforehand (not timed)."""
+    import numpy as np
+    import torch
+
+    from oracle import backward as B
+    from oracle import pkm as O
+    from tests.gpu_util import to_host
+
+    bag = cfg.H * cfg.k
+    idx_h = idx.cpu().numpy().astype(np.int64)
+    w_h = w.cpu().numpy().astype(np.float64)
+    dy_h = dy.cpu().numpy().astype(np.float64)
+
+    def step(n):
+        ii = idx_h[:n]
+        uniq = np.unique(ii[(ii >= 0) & (ii < cfg.N)])
+        stored = to_host(wl.values[torch.from_numpy(uniq).cuda()])
+        table = O.to_f64(stored, cfg.dtype)
+        rows_of = lambda r: table[np.searchsorted(uniq, r)]
+        t1 = time.perf_counter()
+        dw = B.grad_weights(rows_of, ii, dy_h[:n], cfg.N)
+        B.softmax_backward(w_h[:n], dw, cfg.k)
+        rows, grad = B.grad_rows(ii, w_h[:n], dy_h[:n], cfg.N)
+        B.sgd_rows(stored[np.searchsorted(uniq, rows)], grad, 1e-4, cfg.dtype)
+        return time.perf_counter() - t1
+
+    per_tok = step(16) / 16
+    n = int(max(16, min(cfg.T, a.cpu_seconds / max(per_tok, 1e-9))))
+    dt = step(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens ({n * bag} entries) of {cfg.name} as a batch of their own: "
+                      f"float64 NumPy oracle dw, ds, per-row sums (Python loop) and SGD step, {dt:.1f} s"}
+
+
 def bench_backward(a):
     """The sparse training step of the value table behind the forward's gather, as one
     pkm_bag_backward call: dw and the softmax ds for every token, the distinct rows and the
@@ -446,7 +483,7 @@ def bench_backward(a):
         "dw_alone": {"kernel": "bag_dw_kernel (dw + ds, no update)", "ms": dw_ms, "algorithmic_bytes": dw_bytes,
                      "GBps": dw_bytes / (dw_ms * 1e-3) / 1e9,
                      "frac_hbm": dw_bytes / (dw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-        "cpu_baseline": None,
+        "cpu_baseline": None if a.no_cpu_baseline else backward_cpu_baseline(a, cfg, wl, idx, w, dy),
     }
     print(json.dumps(res), flush=True)
 
