@@ -186,6 +186,35 @@ def test_fused_step_shapes(dt, dim):
                                   np.asarray(host[untouched]).view(np.uint8))
 
 
+@pytest.mark.parametrize("dt,dim,n_bags,H,k", [("bf16", 2048, 3, 2, 5), ("f32", 96, 5, 2, 5), ("f32", 1536, 4, 3, 3),
+                                             ("bf16", 64, 1, 1, 1)])
+def test_fused_step_ragged_bags(dt, dim, n_bags, H, k):
+    """Bags whose length is not a multiple of the update kernel's batch of rows in flight
+    (8, or 4 with two slices per lane): 10, 9 and 1 entries; one bag alone."""
+    from tests.gpu_util import to_dev, to_host
+    rng = np.random.default_rng(dim + 7 * H + k)
+    n_rows = 40
+    bag = H * k
+    idx = rng.integers(-1, n_rows + 1, size=(n_bags, bag))
+    idx[0, 0] = idx[-1, -1] = 7                                     # a shared row across bags (or a lone entry)
+    s_ = rng.standard_normal((n_bags, H, k))
+    w = np.exp(s_ - s_.max(-1, keepdims=True))
+    w = (w / w.sum(-1, keepdims=True)).reshape(n_bags, bag).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(17, np.arange(n_rows), dim, dt)
+    table = to_dev(host, dt)
+    lr = 0.5
+    say(f"bag fused step ragged {dt} dim {dim} bags {n_bags}x{bag}")
+    got = _run(table, n_rows, dim, dt, idx, w, dy, k, update=True, lr=lr)
+    rows_of = lambda r: O.to_f64(host[np.asarray(r)], dt)
+    _check(got, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), k)
+    after = to_host(table)
+    _one_ulp(after[got["rows"]], O.to_f64(host[got["rows"]], dt) - lr * got["grad"].astype(np.float64), dt)
+    untouched = np.setdiff1d(np.arange(n_rows), got["rows"])
+    np.testing.assert_array_equal(np.asarray(after[untouched]).view(np.uint8),
+                                  np.asarray(host[untouched]).view(np.uint8))
+
+
 def test_deterministic():
     from tests.gpu_util import to_dev
     rng = np.random.default_rng(1)
