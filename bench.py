@@ -124,7 +124,7 @@ def cpu_baseline(wl, cfg, target_s, max_tokens=None):
     n = int(max(16, min(max_tokens or wl.T, target_s / max(per_tok, 1e-9))))
     log(f"oracle: {per_tok * 1e3:.1f} ms/token estimated, timing {n} tokens")
     dt = run(n)
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(), **numeric_stack(),
             "sample": f"first {n} of {wl.T} tokens of {cfg.name}, float64 NumPy oracle, {dt:.1f} s" + note}
 
 
@@ -151,6 +151,20 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def numeric_stack():
+    """NumPy version and the BLAS library it calls (name, version), for the CPU baseline."""
+    import numpy as np
+    info = {"numpy": np.__version__}
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:
+        pass
+    return info
 
 
 def blas_threads():
@@ -789,6 +803,8 @@ def main():
     cpu = None
     if not a.no_cpu_baseline and not host:
         cpu = cpu_baseline(wl, cfg, a.cpu_seconds)
+        # the oracle's rate in the gather's algorithmic bytes (the same bytes per token)
+        cpu["gather_GBps_equivalent"] = cpu["value"] * alg_b / T / 1e9
 
     # the committed counters were taken at the headline workload with device-resident tables
     traffic = counter_traffic() if (not host and cfg.name == "memplus_16m_bf16") else None
