@@ -28,6 +28,9 @@
 //             4,096 per row.
 //    A lane's count may exceed its CAND / 2 slots (structured data); that row is then
 //    scored exhaustively by the overflow kernel before the combine kernel reads it.
+//  * With fewer than 2k groups (few sub-keys for the k asked for) the bound prunes little
+//    and most rows would overflow: every row is then scored exhaustively, one wave per
+//    row, instead of the two passes.
 //  * Keys are 64-bit (ordered score << 32 | ~index): ties resolve to the lower index
 //    and every key is distinct.
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
@@ -379,11 +382,67 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
   }
 }
 
+// The exact top-k of one row (t, h, c) by exhaustive scoring in plain fp32 FMAs (d in
+// ascending order): each lane keeps the best 32 keys of its share of the sub-keys in
+// registers, the 64 lane lists are merged by k rounds of a wave-wide maximum, and the
+// row's candidate list becomes exactly its top-k (count k in the first lane half, 0 in
+// the second).  qs: this wave's LDS row of DH floats.
+template <typename DT, int DH>
+__device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t r2, int H, int n,
+                               int k, uint64_t* __restrict__ cand, int32_t* __restrict__ count, float* qs, int lane) {
+  constexpr int VE = 16 / (int)sizeof(DT);  // elements per 16-byte load
+  const int pair = (int)(r2 % (2 * H));
+  const DT* q = qhat + r2 * DH;
+  for (int d = lane; d < DH; d += 64) qs[d] = load_elem_f32(q, d);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  uint64_t L[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) L[j] = 0ull;
+  const DT* kb = khat + (size_t)pair * n * DH;
+  for (int i = lane; i < n; i += 64) {
+    const u32x4* kr = (const u32x4*)(kb + (size_t)i * DH);
+    float s = 0.f;
+#pragma unroll 4
+    for (int v = 0; v < DH / VE; ++v) {
+      const u32x4 x = kr[v];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float kv;
+        if constexpr (sizeof(DT) == 2) kv = (e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1]);
+        else kv = __uint_as_float(x[e]);
+        s = __builtin_fmaf(qs[v * VE + e], kv, s);
+      }
+    }
+    uint64_t key = make_key(s, (uint32_t)i);
+    if (key > L[31]) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint64_t lo = key > L[j] ? L[j] : key;
+        L[j] = key > L[j] ? key : L[j];
+        key = lo;
+      }
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    const uint64_t win = wave_max_u64(L[0]);
+    if (L[0] == win) {
+#pragma unroll
+      for (int i = 0; i < 31; ++i) L[i] = L[i + 1];
+      L[31] = 0ull;
+    }
+    if (lane == 0) cand[r2 * CAND + j] = win;
+  }
+  if (lane == 0) {
+    count[2 * r2] = k;
+    count[2 * r2 + 1] = 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Rows whose candidates overflowed (more than CAND / 2 in either lane's half: structured
-// data with many sub-keys above the bound) are scored again here, exhaustively, in plain fp32 FMAs: each lane keeps the
-// best 32 keys of its share of the sub-keys in registers, the 64 lane lists are merged
-// by k rounds of a wave-wide maximum, and the row's candidate list becomes exactly its
-// top-k.  A persistent grid scans the counts; with no overflow it only reads them.
+// data with many sub-keys above the bound) are scored again exhaustively.  A persistent
+// grid scans the counts; with no overflow it only reads them.
 template <typename DT, int DH>
 __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
@@ -397,44 +456,22 @@ __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qh
     while (over) {
       const int64_t r2 = base + __builtin_ctzll(over);
       over &= over - 1;
-      const int pair = (int)(r2 % (2 * H));
-      const DT* q = qhat + r2 * DH;
-      for (int d = lane; d < DH; d += 64) qs[wv][d] = load_elem_f32(q, d);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      uint64_t L[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) L[j] = 0ull;
-      const DT* kb = khat + (size_t)pair * n * DH;
-      for (int i = lane; i < n; i += 64) {
-        float s = 0.f;
-        for (int d = 0; d < DH; ++d) s = __builtin_fmaf(qs[wv][d], load_elem_f32(kb + (size_t)i * DH, d), s);
-        uint64_t key = make_key(s, (uint32_t)i);
-        if (key > L[31]) {
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const uint64_t lo = key > L[j] ? L[j] : key;
-            L[j] = key > L[j] ? key : L[j];
-            key = lo;
-          }
-        }
-      }
-      for (int j = 0; j < k; ++j) {
-        const uint64_t win = wave_max_u64(L[0]);
-        if (L[0] == win) {
-#pragma unroll
-          for (int i = 0; i < 31; ++i) L[i] = L[i + 1];
-          L[31] = 0ull;
-        }
-        if (lane == 0) cand[r2 * CAND + j] = win;
-      }
-      if (lane == 0) {
-        count[2 * r2] = k;
-        count[2 * r2 + 1] = 0;
-      }
-      __builtin_amdgcn_wave_barrier();
+      exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
     }
   }
+}
+
+// Few sub-keys per row (fewer than 2k groups, so the group-maximum bound prunes little and
+// most rows would overflow): every row exhaustively, one wave per row.
+template <typename DT, int DH>
+__global__ void __launch_bounds__(256) direct_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+                                                     int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
+                                                     int32_t* __restrict__ count) {
+  __shared__ float qs[4][DH];
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r2 = (int64_t)blockIdx.x * 4 + wv;
+  if (r2 >= rows2) return;
+  exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
 }
 
 template <typename DT, int DH>
@@ -445,7 +482,13 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   int gshift = 0;
   while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
   const int ngroups = (n + (8 << gshift) - 1) >> (3 + gshift);
+  const int64_t rows = T * H * 2;
   hipError_t e;
+  if (ngroups < 2 * k) {
+    direct_kernel<DT, DH><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n,
+                                                                         k, cand, count);
+    return hipGetLastError();
+  }
 #define PKM_P1(G) pass1_kernel<DT, DH, G><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
   switch (gshift) {
     case 0: PKM_P1(0); break;
@@ -458,7 +501,6 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   }
 #undef PKM_P1
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t rows = T * H * 2;
   theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   pass2_kernel<DT, DH><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
