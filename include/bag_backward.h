@@ -22,7 +22,8 @@
  *
  * Conventions as in pkm.h (caller-owned DEVICE pointers unless stated, row-major,
  * `stream` a hipStream_t as void*, nothing allocated, PKM_OK or a negative code with
- * the reason in pkm_last_error()).
+ * the reason in pkm_last_error()).  Not for HIP graph capture: the sort enqueues
+ * buffer fills.
  */
 #ifndef BAG_BACKWARD_H
 #define BAG_BACKWARD_H

@@ -28,8 +28,9 @@
  *
  * Conventions (as in pkm.h): tensor pointers are caller-owned DEVICE pointers,
  * row-major; `stream` is a hipStream_t as void* (NULL = default stream); the calls
- * only enqueue work, allocate nothing and never wait for the GPU; the return is
- * PKM_OK or a negative PKM_E* code with the reason in pkm_last_error().
+ * only enqueue work, allocate nothing and never wait for the GPU (engram_forward can
+ * be captured in a HIP graph); the return is PKM_OK or a negative PKM_E* code with the
+ * reason in pkm_last_error().
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H

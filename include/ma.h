@@ -10,8 +10,9 @@
  *    EmbeddingBag) and one elementwise add: V = K + E_bar[s].
  *
  * Conventions as in pkm.h: caller-owned DEVICE pointers, row-major; `stream` is a
- * hipStream_t as void*; the calls only enqueue work and allocate nothing; the return
- * is PKM_OK or a negative PKM_E* code with the reason in pkm_last_error().
+ * hipStream_t as void*; the calls only enqueue work and allocate nothing (ma_values
+ * can be captured in a HIP graph); the return is PKM_OK or a negative PKM_E* code with
+ * the reason in pkm_last_error().
  */
 #ifndef MA_H
 #define MA_H

@@ -34,7 +34,9 @@
  *    (typically PyTorch tensors) and must stay valid while in use.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work and returns without waiting for the GPU;
- *    the forward allocates nothing and performs no host sync.  Its results are
+ *    the forward allocates nothing and performs no host sync, so a forward
+ *    (default single-stream mode, GEMM plans made by an earlier call of the same
+ *    shape) can be captured in a HIP graph and replayed.  Its results are
  *    ordered on `stream`: work enqueued on `stream` afterwards sees them.
  *  - A handle belongs to the device that is current at pkm_create.
  *  - Return value: PKM_OK (0) or a negative PKM_E* code; on error, the message

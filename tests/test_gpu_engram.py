@@ -248,3 +248,43 @@ def test_engram_prefetch_refuses_pageable_host_memory():
     with pytest.raises(P.PkmError) as ex:
         P.engram_prefetch(L.ecfg, pageable, L.ids, L.T, cfg.seq_len, None, L.mult, st)
     assert ex.value.code == P.PKM_EINVAL and "pinned" in str(ex.value)
+
+
+def test_lookup_in_a_hip_graph():
+    """engram_forward allocates nothing and never waits on the host: captured in a HIP graph,
+    every replay equals the eager lookup bitwise, also after the captured ids change."""
+    from tests.gpu_util import TORCH_DT
+    cfg = C.ENGRAM_CONFIGS["engram_compress_bf16"]
+    say("engram lookup in a HIP graph")
+    L = Lookup(cfg, seed=5)
+    ids0 = L.ids.clone()
+    ids1 = torch.from_numpy(S.make_engram_inputs(cfg, 6)["ids"][:L.T].copy()).cuda()
+
+    def run(out, e, a):
+        L.P.engram_forward(L.ecfg, L.tables, L.ids, L.T, cfg.seq_len, L.compress, L.mult, L.h, out, e, a)
+
+    def bufs():
+        return (torch.empty((L.T, cfg.d), dtype=TORCH_DT[cfg.dtype], device="cuda"),
+                torch.empty((L.T, cfg.d), dtype=torch.float32, device="cuda"),
+                torch.empty((L.T,), dtype=torch.float32, device="cuda"))
+
+    want = {}
+    for name, ids in (("0", ids0), ("1", ids1)):
+        L.ids.copy_(ids)
+        b = bufs()
+        run(*b)
+        torch.cuda.synchronize()
+        want[name] = [t.clone() for t in b]
+    g_bufs = bufs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(*g_bufs)
+    for rep, name in enumerate(("0", "1", "0")):
+        L.ids.copy_(ids0 if name == "0" else ids1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(g_bufs, want[name]):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager lookup"
+        run(*bufs())
+        torch.cuda.synchronize()

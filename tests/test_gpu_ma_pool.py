@@ -169,3 +169,39 @@ def test_host_resident_value_table():
                             1, 1, y)
     hwl.close()
     dev.close()
+
+
+def test_values_in_a_hip_graph():
+    """ma_values allocates nothing and never waits on the host: captured in a HIP graph, every
+    replay equals the eager call bitwise, also after the captured ids change."""
+    import sparse_key_value_amd as P
+    from tests.gpu_util import TORCH_DT, to_dev
+    cfg = C.MA_CONFIGS["ma_tiny_f32"]
+    say("memory attention values in a HIP graph")
+    d = S.make_ma_inputs(cfg, 9)
+    T = len(d["ids"])
+    E = to_dev(d["E"], cfg.dtype)
+    gain = torch.from_numpy(d["gain"]).cuda() if d["gain"] is not None else None
+    P.ma_fold_table(E, cfg.vocab, cfg.d_v, cfg.n_heads, gain, cfg.norm_eps, cfg.dtype, E)
+    ids = torch.from_numpy(d["ids"]).cuda()
+    ids_other = torch.flip(ids, [0]).contiguous()
+    K = to_dev(d["K"], cfg.dtype)
+    V = torch.empty((T, cfg.d_v), dtype=TORCH_DT[cfg.dtype], device="cuda")
+    want = []
+    for src in (ids.clone(), ids_other):
+        out = torch.empty_like(V)
+        P.ma_values(E, cfg.vocab, cfg.d_v, cfg.dtype, src, T, K, out)
+        torch.cuda.synchronize()
+        want.append(out)
+    captured_ids = ids.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        P.ma_values(E, cfg.vocab, cfg.d_v, cfg.dtype, captured_ids, T, K, V)
+    for rep, which in enumerate((0, 1, 0)):
+        captured_ids.copy_(ids if which == 0 else ids_other)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(V, want[which]), f"replay {rep} differs from the eager call"
+        P.ma_values(E, cfg.vocab, cfg.d_v, cfg.dtype, ids_other, T, K, torch.empty_like(V))
+        torch.cuda.synchronize()
