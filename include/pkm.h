@@ -190,6 +190,13 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
 int pkm_enable_stage_timing(pkm_handle* h, int32_t max_records);
 int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n);
 
+/* Which stages the following forwards record: bit s (1u << PKM_STAGE_*) set records
+ * stage s; the default records all of them.  Every event pair costs the forward a
+ * few microseconds, so a run that times whole forwards can keep only the stages it
+ * needs.  A stage left out of a recorded forward reads as NaN in pkm_stage_times.
+ * Returns PKM_EINVAL for bits at or above PKM_NUM_STAGES. */
+int pkm_set_stage_timing_mask(pkm_handle* h, uint32_t mask);
+
 /* Number of token chunks pkm_forward pipelines a batch over: 0 (the default) or
  * 1 runs every stage on the caller's stream in order; 2..8 that many chunks. */
 int pkm_set_pipeline_chunks(pkm_handle* h, int32_t chunks);

@@ -70,6 +70,7 @@ _sig = {
     "pkm_embedding_bag": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp]),
     "pkm_enable_stage_timing": (ctypes.c_int, [_vp, _i32]),
     "pkm_stage_times": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_float), _i32]),
+    "pkm_set_stage_timing_mask": (ctypes.c_int, [_vp, ctypes.c_uint32]),
     "pkm_set_pipeline_chunks": (ctypes.c_int, [_vp, _i32]),
     "pkm_destroy": (ctypes.c_int, [_vp]),
     "pkm_last_error": (ctypes.c_char_p, []),
@@ -170,6 +171,14 @@ def pkm_embedding_bag(table, n_rows: int, dim: int, dtype, idx, w, n_bags: int, 
 
 def pkm_enable_stage_timing(h: int, max_records: int) -> None:
     _check(_lib.pkm_enable_stage_timing(h, max_records), "pkm_enable_stage_timing")
+
+
+def pkm_set_stage_timing_mask(h: int, stages) -> None:
+    """Record only these stages (names from STAGES or ids) in the following forwards."""
+    mask = 0
+    for st in stages:
+        mask |= 1 << (STAGE_ID[st] if isinstance(st, str) else int(st))
+    _check(_lib.pkm_set_stage_timing_mask(h, mask), "pkm_set_stage_timing_mask")
 
 
 def pkm_stage_times(h: int, stage, n: int) -> list[float]:

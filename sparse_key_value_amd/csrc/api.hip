@@ -95,6 +95,8 @@ struct pkm_handle {
   // stage timing: max_rec records, each with (begin, end) events per stage and chunk plus
   // the whole forward
   int max_rec = 0, next = 0, count = 0;
+  uint32_t stage_mask = 0xFFu;  // bit s: stage s is recorded (bit PKM_STAGE_TOTAL: the whole forward)
+  std::vector<uint32_t> rec_mask;  // the mask each record was taken with
   std::vector<hipEvent_t> ev;
   std::vector<int> rec_chunks;
 
@@ -111,6 +113,7 @@ void destroy_timing(pkm_handle* h) {
     if (e) (void)hipEventDestroy(e);
   h->ev.clear();
   h->rec_chunks.clear();
+  h->rec_mask.clear();
   h->max_rec = h->next = h->count = 0;
 }
 
@@ -146,15 +149,18 @@ struct Timer {
   pkm_handle* h;
   int slot;
   Timer(pkm_handle* h_, int nch) : h(h_), slot(h_->max_rec ? h_->next : -1) {
-    if (slot >= 0) h->rec_chunks[slot] = nch;
+    if (slot >= 0) {
+      h->rec_chunks[slot] = nch;
+      h->rec_mask[slot] = h->stage_mask;
+    }
   }
   hipEvent_t* base() const { return &h->ev[(size_t)slot * EV_PER_REC]; }
   hipError_t stage(int st, int chunk, int end, hipStream_t s) {
-    if (slot < 0) return hipSuccess;
+    if (slot < 0 || !((h->rec_mask[slot] >> st) & 1u)) return hipSuccess;
     return hipEventRecord(base()[(st * MAX_CHUNKS + chunk) * 2 + end], s);
   }
   hipError_t total(int end, hipStream_t s) {
-    if (slot < 0) return hipSuccess;
+    if (slot < 0 || !((h->rec_mask[slot] >> PKM_STAGE_TOTAL) & 1u)) return hipSuccess;
     return hipEventRecord(base()[7 * MAX_CHUNKS * 2 + end], s);
   }
   void commit() {
@@ -491,6 +497,7 @@ int pkm_enable_stage_timing(pkm_handle* h, int32_t max_records) {
   if (max_records == 0) return PKM_OK;
   h->ev.assign((size_t)max_records * EV_PER_REC, nullptr);
   h->rec_chunks.assign(max_records, 0);
+  h->rec_mask.assign(max_records, 0u);
   for (hipEvent_t& e : h->ev) {
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) {
@@ -514,7 +521,9 @@ int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n) {
     const int slot = (first + skip + i) % h->max_rec;
     hipEvent_t* e = &h->ev[(size_t)slot * EV_PER_REC];
     float sum = 0.f;
-    if (stage == PKM_STAGE_TOTAL) {
+    if (!((h->rec_mask[slot] >> stage) & 1u)) {
+      sum = __builtin_nanf("");  // not recorded in this forward
+    } else if (stage == PKM_STAGE_TOTAL) {
       PKM_HIP(hipEventSynchronize(e[7 * MAX_CHUNKS * 2 + 1]));
       PKM_HIP(hipEventElapsedTime(&sum, e[7 * MAX_CHUNKS * 2], e[7 * MAX_CHUNKS * 2 + 1]));
     } else if (gated || (stage != PKM_STAGE_GATE1 && stage != PKM_STAGE_GATE2)) {
@@ -529,6 +538,13 @@ int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n) {
     ms[i] = sum;
   }
   return have;
+}
+
+int pkm_set_stage_timing_mask(pkm_handle* h, uint32_t mask) {
+  if (!h) return fail(PKM_EINVAL, "handle is NULL");
+  if (mask >> PKM_NUM_STAGES) return fail(PKM_EINVAL, "mask has bits above stage %d", PKM_NUM_STAGES - 1);
+  h->stage_mask = mask;
+  return PKM_OK;
 }
 
 int pkm_set_pipeline_chunks(pkm_handle* h, int32_t chunks) {

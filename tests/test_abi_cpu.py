@@ -107,6 +107,7 @@ def test_other_entry_points_reject_bad_arguments(P):
     assert lib.pkm_select(None, 256, 4, None, None, None, None, None, None) == P.PKM_EINVAL
     assert lib.pkm_destroy(None) == P.PKM_EINVAL
     assert lib.pkm_enable_stage_timing(None, 4) == P.PKM_EINVAL
+    assert lib.pkm_set_stage_timing_mask(None, 1) == P.PKM_EINVAL
     assert lib.pkm_copy_normalized_subkeys(None, 256, None) == P.PKM_EINVAL
     eb = lib.pkm_embedding_bag
     assert eb(256, 10, 12, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL   # 12 bf16 = 24 bytes per row
