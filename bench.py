@@ -34,6 +34,9 @@ HOST_LINK_PEAK_GBPS = 64.0    # PCIe 5.0 x16 host link, one direction, published
 METRIC = "PKM fwd tokens/s + value-gather GB/s (% of HBM peak) at 16M keys, 1 MI355X"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gather_memplus_16m_bf16_counters.json")
 ENGRAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "engram_zipf_2m_bf16_counters.json")
+# committed counter runs of the forward's gather, per workload (device-resident tables)
+GATHER_COUNTERS = {"memplus_16m_bf16": COUNTERS_FILE,
+                   "memplus_64m_bf16": os.path.join(ROOT, "profiles", "gather_memplus_64m_bf16_counters.json")}
 
 
 def log(msg):
@@ -815,8 +818,8 @@ def main():
         # the oracle's rate in the gather's algorithmic bytes (the same bytes per token)
         cpu["gather_GBps_equivalent"] = cpu["value"] * alg_b / T / 1e9
 
-    # the committed counters were taken at the headline workload with device-resident tables
-    traffic = counter_traffic() if (not host and cfg.name == "memplus_16m_bf16") else None
+    # the committed counters were taken with device-resident tables
+    traffic = counter_traffic(GATHER_COUNTERS[cfg.name]) if (not host and cfg.name in GATHER_COUNTERS) else None
     res = {
         "metric": METRIC,
         "value": tok_s,
