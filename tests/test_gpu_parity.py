@@ -224,6 +224,9 @@ def test_pkm_1m_bf16_stagewise_ragged():
     dict(name="k1", n_sub=64, k=1, H=2, d_q=128, d_model=64, d_v=64, T=70),
     dict(name="d_h128_gate", n_sub=200, k=32, H=2, d_q=256, d_model=256, d_v=128, T=131, memory_plus=True),
     dict(name="n33_k32", n_sub=33, k=32, H=1, d_q=128, d_model=64, d_v=64, T=64),
+    dict(name="n1_k1", n_sub=1, k=1, H=2, d_q=128, d_model=64, d_v=64, T=17),        # one key: N = 1
+    dict(name="n32_k32", n_sub=32, k=32, H=1, d_q=128, d_model=64, d_v=64, T=40),    # k = n_sub
+    dict(name="h64", n_sub=64, k=4, H=64, d_q=128, d_model=64, d_v=64, T=33),        # the most heads
 ])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_edge_shapes(case, dt):
