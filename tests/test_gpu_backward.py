@@ -309,3 +309,25 @@ def test_full_size_sampled():
     np.testing.assert_array_equal(np.asarray(got_u).view(np.uint8),
                                   np.asarray(wl.host_rows(untouched)).view(np.uint8))
     wl.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_one_row_table(dt):
+    """n_rows = 1: every in-range entry hits the same row (one owner walks them all) and the
+    sort works on one-bit keys; indices -1 and 1 read nothing."""
+    from tests.gpu_util import to_dev, to_host
+    rng = np.random.default_rng(31)
+    n_rows, dim, n_bags, bag = 1, 64, 7, 6
+    idx = rng.integers(-1, 2, size=(n_bags, bag))
+    idx[0, 0] = 0
+    w = rng.random((n_bags, bag)).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(19, np.arange(n_rows), dim, dt)
+    table = to_dev(host, dt)
+    lr = 0.25
+    say(f"bag backward one-row table {dt}")
+    got = _run(table, n_rows, dim, dt, idx, w, dy, 3, update=True, lr=lr)
+    rows_of = lambda r: O.to_f64(host[np.asarray(r)], dt)
+    _check(got, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), 3)
+    np.testing.assert_array_equal(got["rows"], [0])
+    _one_ulp(to_host(table)[[0]], O.to_f64(host[[0]], dt) - lr * got["grad"].astype(np.float64), dt)
