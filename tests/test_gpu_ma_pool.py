@@ -115,9 +115,11 @@ def test_shared_pool_three_layers_over_one_table():
     before = torch.cuda.memory_allocated()
     first = G.Workload(cfg, seed=0, T=T)
     table_bytes = first.values.numel() * first.values.element_size()
+    storage_bytes = first.values.untyped_storage().nbytes()   # with any alignment padding
     layers = [first] + [G.Workload(cfg, seed=s, T=T, values=first.values, value_seed=0) for s in (1, 2)]
     grown = torch.cuda.memory_allocated() - before
-    assert grown < 1.5 * table_bytes, "each layer must borrow the pool, not copy it"
+    # two more copies would add 2 x table_bytes; the handles' own workspaces are far smaller
+    assert grown < storage_bytes + 0.5 * table_bytes, "each layer must borrow the pool, not copy it"
     for i, wl in enumerate(layers):
         say(f"shared pool layer {i}")
         assert wl.values.data_ptr() == first.values.data_ptr()
