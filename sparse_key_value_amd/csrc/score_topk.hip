@@ -12,9 +12,10 @@
 //    v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32), computing
 //    S^T = Khat * Qhat^T so that each lane's 16 accumulators belong to ONE token.  A wave
 //    owns 64 tokens (two 32-token MFMA columns), so every 16-byte LDS operand read feeds
-//    two MFMAs.  A block is 4 waves = 256 tokens of one (h, c); 32-sub-key chunks are
-//    staged through a double-buffered, XOR-swizzled LDS tile shared by the 4 waves, the
-//    next chunk being prefetched into registers.  Nothing else lives in LDS.
+//    two MFMAs.  A block is 4 or 8 waves = 256 or 512 tokens of one (h, c); 32-sub-key
+//    chunks reach a double-buffered, XOR-swizzled LDS tile shared by the block's waves by
+//    direct buffer->LDS loads, the next chunk's while the current one is scored.  Pass 2
+//    also keeps a small per-lane row of scores in LDS for its appends.
 //  * The scores are never written out; selection takes two passes:
 //      pass 1 writes, per row, the maximum score of every group of G consecutive
 //             sub-keys (G in {8, 16, 32, 64, ...}, the smallest giving <= 128 groups);
@@ -43,8 +44,6 @@ namespace pkm {
 namespace {
 
 constexpr int TPW = 64;         // tokens per wave (two MFMA columns of 32)
-constexpr int NWAVES = 4;
-constexpr int TPB = TPW * NWAVES;
 constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
 
 template <typename DT, int DH>
@@ -87,10 +86,19 @@ __device__ __forceinline__ float load_elem_f32(const uint16_t* p, size_t i) { re
 
 __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_base + 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-// The shared MFMA sweep over all sub-keys of one pair for the block's 256 tokens.
+// The shared MFMA sweep over all sub-keys of one pair for the block's NW * 64 tokens.
 // `on_tile(ch, acc)` receives, per 32-sub-key chunk, the scores of this lane's two
 // tokens (acc[0]: token lane%32 of the wave, acc[1]: token 32 + lane%32).
-template <typename DT, int DH, typename F>
+//
+// NW = 4: one wave per SIMD per block, two blocks per CU.  Both blocks start together and
+// do the same work, so their two waves on a SIMD run in step: both issue MFMAs, then both
+// run the selection on the VALU, then both wait at the barrier, and the matrix core idles
+// through the second half.  NW = 8: one block of 8 waves per CU, waves w and w + 4 sharing
+// a SIMD; the second group takes each chunk's scores one chunk late (its selection of
+// chunk ch - 1 runs right after the barrier, beside the first group's MFMAs of chunk ch,
+// and its MFMAs of chunk ch beside the first group's selection), which keeps the matrix
+// core fed through both halves.  The accumulators live across the barrier for that.
+template <typename DT, int DH, int NW, typename F>
 __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t T, int H, int n,
                                       uint8_t* ks, F&& on_tile) {
   using M = Mma<DT, DH>;
@@ -106,7 +114,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   typename M::frag qf[2][M::NK];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
     const DT* qrow = qhat + ((t * H + h) * 2 + c) * (int64_t)DH;
 #pragma unroll
     for (int kk = 0; kk < M::NK; ++kk) qf[g][kk] = t < T ? M::load_q(qrow, kk, hi) : typename M::frag{};
@@ -118,8 +126,15 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   // the 64 consecutive 16-byte units starting at unit (wv * DPW + i) * 64, and each lane
   // fetches the global unit that belongs at its LDS unit under the XOR swizzle.  Rows past
   // n_sub load row 0 instead (in bounds); their scores are masked by every consumer.
-  constexpr int DPW = CHUNK * U16 / 64 / NWAVES;  // loads per wave per chunk
-  static_assert(DPW >= 1 && CHUNK * U16 % (64 * NWAVES) == 0, "chunk must split evenly over the waves");
+  // The loads are buffer loads (a descriptor over this pair's n_sub * RB bytes) rather than
+  // global ones: the compiler counts a global load into LDS as both a memory and an LDS
+  // access, and then waits for every LDS read in flight (lgkmcnt(0)) before each MFMA
+  // operand instead of only the one it needs, which exposed the LDS latency four times
+  // per chunk.
+  constexpr int DPW = CHUNK * U16 / 64 / NW;  // loads per wave per chunk
+  static_assert(DPW >= 1 && CHUNK * U16 % (64 * NW) == 0, "chunk must split evenly over the waves");
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, n * RB, 0x00020000);  // raw, 32-bit dwords
   auto fetch = [&](int ch, int buf) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
@@ -131,13 +146,16 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
       // bytes) keeps one VGPR per address; 64-bit per-lane addresses made pass 2 spill
       // them, and every reload from scratch waited for all loads in flight
       const uint32_t off = (uint32_t)sub * RB + (uint32_t)col * 16;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kbase + off),
-          (void __attribute__((address_space(3)))*)(ks + buf * CHUNK * RB + (wv * DPW + i) * 64 * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krsrc, (void __attribute__((address_space(3)))*)(ks + buf * CHUNK * RB + (wv * DPW + i) * 64 * 16), 16, off,
+          0, 0, 0);
     }
   };
   const int swz = (lane & 31) % U16;
 
+  // the lagging group (wave-uniform)
+  const bool lag = NW == 8 && wv >= 4;
+  f32x16 acc[2];
   fetch(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
   __syncthreads();
@@ -145,8 +163,10 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
     const int buf = ch & 1;
     // the other buffer was last read in the previous chunk, before the barrier that ended it
     if (ch + 1 < nch) fetch(ch + 1, buf ^ 1);
+    if (lag && ch > 0) on_tile(ch - 1, (const f32x16*)acc);
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
     if constexpr (M::EB == 2) {
       // bf16: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling groups
       // below keep the compiler from pulling the reads back next to their use (it
@@ -176,10 +196,11 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
         acc[1] = M::mma(a, qf[1][kk], acc[1]);
       }
     }
-    on_tile(ch, acc);
+    if (!lag) on_tile(ch, (const f32x16*)acc);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+  if (lag) on_tile(nch - 1, (const f32x16*)acc);
 }
 
 // Max over the 16 scores of one lane, or only over those of sub-keys < n.
@@ -192,10 +213,12 @@ __device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, 
 }
 
 // Pass 1: per row, the maximum of every group of G = 8 << GS sub-keys.  The maxima of
-// 8 consecutive groups are collected in registers (a shift register) and written as
-// two 16-byte stores, so that few stores are in flight when a chunk waits for its loads.
-template <typename DT, int DH, int GS>
-__global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+// NB consecutive groups are collected in registers (a shift register) and written as
+// 16-byte stores, so that few stores are in flight when a chunk waits for its loads
+// (NB = 4 with 8-wave blocks, whose lagging group holds its accumulators across the
+// barrier: 8 spilled there).
+template <typename DT, int DH, int GS, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, float* __restrict__ gmax) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
@@ -206,18 +229,19 @@ __global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qh
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
+  constexpr int NB = NW == 8 ? 4 : 8;
   float run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float buf[2][8];
+  float buf[2][NB];
   int nbuf = 0;  // groups in buf (wave-uniform)
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) buf[g][j] = 0.f;
+    for (int j = 0; j < NB; ++j) buf[g][j] = 0.f;
   float* gm[2];
   bool live[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
     live[g] = hi == 0 && t < T;
     gm[g] = gmax + ((t * H + h) * 2 + c) * (int64_t)MAX_GROUPS;
   }
@@ -226,23 +250,23 @@ __global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qh
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
-      for (int j = 0; j < 7; ++j) buf[g][j] = buf[g][j + 1];
-      buf[g][7] = m[g];
+      for (int j = 0; j < NB - 1; ++j) buf[g][j] = buf[g][j + 1];
+      buf[g][NB - 1] = m[g];
     }
-    // shift register: the newest is buf[7]; after 8 pushes buf[0] is the oldest
-    if (++nbuf == 8) {
-      // reorder: oldest first at gm[done]
+    // shift register: the newest is buf[NB - 1]; after NB pushes buf[0] is the oldest
+    if (++nbuf == NB) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         if (!live[g]) continue;
-        *(f32x4*)(gm[g] + done) = f32x4{buf[g][0], buf[g][1], buf[g][2], buf[g][3]};
-        *(f32x4*)(gm[g] + done + 4) = f32x4{buf[g][4], buf[g][5], buf[g][6], buf[g][7]};
+#pragma unroll
+        for (int j = 0; j < NB; j += 4)
+          *(f32x4*)(gm[g] + done + j) = f32x4{buf[g][j], buf[g][j + 1], buf[g][j + 2], buf[g][j + 3]};
       }
-      done += 8;
+      done += NB;
       nbuf = 0;
     }
   };
-  sweep<DT, DH>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     float mg[2][GPC];
 #pragma unroll
@@ -273,13 +297,13 @@ __global__ void __launch_bounds__(256, 2) pass1_kernel(const DT* __restrict__ qh
       }
     }
   });
-  // the last < 8 groups: buf[8 - nbuf .. 7] hold groups done .. done + nbuf - 1
+  // the last < NB groups: buf[NB - nbuf .. NB - 1] hold groups done .. done + nbuf - 1
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     if (!live[g]) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nbuf) gm[g][done + i] = buf[g][8 - nbuf + i];
+    for (int i = 0; i < NB; ++i)
+      if (i < nbuf) gm[g][done + i] = buf[g][NB - nbuf + i];
   }
 }
 
@@ -309,15 +333,18 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
 
 // Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
 // theta).  Each of a token's two lanes owns half of the row's CAND slots and counts its
-// own candidates, so the common case (no survivor) costs one compare per score and a
-// skipped branch.
-template <typename DT, int DH>
-__global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
+// own candidates.
+template <typename DT, int DH, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, int k, const float* __restrict__ theta,
                                                        uint64_t* __restrict__ cand, int32_t* __restrict__ count) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int HALF = CAND / 2;
+  // SROW floats per lane: the lane's 32 scores of the chunk, read back by position for the
+  // appends (36, not 32: 16-byte stores of 16 consecutive lanes then hit distinct banks)
+  constexpr int SROW = 36;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
   const int pairs = 2 * H;
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
@@ -329,7 +356,7 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
   int64_t row[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
     row[g] = (t * H + h) * 2 + c;
     thr[g] = t < T ? theta[row[g]] : __builtin_inff();
     dst[g] = cand + row[g] * CAND + hi * HALF;
@@ -339,45 +366,65 @@ __global__ void __launch_bounds__(256, 2) pass2_kernel(const DT* __restrict__ qh
   float thz[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
-  sweep<DT, DH>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  float* my = stage + (wv * 64 + lane) * SROW;
+  sweep<DT, DH, NW>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
+    // bit 16 g + r: score r of token fragment g reaches the bound.  The sign bits of the
+    // differences are shifted in with v_alignbit: two VALU ops per score and no lane
+    // masks (a compare and select per score costs twice that, with a wait state after
+    // every compare).
+    uint32_t m = 0;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      // bit r: score r reaches the bound.  The sign bits of the differences are shifted in
-      // with v_alignbit: two VALU ops per score and no lane masks (a compare and select
-      // per score costs twice that, with a wait state after every compare).  The appends
-      // then loop over the set bits only, so the wave runs as many append rounds as its
-      // busiest lane has candidates in this chunk (usually 0-2).
       uint32_t miss = 0;
 #pragma unroll
       for (int r = 15; r >= 0; --r) miss = __builtin_amdgcn_alignbit(miss, __float_as_uint(acc[g][r] - thz[g]), 31);
-      uint32_t m = ~miss & 0xFFFFu;
-      if (!full) {  // the last chunk: only sub-keys < n exist
-        const int nv = n - ch * CHUNK;
-        uint32_t valid = 0;
+      m |= (~miss & 0xFFFFu) << (16 * g);
+    }
+    if (!full) {  // the last chunk: only sub-keys < n exist
+      const int nv = n - ch * CHUNK;
+      uint32_t valid = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) valid |= (8 * (r >> 2) + 4 * hi + (r & 3) < nv ? 1u : 0u) << r;
-        m &= valid;
+      for (int r = 0; r < 16; ++r) valid |= (8 * (r >> 2) + 4 * hi + (r & 3) < nv ? 1u : 0u) << r;
+      m &= valid * 0x10001u;
+    }
+    // the appends loop over the set bits only (both fragments in one loop), so the wave
+    // runs as many rounds as its busiest lane has candidates in this chunk; a hit's score
+    // comes back from the lane's own LDS row (a select over 16 registers by a per-lane
+    // position cost 30 VALU ops per round)
+    if (m) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(f32x4*)(my + 16 * g + 4 * j) = f32x4{acc[g][4 * j], acc[g][4 * j + 1], acc[g][4 * j + 2], acc[g][4 * j + 3]};
+    }
+    while (m) {
+      const int b = __builtin_ctz(m);  // fragment 0 first, ascending positions: the order of a scan
+      m &= m - 1;
+      const int g = b >> 4, r = b & 15;
+      const float s = my[b];
+      const int sub = sub_of(ch * CHUNK, r, hi);
+      int cn = g ? cnt[1] : cnt[0];
+      int e = g ? eq[1] : eq[0];
+      bool take = true;
+      if (s == (g ? thr[1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
+      if (take) {
+        if (cn < HALF) (g ? dst[1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
+        ++cn;
       }
-      while (m) {
-        const int r = __builtin_ctz(m);  // ascending positions: the same order as a scan
-        m &= m - 1;
-        float s = acc[g][0];
-#pragma unroll
-        for (int q = 1; q < 16; ++q) s = r == q ? acc[g][q] : s;
-        const int sub = sub_of(ch * CHUNK, r, hi);
-        bool take = true;
-        if (s == thr[g]) take = eq[g]++ < k;  // exact ties with the bound: the first k suffice
-        if (take) {
-          if (cnt[g] < HALF) dst[g][cnt[g]] = make_key(s, (uint32_t)sub);
-          ++cnt[g];
-        }
+      if (g) {
+        cnt[1] = cn;
+        eq[1] = e;
+      } else {
+        cnt[0] = cn;
+        eq[0] = e;
       }
     }
   });
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * TPB + wv * TPW + g * 32 + (lane & 31);
+    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
     if (t < T) count[row[g] * 2 + hi] = cnt[g];
   }
 }
@@ -474,10 +521,10 @@ __global__ void __launch_bounds__(256) direct_kernel(const DT* __restrict__ qhat
   exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
 }
 
-template <typename DT, int DH>
-hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax, float* theta,
-                         uint64_t* cand, int32_t* count, hipStream_t s) {
-  const int64_t tiles = (T + TPB - 1) / TPB;
+template <typename DT, int DH, int NW>
+hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax,
+                            float* theta, uint64_t* cand, int32_t* count, hipStream_t s) {
+  const int64_t tiles = (T + TPW * NW - 1) / (TPW * NW);
   const dim3 grid((unsigned)(tiles * 2 * H));
   int gshift = 0;
   while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
@@ -489,7 +536,7 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
                                                                          k, cand, count);
     return hipGetLastError();
   }
-#define PKM_P1(G) pass1_kernel<DT, DH, G><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
+#define PKM_P1(G) pass1_kernel<DT, DH, G, NW><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
   switch (gshift) {
     case 0: PKM_P1(0); break;
     case 1: PKM_P1(1); break;
@@ -503,12 +550,35 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   if ((e = hipGetLastError()) != hipSuccess) return e;
   theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  pass2_kernel<DT, DH><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
+  pass2_kernel<DT, DH, NW><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t scan_waves = (rows + 63) / 64;
   const int64_t ob = (scan_waves + 3) / 4 < 1024 ? (scan_waves + 3) / 4 : 1024;
   overflow_kernel<DT, DH><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand, count);
   return hipGetLastError();
+}
+
+// 8-wave blocks where a chunk splits evenly over 8 waves and the batch gives every CU one
+// block of them; else 4-wave blocks (twice the blocks for small batches).
+template <typename DT, int DH>
+constexpr bool eight_waves_built() {
+  return (CHUNK * DH * (int)sizeof(DT) / 16) % (64 * 8) == 0;
+}
+
+template <typename DT, int DH>
+hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax, float* theta,
+                         uint64_t* cand, int32_t* count, hipStream_t s) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cus = c;
+  }
+  if constexpr (eight_waves_built<DT, DH>()) {
+    if ((T + 511) / 512 * 2 * H >= cus) return launch_passes_nw<DT, DH, 8>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+  }
+  return launch_passes_nw<DT, DH, 4>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
 }
 
 }  // namespace

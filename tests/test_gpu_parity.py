@@ -254,6 +254,15 @@ def test_edge_shapes(case, dt):
     # 256-wide sub-keys (the 16M-key kernels) with a partial last chunk of sub-keys
     dict(name="dh256_partial_chunk", dtype="bf16", qk_norm=True, n_sub=77, k=8, H=2, d_q=512, d_model=128, d_v=64,
          T=70),
+    # batches that give every CU an 8-wave scoring block (512 tokens x one (head, half) each),
+    # with a ragged last block and a partial last chunk of sub-keys: 256-, 128- and 64-wide
+    # sub-keys
+    dict(name="eight_waves_dh256", dtype="bf16", qk_norm=True, n_sub=140, k=8, H=64, d_q=512, d_model=64, d_v=64,
+         T=600),
+    dict(name="eight_waves_dh128", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=300, k=16, H=16, d_q=256,
+         d_model=128, d_v=128, T=3700),
+    dict(name="eight_waves_f32_dh64", dtype="f32", qk_norm=False, n_sub=200, k=8, H=32, d_q=128, d_model=64, d_v=64,
+         T=1600),
 ])
 def test_flag_combinations(case):
     case = dict(case)
