@@ -274,11 +274,13 @@ def test_flag_combinations(case):
     wl.close()
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_exact_ties_resolve_to_lowest_index(dt):
+@pytest.mark.parametrize("dt,H,T", [("f32", 2, 100), ("bf16", 2, 100),
+                                    # 64 heads x 520 tokens: 8-wave scoring blocks with a ragged last block
+                                    ("bf16", 64, 520)])
+def test_exact_ties_resolve_to_lowest_index(dt, H, T):
     """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}", dtype=dt, n_sub=96, k=16, H=2, d_q=128, d_model=64,
-                                        d_v=64, T=100, qk_norm=True)
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=96, k=16, H=H, d_q=128, d_model=64,
+                                        d_v=64, T=T, qk_norm=True)
     inp = S.make_inputs(cfg, seed=4)
     sk = inp["subkeys"].copy()
     sk[:, :, 1::2] = sk[:, :, 0::2]      # sub-key 2i+1 duplicates 2i in every codebook
@@ -286,7 +288,7 @@ def test_exact_ties_resolve_to_lowest_index(dt):
     x = inp["x"].copy()
     x[::5] = 0                          # every fifth token is all zero: every score is 0
     inp["x"] = x
-    say(f"ties {dt}")
+    say(f"ties {dt} H={H} T={T}")
     wl = _G().Workload(cfg, seed=4, host_inputs=inp)
     o = run_debug(wl)
     full_check(wl, o)
@@ -464,6 +466,44 @@ def test_candidate_overflow_takes_exhaustive_path():
     np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"])
     np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"])
     np.testing.assert_allclose(sc.cpu().numpy(), sel["score"], rtol=0, atol=0)
+    pk.close()
+
+
+def test_candidate_overflow_in_eight_wave_blocks():
+    """The overflow case above in every (token, head) of a batch that takes the 8-wave scoring
+    blocks (64 heads x 600 tokens): each (token, head) gets one of the three queries, so its
+    lists must equal the oracle's for that query exactly."""
+    import sparse_key_value_amd as P
+    n, dh, k, H, T = 2048, 64, 32, 64, 600
+    K1 = np.zeros((2, n, dh), dtype=np.float32)
+    K1[0, :, 0] = np.arange(n, dtype=np.float32)
+    K1[1, :, 1] = np.arange(n, dtype=np.float32)[::-1] * 0.5
+    K = np.ascontiguousarray(np.broadcast_to(K1, (H, 2, n, dh)))
+    pats = np.zeros((3, 2, dh), dtype=np.float32)
+    pats[:, 0, 0] = [1.0, 2.0, 0.5]
+    pats[:, 1, 1] = [1.0, 1.0, 3.0]
+    which = (np.arange(T)[:, None] + np.arange(H)[None, :]) % 3            # [T, H]
+    q = np.ascontiguousarray(pats[which])                                  # [T, H, 2, dh]
+    say(f"overflow in 8-wave blocks: T={T} H={H}")
+    wq = torch.zeros((64, H * 2 * dh), dtype=torch.float32, device="cuda")
+    vals = torch.zeros((n * n, 4), dtype=torch.float32, device="cuda")
+    pk = P.ProductKeyMemory(d_model=64, n_heads=H, d_query=2 * dh, n_sub=n, k=k, d_value=4, dtype="f32", qk_norm=0,
+                            memory_plus=0, max_tokens=T, W_q=wq, subkeys=torch.from_numpy(K).cuda(), values=vals)
+    hi_ = torch.empty((T, H, 2, k), dtype=torch.int32, device="cuda")
+    hs_ = torch.empty((T, H, 2, k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, H, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, H, k), dtype=torch.float32, device="cuda")
+    w = torch.empty((T, H, k), dtype=torch.float32, device="cuda")
+    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), T, hi_, hs_, idx, sc, w)
+    torch.cuda.synchronize()
+    q64 = pats.astype(np.float64).reshape(3, 1, 2 * dh)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K1[None, 0].astype(np.float64), K1[None, 1].astype(np.float64), k)
+    got_hi, got_idx, got_sc = hi_.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    for p in range(3):
+        m = which == p
+        np.testing.assert_array_equal(got_hi[m], np.broadcast_to(sel["half_idx"][p, 0], got_hi[m].shape))
+        np.testing.assert_array_equal(got_idx[m], np.broadcast_to(sel["idx"][p, 0], got_idx[m].shape))
+        np.testing.assert_array_equal(got_sc[m], np.broadcast_to(sel["score"][p, 0].astype(np.float32), got_sc[m].shape))
     pk.close()
 
 
