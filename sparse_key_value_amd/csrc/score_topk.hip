@@ -19,9 +19,9 @@
 //  * The scores are never written out; selection takes two passes:
 //      pass 1 writes, per row, the maximum score of every group of G consecutive
 //             sub-keys (G in {8, 16, 32, 64, ...}, the smallest giving <= 128 groups);
-//      theta  picks per row the k-th largest group maximum: at least k sub-keys reach
-//             it, so it bounds the row's k-th best score from below (found bit by bit
-//             with wave ballots);
+//      theta  picks per row the k-th largest group maximum, rounded down to its top 16
+//             bits: at least k sub-keys reach it, so it bounds the row's k-th best score
+//             from below (found bit by bit with wave ballots);
 //      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring
 //             above the bound, and of those scoring exactly the bound the first k each
 //             lane sees (lowest indices first), as 64-bit keys to the row's candidate
@@ -307,7 +307,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   }
 }
 
-// theta: per row the k-th largest of its group maxima (-inf if there are fewer than k).
+// theta: per row a lower bound of the k-th largest of its group maxima (-inf if there are
+// fewer than k).  Any value at or below that k-th largest bounds the row's k-th score from
+// below, so the descent stops after the top THETA_BITS bits of the ordered key (sign,
+// exponent and 7 mantissa bits: within 2^-7 of the k-th group maximum, which adds about one
+// candidate per row) and takes the prefix with zero low bits.  The kernel is bound by the
+// scalar unit (popcounts, adds and compares per bit), so half the bits is half the time.
+// Keys strictly above a bound that is below the k-th group maximum already number at least
+// k, so pass 2's cap on keys equal to the bound drops none that matter.
+constexpr int THETA_BITS = 16;
 __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gmax, int64_t rows, int ngroups, int k,
                                                     float* __restrict__ theta) {
   const int lane = threadIdx.x & 63;
@@ -320,10 +328,10 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
   const float* gm = gmax + row * MAX_GROUPS;
   const uint32_t v0 = lane < ngroups ? ord_score(gm[lane]) : 0u;
   const uint32_t v1 = lane + 64 < ngroups ? ord_score(gm[lane + 64]) : 0u;
-  // largest x with #{v >= x} >= k, bit by bit from the top
+  // largest x (low 32 - THETA_BITS bits zero) with #{v >= x} >= k, bit by bit from the top
   uint32_t prefix = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= 32 - THETA_BITS; --bit) {
     const uint32_t cand = prefix | (1u << bit);
     const int cnt = __popcll(__ballot(v0 >= cand)) + __popcll(__ballot(v1 >= cand));
     if (cnt >= k) prefix = cand;
