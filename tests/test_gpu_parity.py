@@ -254,15 +254,6 @@ def test_edge_shapes(case, dt):
     # 256-wide sub-keys (the 16M-key kernels) with a partial last chunk of sub-keys
     dict(name="dh256_partial_chunk", dtype="bf16", qk_norm=True, n_sub=77, k=8, H=2, d_q=512, d_model=128, d_v=64,
          T=70),
-    # batches that give every CU an 8-wave scoring block (512 tokens x one (head, half) each),
-    # with a ragged last block and a partial last chunk of sub-keys: 256-, 128- and 64-wide
-    # sub-keys
-    dict(name="eight_waves_dh256", dtype="bf16", qk_norm=True, n_sub=140, k=8, H=64, d_q=512, d_model=64, d_v=64,
-         T=600),
-    dict(name="eight_waves_dh128", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=300, k=16, H=16, d_q=256,
-         d_model=128, d_v=128, T=3700),
-    dict(name="eight_waves_f32_dh64", dtype="f32", qk_norm=False, n_sub=200, k=8, H=32, d_q=128, d_model=64, d_v=64,
-         T=1600),
 ])
 def test_flag_combinations(case):
     case = dict(case)
@@ -274,12 +265,42 @@ def test_flag_combinations(case):
     wl.close()
 
 
-@pytest.mark.parametrize("dt,H,T", [("f32", 2, 100), ("bf16", 2, 100),
-                                    # 64 heads x 520 tokens: 8-wave scoring blocks with a ragged last block
-                                    ("bf16", 64, 520)])
-def test_exact_ties_resolve_to_lowest_index(dt, H, T):
+def _sample_tokens(T, n=96, tail=24):
+    """About n evenly spread tokens plus the last `tail` (the ragged last block)."""
+    return np.unique(np.concatenate([np.linspace(0, T - 1, n).astype(np.int64), np.arange(max(0, T - tail), T)]))
+
+
+@pytest.mark.parametrize("case", [
+    # batches that give every CU an 8-wave scoring block (512 tokens x one (head, half) each;
+    # more than 1,024 sub-keys), with a ragged last block and a partial last chunk of
+    # sub-keys: 256-, 128- and 64-wide sub-keys.  The GPU runs every token; the oracle
+    # checks a spread of tokens over both wave groups and the end of the last block.
+    dict(name="eight_waves_dh256", dtype="bf16", qk_norm=True, n_sub=1100, k=8, H=64, d_q=512, d_model=64, d_v=64,
+         T=600),
+    dict(name="eight_waves_dh128", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=1030, k=16, H=16, d_q=256,
+         d_model=128, d_v=128, T=3700),
+    dict(name="eight_waves_f32_dh64", dtype="f32", qk_norm=False, n_sub=1050, k=8, H=32, d_q=128, d_model=64, d_v=64,
+         T=1600),
+])
+def test_eight_wave_scoring_blocks(case):
+    case = dict(case)
+    name = case.pop("name")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=name, memory_plus=case.pop("memory_plus", False), **case)
+    say(f"8-wave scoring {cfg.name}")
+    wl = _G().Workload(cfg, seed=7)
+    o = run_debug(wl)
+    T = cfg.T
+    full_check(wl, o, rows=_sample_tokens(T))
+    wl.close()
+
+
+@pytest.mark.parametrize("dt,H,T,n_sub", [("f32", 2, 100, 96), ("bf16", 2, 100, 96),
+                                          # 64 heads x 520 tokens over 1,040 sub-keys: 8-wave scoring
+                                          # blocks with a ragged last block
+                                          ("bf16", 64, 520, 1040)])
+def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub):
     """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=96, k=16, H=H, d_q=128, d_model=64,
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=n_sub, k=16, H=H, d_q=128, d_model=64,
                                         d_v=64, T=T, qk_norm=True)
     inp = S.make_inputs(cfg, seed=4)
     sk = inp["subkeys"].copy()
@@ -291,7 +312,9 @@ def test_exact_ties_resolve_to_lowest_index(dt, H, T):
     say(f"ties {dt} H={H} T={T}")
     wl = _G().Workload(cfg, seed=4, host_inputs=inp)
     o = run_debug(wl)
-    full_check(wl, o)
+    # the oracle on every token of the small cases, on a spread (every fifth token, the zero
+    # ones, included) of the 64-head one
+    full_check(wl, o, rows=None if H < 64 else np.unique(np.concatenate([_sample_tokens(T), np.arange(0, T, 5)])))
     # zero tokens: per-half lists are 0..k-1 and the final list is cells (0, 0..k-1)
     z = np.arange(0, cfg.T, 5)
     assert (o["half_idx"][z] == np.arange(cfg.k)).all()
