@@ -552,7 +552,8 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
     case 3: PKM_P1(3); break;
     case 4: PKM_P1(4); break;
     case 5: PKM_P1(5); break;
-    default: return hipErrorInvalidValue;  // n_sub > 8192 * 4: not built
+    case 6: PKM_P1(6); break;   // groups of 512: every n_sub with n_sub^2 < 2^31
+    default: return hipErrorInvalidValue;  // n_sub > 128 * 512: rejected at create
   }
 #undef PKM_P1
   if ((e = hipGetLastError()) != hipSuccess) return e;

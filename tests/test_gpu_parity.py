@@ -530,6 +530,36 @@ def test_candidate_overflow_in_eight_wave_blocks():
     pk.close()
 
 
+def test_largest_sub_key_lists():
+    """n_sub = 40,000 (the table would have 1.6e9 rows, near the int32 limit of the flat
+    index): group maxima over 512 sub-keys, the largest group size built.  The selection
+    (pkm_select) against the oracle's exhaustive per-half sort, exactly, since the scores
+    are small multiples of 1/64."""
+    import sparse_key_value_amd as P
+    n, dh, k, T = 40000, 64, 32, 40
+    rng = np.random.default_rng(11)
+    K = (rng.integers(-64, 65, size=(1, 2, n, dh)) / 64.0).astype(np.float32)
+    q = (rng.integers(-8, 9, size=(T, 1, 2, dh)) / 8.0).astype(np.float32)
+    say(f"largest sub-key lists: n_sub={n}")
+    wq = torch.zeros((64, 2 * dh), dtype=torch.float32, device="cuda")
+    vals = torch.zeros((16, 4), dtype=torch.float32, device="cuda")   # never read by pkm_select
+    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=2 * dh, n_sub=n, k=k, d_value=4, dtype="f32", qk_norm=0,
+                            memory_plus=0, max_tokens=T, W_q=wq, subkeys=torch.from_numpy(K).cuda(), values=vals)
+    hi_ = torch.empty((T, 1, 2, k), dtype=torch.int32, device="cuda")
+    hs_ = torch.empty((T, 1, 2, k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, 1, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+    w = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), T, hi_, hs_, idx, sc, w)
+    torch.cuda.synchronize()
+    q64 = q.astype(np.float64).reshape(T, 1, 2 * dh)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64), k)
+    np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"])
+    np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"])
+    np.testing.assert_array_equal(sc.cpu().numpy(), sel["score"].astype(np.float32))
+    pk.close()
+
+
 def test_forward_in_a_hip_graph():
     """The forward allocates nothing and never waits on the host, so it can be captured in a
     HIP graph: every replay equals the eager forward bitwise, also after the captured input
