@@ -30,6 +30,7 @@ namespace {
 
 struct Stair {
   uint16_t pos[128];  // (i << 8) | j for staircase slot s, 0xFFFF = empty
+  uint8_t first_off[32];  // row a's first column off the staircase: floor(k / (a + 1))
 };
 
 // Sort 128 keys held two per lane (element e = 2 * lane + slot) in descending order.
@@ -144,7 +145,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   const float kth_score = key_score(kth);
   bool beaten = false;
   if (lane < k) {
-    const int b0 = k / (lane + 1);
+    const int b0 = st.first_off[lane];  // a table: a per-lane integer division costs ~20 VALU ops
     if (b0 < k) beaten = key_score(L0[lane]) + key_score(L1[b0]) >= kth_score;
   }
   uint64_t mine;  // lane j < k ends up with the j-th best key
@@ -197,6 +198,7 @@ hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T,
   for (int a = 0; a < k; ++a)
     for (int b = 0; (a + 1) * (b + 1) <= k; ++b) st.pos[m++] = (uint16_t)((a << 8) | b);
   for (; m < 128; ++m) st.pos[m] = 0xFFFF;
+  for (int a = 0; a < 32; ++a) st.first_off[a] = (uint8_t)(a < k ? k / (a + 1) : 0);
   combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(cand, count, rows, n, k, st, half_idx, half_score,
                                                                   idx, score, w);
   return hipGetLastError();
