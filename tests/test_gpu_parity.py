@@ -281,6 +281,8 @@ def _sample_tokens(T, n=96, tail=24):
          d_model=128, d_v=128, T=3700),
     dict(name="eight_waves_f32_dh64", dtype="f32", qk_norm=False, n_sub=1050, k=8, H=32, d_q=128, d_model=64, d_v=64,
          T=1600),
+    dict(name="eight_waves_f32_dh128", dtype="f32", qk_norm=True, memory_plus=True, n_sub=1100, k=32, H=32, d_q=256,
+         d_model=64, d_v=64, T=1600),
 ])
 def test_eight_wave_scoring_blocks(case):
     case = dict(case)
