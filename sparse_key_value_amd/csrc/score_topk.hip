@@ -45,6 +45,9 @@ namespace {
 
 constexpr int TPW = 64;         // tokens per wave (two MFMA columns of 32)
 constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
+// chunks loaded per barrier: 8-wave blocks (one per CU, LDS to spare) take two chunks
+// between barriers, which halves the barriers and the skew every one of them absorbs
+constexpr int chunks_per_barrier(int nw) { return nw == 8 ? 2 : 1; }
 
 template <typename DT, int DH>
 struct Mma;
@@ -153,16 +156,25 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   };
   const int swz = (lane & 31) % U16;
 
+  // SC chunks per barrier: chunk ch lives in LDS buffer ch % (2 SC); the SC chunks after a
+  // barrier are loaded into the other SC buffers while they are scored
+  constexpr int SC = chunks_per_barrier(NW);
   // the lagging group (wave-uniform)
   const bool lag = NW == 8 && wv >= 4;
   f32x16 acc[2];
-  fetch(0, 0);
+#pragma unroll
+  for (int j = 0; j < SC; ++j)
+    if (j < nch) fetch(j, j);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
   __syncthreads();
   for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    // the other buffer was last read in the previous chunk, before the barrier that ended it
-    if (ch + 1 < nch) fetch(ch + 1, buf ^ 1);
+    const int buf = ch % (2 * SC);
+    // the other SC buffers were last read before the barrier that ended the previous group
+    if (ch % SC == 0) {
+#pragma unroll
+      for (int j = 0; j < SC; ++j)
+        if (ch + SC + j < nch) fetch(ch + SC + j, (ch + SC + j) % (2 * SC));
+    }
     if (lag && ch > 0) on_tile(ch - 1, (const f32x16*)acc);
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
     acc[0] = f32x16{};
@@ -197,8 +209,10 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
       }
     }
     if (!lag) on_tile(ch, (const f32x16*)acc);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+    if (ch % SC == SC - 1 || ch + 1 == nch) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
   }
   if (lag) on_tile(nch - 1, (const f32x16*)acc);
 }
@@ -223,7 +237,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
   constexpr int SPAN = GS <= 2 ? 1 : (1 << (GS - 2)); // chunks per group when a group spans chunks
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   const int pairs = 2 * H;
   const int pair = blockIdx.x % pairs;
   const int64_t tile = blockIdx.x / pairs;
@@ -351,7 +365,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   // SROW floats per lane: the lane's 32 scores of the chunk, read back by position for the
   // appends (36, not 32: 16-byte stores of 16 consecutive lanes then hit distinct banks)
   constexpr int SROW = 36;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
   const int pairs = 2 * H;
   const int pair = blockIdx.x % pairs;
