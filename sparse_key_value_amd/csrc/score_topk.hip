@@ -581,11 +581,8 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   return hipGetLastError();
 }
 
-// 8-wave blocks where a chunk splits evenly over 8 waves, the batch gives every CU one
-// block of them and groups span at least 16 sub-keys; else 4-wave blocks (twice the blocks
-// for small batches).  With groups of 8 (n_sub <= 1,024) the 8-wave pass 1 keeps four
-// group maxima per chunk in flight and spills a register; measured, it is then no faster
-// than the 4-wave one (at 32,768 tokens, 1,024 sub-keys: 480-497 against 470-475 us).
+// 8-wave blocks where a chunk splits evenly over 8 waves and the batch gives every CU one
+// block of them; else 4-wave blocks (twice the blocks for small batches).
 template <typename DT, int DH>
 constexpr bool eight_waves_built() {
   return (CHUNK * DH * (int)sizeof(DT) / 16) % (64 * 8) == 0;
@@ -602,7 +599,7 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
     cus = c;
   }
   if constexpr (eight_waves_built<DT, DH>()) {
-    if ((T + 511) / 512 * 2 * H >= cus && n > 8 * MAX_GROUPS)
+    if ((T + 511) / 512 * 2 * H >= cus)
       return launch_passes_nw<DT, DH, 8>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
   }
   return launch_passes_nw<DT, DH, 4>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);

@@ -271,8 +271,8 @@ def _sample_tokens(T, n=96, tail=24):
 
 
 @pytest.mark.parametrize("case", [
-    # batches that give every CU an 8-wave scoring block (512 tokens x one (head, half) each;
-    # more than 1,024 sub-keys), with a ragged last block and a partial last chunk of
+    # batches that give every CU an 8-wave scoring block (512 tokens x one (head, half) each),
+    # with a ragged last block and a partial last chunk of
     # sub-keys: 256-, 128- and 64-wide sub-keys.  The GPU runs every token; the oracle
     # checks a spread of tokens over both wave groups and the end of the last block.
     dict(name="eight_waves_dh256", dtype="bf16", qk_norm=True, n_sub=1100, k=8, H=64, d_q=512, d_model=64, d_v=64,
@@ -283,6 +283,9 @@ def _sample_tokens(T, n=96, tail=24):
          T=1600),
     dict(name="eight_waves_f32_dh128", dtype="f32", qk_norm=True, memory_plus=True, n_sub=1100, k=32, H=32, d_q=256,
          d_model=64, d_v=64, T=1600),
+    # groups of 8 sub-keys (four group maxima per chunk) in 8-wave blocks
+    dict(name="eight_waves_groups_of_8", dtype="bf16", qk_norm=True, n_sub=700, k=16, H=64, d_q=512, d_model=64,
+         d_v=64, T=700),
 ])
 def test_eight_wave_scoring_blocks(case):
     case = dict(case)
