@@ -198,8 +198,11 @@ int run_select(pkm_handle* h, const void* qhat, int64_t T, const SelScratch& sx,
   return PKM_OK;
 }
 
-// Selection (a1-a6) for tokens [t0, t0 + tc) on stream sa.
-int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream_t sa, Timer& tm, int chunk) {
+// Selection (a1-a6) for tokens [t0, t0 + tc) on stream sa.  The per-half lists are
+// written only when `halves` (a debug forward that asks for them): the forward itself needs
+// only the final lists.
+int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream_t sa, Timer& tm, int chunk,
+                 bool halves) {
   const pkm_config& c = h->cfg;
   const pkm::Layout& L = h->L;
   const int H = c.n_heads, dq = c.d_query, k = c.k;
@@ -219,8 +222,9 @@ int chunk_select(pkm_handle* h, const void* x, int64_t t0, int64_t tc, hipStream
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, chunk, 1, sa));
   // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
   const size_t sel = (size_t)t0 * H * k;
-  int rc = run_select(h, qhat, tc, scratch_at(h, t0), h->at<int32_t>(L.hidx) + 2 * sel, h->at<float>(L.hsc) + 2 * sel,
-                      h->at<int32_t>(L.idx) + sel, h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
+  int rc = run_select(h, qhat, tc, scratch_at(h, t0), halves ? h->at<int32_t>(L.hidx) + 2 * sel : nullptr,
+                      halves ? h->at<float>(L.hsc) + 2 * sel : nullptr, h->at<int32_t>(L.idx) + sel,
+                      h->at<float>(L.sc) + sel, h->at<float>(L.w) + sel, sa, &tm, chunk);
   if (rc || !c.memory_plus) return rc;
   // z = x W1 came with the projection: the stage is kept, empty, so that stage records
   // keep their shape
@@ -289,6 +293,7 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   const int H = c.n_heads, dq = c.d_query, k = c.k;
   const size_t eb = c.dtype == PKM_BF16 ? 2 : 4;
   float* ydbg = dbg ? dbg->y : nullptr;
+  const bool halves = dbg && (dbg->half_idx || dbg->half_score);
 
   const int nch = chunks_for(h, T);
   const int64_t tcs = (T + nch - 1) / nch;
@@ -296,7 +301,7 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   PKM_LAUNCH(tm.total(0, s));
   const bool gated = c.memory_plus != 0;
   if (nch == 1) {
-    int rc = chunk_select(h, x, 0, T, s, tm, 0);
+    int rc = chunk_select(h, x, 0, T, s, tm, 0, halves);
     if (!rc) rc = chunk_gather(h, 0, T, out, ydbg, s, tm, 0, false);
     if (!rc && gated) rc = chunk_gate(h, 0, T, out, s, tm, 0);
     if (rc) return rc;
@@ -317,7 +322,7 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
       int64_t t0, tc;
       span(ch, t0, tc);
       if (tc <= 0) break;
-      int rc = chunk_select(h, x, t0, tc, h->sA, tm, ch);
+      int rc = chunk_select(h, x, t0, tc, h->sA, tm, ch, halves);
       if (rc) return rc;
       PKM_HIP(hipEventRecord(h->ev_sel[ch], h->sA));
       PKM_HIP(hipStreamWaitEvent(h->sB, h->ev_sel[ch], 0));

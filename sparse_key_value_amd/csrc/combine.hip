@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  if (lane < 2 * k) {
+  if (half_idx && lane < 2 * k) {  // the per-half lists, when asked for
     const int c = lane / k, j = lane - c * k;
     const uint64_t key = lists[wv][c][j];
     const int64_t o = (row * 2 + c) * k + j;

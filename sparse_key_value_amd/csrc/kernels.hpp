@@ -35,7 +35,7 @@ hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T
                                    int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
                                    hipStream_t s);
 // Per-half top-k from the candidates, k x k combine, final top-k and softmax.
-// Outputs half_idx/half_score [T, H, 2, k], idx/score/w [T, H, k].
+// Outputs half_idx/half_score [T, H, 2, k] (both NULL: not written), idx/score/w [T, H, k].
 hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T, int H, int n, int k,
                           int32_t* half_idx, float* half_score, int32_t* idx, float* score, float* w, hipStream_t s);
 // Weighted EmbeddingBag: y[b] = sum_j w[b,j] table[idx[b,j]]; y fp32 or dtype.  With z
