@@ -215,6 +215,34 @@ def test_fused_step_ragged_bags(dt, dim, n_bags, H, k):
                                   np.asarray(host[untouched]).view(np.uint8))
 
 
+@pytest.mark.parametrize("dt,dim,n_rows", [("bf16", 256, 40), ("f32", 64, 5000)])
+def test_largest_bags(dt, dim, n_rows):
+    """Bags of 2,048 entries (64 heads x k = 32, the largest bag the backward takes): dw, ds,
+    the per-row gradients and the update, over 40 rows (every row shared by about 150
+    entries of three bags) and over 5,000 rows."""
+    from tests.gpu_util import to_dev, to_host
+    rng = np.random.default_rng(dim + n_rows)
+    n_bags, H, k = 3, 64, 32
+    bag = H * k
+    idx = rng.integers(-1, n_rows + 1, size=(n_bags, bag))
+    s_ = rng.standard_normal((n_bags, H, k))
+    w = np.exp(s_ - s_.max(-1, keepdims=True))
+    w = (w / w.sum(-1, keepdims=True)).reshape(n_bags, bag).astype(np.float32)
+    dy = rng.standard_normal((n_bags, dim)).astype(np.float32)
+    host = S.value_rows(19, np.arange(n_rows), dim, dt)
+    table = to_dev(host, dt)
+    lr = 0.25
+    say(f"bag fused step, largest bags {dt} dim {dim} rows {n_rows}")
+    got = _run(table, n_rows, dim, dt, idx, w, dy, k, update=True, lr=lr)
+    rows_of = lambda r: O.to_f64(host[np.asarray(r)], dt)
+    _check(got, rows_of, n_rows, idx, w.astype(np.float64), dy.astype(np.float64), k)
+    after = to_host(table)
+    _one_ulp(after[got["rows"]], O.to_f64(host[got["rows"]], dt) - lr * got["grad"].astype(np.float64), dt)
+    untouched = np.setdiff1d(np.arange(n_rows), got["rows"])
+    np.testing.assert_array_equal(np.asarray(after[untouched]).view(np.uint8),
+                                  np.asarray(host[untouched]).view(np.uint8))
+
+
 def test_deterministic():
     from tests.gpu_util import to_dev
     rng = np.random.default_rng(1)
