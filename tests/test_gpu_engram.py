@@ -134,6 +134,9 @@ def test_engram_small_workloads_every_token(name):
     dict(heads=1, head_dim=8, T=40, seq_len=40),              # one 16-byte slice per token... in f32: 2
     dict(heads=16, head_dim=128, dtype="bf16", T=70, seq_len=70),  # 4096-byte tokens, four slices per lane
     dict(heads=3, head_dim=24, dtype="bf16", T=50, seq_len=10, residual=True),  # slices not a multiple of 64
+    # 64 heads x 4 orders: 256 (order, head) pairs, four per lane
+    dict(heads=64, head_dim=8, min_order=1, n_orders=4, T=50, seq_len=20),
+    dict(heads=64, head_dim=32, dtype="bf16", min_order=2, n_orders=4, T=45, seq_len=45),  # and 4096-byte tokens
 ])
 def test_engram_edge_shapes(shape):
     cfg = C.ENGRAM_CONFIGS["engram_tiny_f32"].with_(**shape)
