@@ -31,7 +31,22 @@ namespace {
 struct Stair {
   uint16_t pos[128];  // (i << 8) | j for staircase slot s, 0xFFFF = empty
   uint8_t first_off[32];  // row a's first column off the staircase: floor(k / (a + 1))
+  uint8_t rect_col[32];   // ceil(k / (a + 1)) - 1: rows 0..a x columns 0..rect_col[a] hold >= k cells
 };
+
+// Sort 64 keys held one per lane in descending order (lane 0 ends with the largest).
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(x, stride);
+      const bool take_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      x = take_max ? (x > o ? x : o) : (x > o ? o : x);
+    }
+  }
+  return x;
+}
 
 // Sort 128 keys held two per lane (element e = 2 * lane + slot) in descending order.
 __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lane) {
@@ -64,6 +79,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
                                                       float* __restrict__ half_score, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, float* __restrict__ w) {
   __shared__ uint64_t lists[4][2][32];
+  __shared__ uint64_t surv[4][64];
   // the wave index made explicitly uniform: the row, its counts and the ranking loops
   // below are then scalar (a per-lane count made each loop divergent, with exec-mask
   // updates in every iteration)
@@ -132,9 +148,34 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   const uint16_t p0 = st.pos[2 * lane], p1 = st.pos[2 * lane + 1];
   uint64_t x0 = p0 != 0xFFFF ? cell_key(p0 >> 8, p0 & 0xFF) : 0ull;
   uint64_t x1 = p1 != 0xFFFF ? cell_key(p1 >> 8, p1 & 0xFF) : 0ull;
-  sort128_desc(x0, x1, lane);
-  // element e = 2 * lane + slot; the k-th best is element k - 1
-  const uint64_t kth = shfl_u64((k - 1) & 1 ? x1 : x0, (k - 1) >> 1);
+  // A lower bound of the k-th best sum: rows 0..a x columns 0..ceil(k/(a+1))-1 are at
+  // least k cells, each summing to at least the corner's sum (sorted lists, monotone fp32
+  // add), for every a; the largest such corner bounds the k-th best from below.  Staircase
+  // cells below it cannot be among the best k.  When at least k and at most 64 survive
+  // (about 70% of rows with random data), they are sorted one per lane; otherwise all
+  // 128 slots are, two per lane.
+  float lb = lane < k ? key_score(L0[lane]) + key_score(L1[st.rect_col[lane]]) : -__builtin_inff();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lb = fmaxf(lb, __shfl_xor(lb, o, WAVE));
+  const bool keep0 = x0 != 0ull && key_score(x0) >= lb, keep1 = x1 != 0ull && key_score(x1) >= lb;
+  const uint64_t m0 = __ballot(keep0), m1 = __ballot(keep1);
+  const int ns = __popcll(m0) + __popcll(m1);
+  const bool few = ns >= k && ns <= 64;  // wave-uniform
+  uint64_t y = 0ull, kth;
+  if (few) {
+    const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one (lane < 64)
+    if (keep0) surv[wv][__popcll(m0 & below)] = x0;
+    if (keep1) surv[wv][__popcll(m0) + __popcll(m1 & below)] = x1;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    y = lane < ns ? surv[wv][lane] : 0ull;
+    y = sort64_desc(y, lane);
+    kth = shfl_u64(y, k - 1);
+  } else {
+    sort128_desc(x0, x1, lane);
+    // element e = 2 * lane + slot; the k-th best is element k - 1
+    kth = shfl_u64((k - 1) & 1 ? x1 : x0, (k - 1) >> 1);
+  }
 
   // nothing off the staircase may beat the k-th key.  Both lists are sorted and an fp32
   // add is monotone, so the largest off-staircase sum of row a is at its first
@@ -150,9 +191,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   }
   uint64_t mine;  // lane j < k ends up with the j-th best key
   if (__ballot(beaten) == 0) {
-    // lane j takes element j = 2 * (j >> 1) + (j & 1)
-    const uint64_t a0 = shfl_u64(x0, lane >> 1), a1 = shfl_u64(x1, lane >> 1);
-    mine = (lane & 1) ? a1 : a0;
+    if (few) {
+      mine = y;
+    } else {
+      // lane j takes element j = 2 * (j >> 1) + (j & 1)
+      const uint64_t a0 = shfl_u64(x0, lane >> 1), a1 = shfl_u64(x1, lane >> 1);
+      mine = (lane & 1) ? a1 : a0;
+    }
   } else {
     // exhaustive: k rounds of a wave-wide maximum over all k*k keys
     const int kk = k * k;
@@ -199,6 +244,7 @@ hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T,
     for (int b = 0; (a + 1) * (b + 1) <= k; ++b) st.pos[m++] = (uint16_t)((a << 8) | b);
   for (; m < 128; ++m) st.pos[m] = 0xFFFF;
   for (int a = 0; a < 32; ++a) st.first_off[a] = (uint8_t)(a < k ? k / (a + 1) : 0);
+  for (int a = 0; a < 32; ++a) st.rect_col[a] = (uint8_t)(a < k ? (k + a) / (a + 1) - 1 : 0);
   combine_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(cand, count, rows, n, k, st, half_idx, half_score,
                                                                   idx, score, w);
   return hipGetLastError();
