@@ -12,11 +12,12 @@
 // One wave per (token, head).  First the two per-half lists: each half's candidates
 // (at most CAND keys from the scoring kernel, a superset of its top-k) are ranked by
 // comparing every key with every other (v_readlane broadcasts), and the k best are
-// written, in order, to LDS and to the per-half outputs.  Both lists are then sorted,
-// so the pair of positions (i, j)
-// is beaten by every (i', j') with i' <= i, j' <= j; in exact arithmetic only the
-// "staircase" (i + 1)(j + 1) <= k can reach the top-k (119 pairs for k = 32 instead of
-// 1,024).  The staircase is sorted with a bitonic network over two keys per lane.  The
+// written, in order, to LDS (and to the per-half outputs when asked for).  Both lists are
+// then sorted, so the pair of positions (i, j) is beaten by every (i', j') with i' <= i,
+// j' <= j; in exact arithmetic only the "staircase" (i + 1)(j + 1) <= k can reach the
+// top-k (119 pairs for k = 32 instead of 1,024).  Staircase cells below a lower bound of
+// the k-th best sum are dropped, and the rest sorted with a bitonic network (one key per
+// lane when at most 64 are left, else two per lane over all 128 slots).  The
 // fp32 rounding of a sum can merge two distinct sums into a tie that the flat index
 // then breaks the other way, so the cells off the staircase are checked against the
 // k-th key found (one check per row of the grid, by monotonicity); if any could reach
