@@ -565,14 +565,18 @@ def test_largest_sub_key_lists():
     pk.close()
 
 
-def test_forward_in_a_hip_graph():
+@pytest.mark.parametrize("shape", [
+    dict(n_sub=256, T=300),             # few sub-keys: every row scored exhaustively
+    dict(n_sub=1100, T=600, H=64),      # the two MFMA passes in 8-wave blocks, theta, overflow scan
+])
+def test_forward_in_a_hip_graph(shape):
     """The forward allocates nothing and never waits on the host, so it can be captured in a
     HIP graph: every replay equals the eager forward bitwise, also after the captured input
     changes, with eager forwards and other work between the replays."""
     import sparse_key_value_amd as P
     G = _G()
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name="graph", n_sub=256, T=300, d_v=256, d_model=256, memory_plus=True)
-    say("forward in a HIP graph")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name="graph", d_v=256, d_model=256, memory_plus=True, **shape)
+    say(f"forward in a HIP graph {shape}")
     wl = G.Workload(cfg, seed=21)
     T, H, k = wl.T, cfg.H, cfg.k
     x = wl.dev["x"].clone()
