@@ -43,7 +43,9 @@ namespace pkm {
 
 namespace {
 
-constexpr int TPW = 64;         // tokens per wave (two MFMA columns of 32)
+// A wave scores FR token fragments of 32 (one 32-token MFMA column each): FR = 2 (64
+// tokens per wave) reuses every LDS operand read for two MFMAs; FR = 1 serves batches too
+// small to give every CU eight 64-token waves per pair.
 constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
 // chunks loaded per barrier: 8-wave blocks (one per CU, LDS to spare) take two chunks
 // between barriers, which halves the barriers and the skew every one of them absorbs
@@ -89,9 +91,9 @@ __device__ __forceinline__ float load_elem_f32(const uint16_t* p, size_t i) { re
 
 __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_base + 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-// The shared MFMA sweep over all sub-keys of one pair for the block's NW * 64 tokens.
-// `on_tile(ch, acc)` receives, per 32-sub-key chunk, the scores of this lane's two
-// tokens (acc[0]: token lane%32 of the wave, acc[1]: token 32 + lane%32).
+// The shared MFMA sweep over all sub-keys of one pair for the block's NW * FR * 32 tokens.
+// `on_tile(ch, acc)` receives, per 32-sub-key chunk, the scores of this lane's FR tokens
+// (acc[g]: token 32 g + lane%32 of the wave).
 //
 // NW = 4: one wave per SIMD per block, two blocks per CU.  Both blocks start together and
 // do the same work, so their two waves on a SIMD run in step: both issue MFMAs, then both
@@ -101,7 +103,7 @@ __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_
 // chunk ch - 1 runs right after the barrier, beside the first group's MFMAs of chunk ch,
 // and its MFMAs of chunk ch beside the first group's selection), which keeps the matrix
 // core fed through both halves.  The accumulators live across the barrier for that.
-template <typename DT, int DH, int NW, typename F>
+template <typename DT, int DH, int NW, int FR, typename F>
 __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t T, int H, int n,
                                       uint8_t* ks, F&& on_tile) {
   using M = Mma<DT, DH>;
@@ -114,10 +116,10 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   const int h = pair >> 1, c = pair & 1;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), hi = lane >> 5;
 
-  typename M::frag qf[2][M::NK];
+  typename M::frag qf[FR][M::NK];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
+  for (int g = 0; g < FR; ++g) {
+    const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     const DT* qrow = qhat + ((t * H + h) * 2 + c) * (int64_t)DH;
 #pragma unroll
     for (int kk = 0; kk < M::NK; ++kk) qf[g][kk] = t < T ? M::load_q(qrow, kk, hi) : typename M::frag{};
@@ -161,7 +163,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   constexpr int SC = chunks_per_barrier(NW);
   // the lagging group (wave-uniform)
   const bool lag = NW == 8 && wv >= 4;
-  f32x16 acc[2];
+  f32x16 acc[FR];
 #pragma unroll
   for (int j = 0; j < SC; ++j)
     if (j < nch) fetch(j, j);
@@ -177,8 +179,8 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
     }
     if (lag && ch > 0) on_tile(ch - 1, (const f32x16*)acc);
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
-    acc[0] = f32x16{};
-    acc[1] = f32x16{};
+#pragma unroll
+    for (int g = 0; g < FR; ++g) acc[g] = f32x16{};
     if constexpr (M::EB == 2) {
       // bf16: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling groups
       // below keep the compiler from pulling the reads back next to their use (it
@@ -191,21 +193,21 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
         if (kk + PD < M::NK) a[kk + PD] = M::lds_k(myrow, swz, kk + PD, hi);
-        acc[0] = M::mma(a[kk], qf[0][kk], acc[0]);
-        acc[1] = M::mma(a[kk], qf[1][kk], acc[1]);
+#pragma unroll
+        for (int g = 0; g < FR; ++g) acc[g] = M::mma(a[kk], qf[g][kk], acc[g]);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, PD < M::NK ? PD : M::NK, 0);  // DS reads
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
         if (kk + PD < M::NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                      // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, FR, 0);                     // MFMAs
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
         const typename M::frag a = M::lds_k(myrow, swz, kk, hi);
-        acc[0] = M::mma(a, qf[0][kk], acc[0]);
-        acc[1] = M::mma(a, qf[1][kk], acc[1]);
+#pragma unroll
+        for (int g = 0; g < FR; ++g) acc[g] = M::mma(a, qf[g][kk], acc[g]);
       }
     }
     if (!lag) on_tile(ch, (const f32x16*)acc);
@@ -231,7 +233,7 @@ __device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, 
 // 16-byte stores, so that few stores are in flight when a chunk waits for its loads
 // (NB = 4 with 8-wave blocks, whose lagging group holds its accumulators across the
 // barrier: 8 spilled there).
-template <typename DT, int DH, int GS, int NW>
+template <typename DT, int DH, int GS, int NW, int FR>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, float* __restrict__ gmax) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
@@ -244,25 +246,27 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   const int h = pair >> 1, c = pair & 1;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   constexpr int NB = NW == 8 ? 4 : 8;
-  float run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float buf[2][NB];
+  float run[FR];
+  float buf[FR][NB];
   int nbuf = 0;  // groups in buf (wave-uniform)
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < FR; ++g) {
+    run[g] = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < NB; ++j) buf[g][j] = 0.f;
-  float* gm[2];
-  bool live[2];
+  }
+  float* gm[FR];
+  bool live[FR];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
+  for (int g = 0; g < FR; ++g) {
+    const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     live[g] = hi == 0 && t < T;
     gm[g] = gmax + ((t * H + h) * 2 + c) * (int64_t)MAX_GROUPS;
   }
   int done = 0;  // groups written
   auto push = [&](const float* m) {  // one finished group per token of this lane
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < FR; ++g) {
 #pragma unroll
       for (int j = 0; j < NB - 1; ++j) buf[g][j] = buf[g][j + 1];
       buf[g][NB - 1] = m[g];
@@ -270,7 +274,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
     // shift register: the newest is buf[NB - 1]; after NB pushes buf[0] is the oldest
     if (++nbuf == NB) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < FR; ++g) {
         if (!live[g]) continue;
 #pragma unroll
         for (int j = 0; j < NB; j += 4)
@@ -280,11 +284,11 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
       nbuf = 0;
     }
   };
-  sweep<DT, DH, NW>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
-    float mg[2][GPC];
+    float mg[FR][GPC];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < FR; ++g) {
       // a group of 8 << GS sub-keys inside the chunk covers rows [4j, 4j + 4 << GS) of both lanes
 #pragma unroll
       for (int j = 0; j < GPC; ++j) {
@@ -298,22 +302,25 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
 #pragma unroll
       for (int j = 0; j < GPC; ++j) {
         if (ch * CHUNK + j * (8 << GS) < n) {
-          const float m[2] = {mg[0][j], mg[1][j]};
+          float m[FR];
+#pragma unroll
+          for (int g = 0; g < FR; ++g) m[g] = mg[g][j];
           push(m);
         }
       }
     } else {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) run[g] = fmaxf(run[g], mg[g][0]);
+      for (int g = 0; g < FR; ++g) run[g] = fmaxf(run[g], mg[g][0]);
       if (((ch + 1) & (SPAN - 1)) == 0 || (ch + 1) * CHUNK >= n) {
         push(run);
-        run[0] = run[1] = -__builtin_inff();
+#pragma unroll
+        for (int g = 0; g < FR; ++g) run[g] = -__builtin_inff();
       }
     }
   });
   // the last < NB groups: buf[NB - nbuf .. NB - 1] hold groups done .. done + nbuf - 1
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < FR; ++g) {
     if (!live[g]) continue;
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -357,15 +364,16 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
 // Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
 // theta).  Each of a token's two lanes owns half of the row's CAND slots and counts its
 // own candidates.
-template <typename DT, int DH, int NW>
+template <typename DT, int DH, int NW, int FR>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, int k, const float* __restrict__ theta,
                                                        uint64_t* __restrict__ cand, int32_t* __restrict__ count) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int HALF = CAND / 2;
-  // SROW floats per lane: the lane's 32 scores of the chunk, read back by position for the
-  // appends (36, not 32: 16-byte stores of 16 consecutive lanes then hit distinct banks)
-  constexpr int SROW = 36;
+  // SROW floats per lane: the lane's 16 FR scores of the chunk, read back by position for
+  // the appends (36 or 20, not 32 or 16: 16-byte stores of 16 consecutive lanes then hit
+  // distinct banks)
+  constexpr int SROW = 16 * FR + 4;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
   const int pairs = 2 * H;
@@ -373,24 +381,25 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  float thr[2];
-  int cnt[2] = {0, 0}, eq[2] = {0, 0};
-  uint64_t* dst[2];
-  int64_t row[2];
+  float thr[FR];
+  int cnt[FR], eq[FR];
+  uint64_t* dst[FR];
+  int64_t row[FR];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
+  for (int g = 0; g < FR; ++g) {
+    cnt[g] = eq[g] = 0;
+    const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     row[g] = (t * H + h) * 2 + c;
     thr[g] = t < T ? theta[row[g]] : __builtin_inff();
     dst[g] = cand + row[g] * CAND + hi * HALF;
   }
   // thz: the bound with a zero bound taken as -0, so that the sign of (score - thz) is
   // set exactly when score < bound, -0 scores included (x - x is +0; finite values)
-  float thz[2];
+  float thz[FR];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
+  for (int g = 0; g < FR; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
   float* my = stage + (wv * 64 + lane) * SROW;
-  sweep<DT, DH, NW>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     // bit 16 g + r: score r of token fragment g reaches the bound.  The sign bits of the
     // differences are shifted in with v_alignbit: two VALU ops per score and no lane
@@ -398,7 +407,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
     // every compare).
     uint32_t m = 0;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < FR; ++g) {
       uint32_t miss = 0;
 #pragma unroll
       for (int r = 15; r >= 0; --r) miss = __builtin_amdgcn_alignbit(miss, __float_as_uint(acc[g][r] - thz[g]), 31);
@@ -409,7 +418,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       uint32_t valid = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) valid |= (8 * (r >> 2) + 4 * hi + (r & 3) < nv ? 1u : 0u) << r;
-      m &= valid * 0x10001u;
+      m &= FR == 2 ? valid * 0x10001u : valid;
     }
     // the appends loop over the set bits only (both fragments in one loop), so the wave
     // runs as many rounds as its busiest lane has candidates in this chunk; a hit's score
@@ -417,7 +426,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
     // position cost 30 VALU ops per round)
     if (m) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < FR; ++g)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *(f32x4*)(my + 16 * g + 4 * j) = f32x4{acc[g][4 * j], acc[g][4 * j + 1], acc[g][4 * j + 2], acc[g][4 * j + 3]};
@@ -428,17 +437,17 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       const int g = b >> 4, r = b & 15;
       const float s = my[b];
       const int sub = sub_of(ch * CHUNK, r, hi);
-      int cn = g ? cnt[1] : cnt[0];
-      int e = g ? eq[1] : eq[0];
+      int cn = g ? cnt[FR - 1] : cnt[0];
+      int e = g ? eq[FR - 1] : eq[0];
       bool take = true;
-      if (s == (g ? thr[1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
+      if (s == (g ? thr[FR - 1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
       if (take) {
-        if (cn < HALF) (g ? dst[1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
+        if (cn < HALF) (g ? dst[FR - 1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
         ++cn;
       }
       if (g) {
-        cnt[1] = cn;
-        eq[1] = e;
+        cnt[FR - 1] = cn;
+        eq[FR - 1] = e;
       } else {
         cnt[0] = cn;
         eq[0] = e;
@@ -446,8 +455,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
     }
   });
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int64_t t = tile * (TPW * NW) + wv * TPW + g * 32 + (lane & 31);
+  for (int g = 0; g < FR; ++g) {
+    const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     if (t < T) count[row[g] * 2 + hi] = cnt[g];
   }
 }
@@ -544,10 +553,10 @@ __global__ void __launch_bounds__(256) direct_kernel(const DT* __restrict__ qhat
   exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
 }
 
-template <typename DT, int DH, int NW>
+template <typename DT, int DH, int NW, int FR>
 hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax,
                             float* theta, uint64_t* cand, int32_t* count, hipStream_t s) {
-  const int64_t tiles = (T + TPW * NW - 1) / (TPW * NW);
+  const int64_t tiles = (T + 32 * FR * NW - 1) / (32 * FR * NW);
   const dim3 grid((unsigned)(tiles * 2 * H));
   int gshift = 0;
   while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
@@ -559,7 +568,7 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
                                                                          k, cand, count);
     return hipGetLastError();
   }
-#define PKM_P1(G) pass1_kernel<DT, DH, G, NW><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
+#define PKM_P1(G) pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
   switch (gshift) {
     case 0: PKM_P1(0); break;
     case 1: PKM_P1(1); break;
@@ -574,7 +583,7 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   if ((e = hipGetLastError()) != hipSuccess) return e;
   theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  pass2_kernel<DT, DH, NW><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
+  pass2_kernel<DT, DH, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t scan_waves = (rows + 63) / 64;
   const int64_t ob = (scan_waves + 3) / 4 < 1024 ? (scan_waves + 3) / 4 : 1024;
@@ -583,7 +592,8 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
 }
 
 // 8-wave blocks where a chunk splits evenly over 8 waves and the batch gives every CU one
-// block of them; else 4-wave blocks (twice the blocks for small batches).
+// block of them: 64 tokens per wave if the batch allows, else 32 (a block of 256 tokens).
+// Else 4-wave blocks of 64-token waves (fewer blocks than CUs: one wave per SIMD).
 template <typename DT, int DH>
 constexpr bool eight_waves_built() {
   return (CHUNK * DH * (int)sizeof(DT) / 16) % (64 * 8) == 0;
@@ -601,9 +611,11 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   }
   if constexpr (eight_waves_built<DT, DH>()) {
     if ((T + 511) / 512 * 2 * H >= cus)
-      return launch_passes_nw<DT, DH, 8>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+      return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+    if ((T + 255) / 256 * 2 * H >= cus)
+      return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
   }
-  return launch_passes_nw<DT, DH, 4>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+  return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
 }
 
 }  // namespace

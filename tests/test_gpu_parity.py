@@ -286,6 +286,13 @@ def _sample_tokens(T, n=96, tail=24):
     # groups of 8 sub-keys (four group maxima per chunk) in 8-wave blocks
     dict(name="eight_waves_groups_of_8", dtype="bf16", qk_norm=True, n_sub=700, k=16, H=64, d_q=512, d_model=64,
          d_v=64, T=700),
+    # batches that fill the CUs only with 32-token waves (8-wave blocks of 256 tokens)
+    dict(name="eight_waves_32_tokens_dh256", dtype="bf16", qk_norm=True, n_sub=1100, k=8, H=64, d_q=512, d_model=64,
+         d_v=64, T=300),
+    dict(name="eight_waves_32_tokens_dh128", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=1030, k=16, H=16,
+         d_q=256, d_model=128, d_v=128, T=1900),
+    dict(name="eight_waves_32_tokens_f32_dh64", dtype="f32", qk_norm=False, n_sub=1050, k=8, H=32, d_q=128, d_model=64,
+         d_v=64, T=1000),
 ])
 def test_eight_wave_scoring_blocks(case):
     case = dict(case)
@@ -369,9 +376,10 @@ def _sample_rows(T, n=40, seed=1):
     return rows
 
 
-@pytest.mark.parametrize("name", ["memplus_16m_bf16", "memplus_64m_bf16"])
+@pytest.mark.parametrize("name", ["memplus_16m_bf16", "memplus_64m_bf16", "pkm_1m_bf16"])
 def test_full_size_sampled_tokens(name):
-    """The headline and the largest workload at full size, as the benchmark runs them."""
+    """The headline, the largest and the 1M-key workload at full size, as the benchmark runs
+    them (the 1M-key batch takes the 32-token waves of the scoring passes)."""
     cfg = CONFIGS[name]
     say(f"{name}: filling {cfg.N} x {cfg.d_v} value table on the GPU")
     wl = _G().Workload(cfg)
