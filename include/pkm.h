@@ -67,7 +67,7 @@ typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 
 typedef struct {
   int32_t d_model;      /* width of x; a multiple of 32 for bf16 (4 for fp32) */
-  int32_t n_heads;      /* H >= 1 */
+  int32_t n_heads;      /* 1 <= H <= 64 */
   int32_t d_query;      /* per-head query width d_q; d_q / 2 in {64, 128, 256} (256: bf16 only) */
   int32_t n_sub;        /* sub-keys per half; the table has N = n_sub^2 < 2^31 rows */
   int32_t k;            /* per-half and final top-k, 1 <= k <= min(n_sub, 32) */
