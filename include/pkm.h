@@ -75,8 +75,8 @@ typedef struct {
   int32_t dtype;        /* pkm_dtype of x, W_q, subkeys, values, W1, W2 and out */
   int32_t qk_norm;      /* 0 or 1: RMSNorm of the query (before the split) and of sub-key rows */
   int32_t memory_plus;  /* 0: out = y [T, d_value]; 1: gated out [T, d_model] */
-  float norm_eps;       /* RMSNorm epsilon, >= 0 (1e-6 in the shipped workloads) */
-  int64_t max_tokens;   /* largest T a forward may take; sizes the workspace */
+  float norm_eps;       /* RMSNorm epsilon in [0, 1] (1e-6 in the shipped workloads) */
+  int64_t max_tokens;   /* largest T a forward may take, 1..2^24; sizes the workspace */
 } pkm_config;
 
 /* Stage ids for the optional per-stage timing. */
