@@ -105,14 +105,11 @@ __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_
 // core fed through both halves.  The accumulators live across the barrier for that.
 template <typename DT, int DH, int NW, int FR, typename F>
 __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t T, int H, int n,
-                                      uint8_t* ks, F&& on_tile) {
+                                      int pair, int64_t tile, int c0, int c1, uint8_t* ks, F&& on_tile) {
   using M = Mma<DT, DH>;
   constexpr int RB = DH * M::EB;          // bytes per sub-key row
   constexpr int U16 = RB / 16;            // 16-byte units per row
 
-  const int pairs = 2 * H;
-  const int pair = blockIdx.x % pairs;
-  const int64_t tile = blockIdx.x / pairs;
   const int h = pair >> 1, c = pair & 1;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), hi = lane >> 5;
 
@@ -126,7 +123,6 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   }
 
   const uint8_t* kbase = (const uint8_t*)(khat + (size_t)pair * n * DH);
-  const int nch = (n + CHUNK - 1) / CHUNK;
   // Chunk ch goes to LDS buffer b by direct global->LDS loads: wave wv's i-th load fills
   // the 64 consecutive 16-byte units starting at unit (wv * DPW + i) * 64, and each lane
   // fetches the global unit that belongs at its LDS unit under the XOR swizzle.  Rows past
@@ -158,26 +154,28 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   };
   const int swz = (lane & 31) % U16;
 
-  // SC chunks per barrier: chunk ch lives in LDS buffer ch % (2 SC); the SC chunks after a
-  // barrier are loaded into the other SC buffers while they are scored
+  // The block sweeps chunks [c0, c1).  SC chunks per barrier: the chunk at position lc =
+  // ch - c0 lives in LDS buffer lc % (2 SC); the SC chunks after a barrier are loaded into
+  // the other SC buffers while they are scored
   constexpr int SC = chunks_per_barrier(NW);
   // the lagging group (wave-uniform)
   const bool lag = NW == 8 && wv >= 4;
   f32x16 acc[FR];
 #pragma unroll
   for (int j = 0; j < SC; ++j)
-    if (j < nch) fetch(j, j);
+    if (c0 + j < c1) fetch(c0 + j, j);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch % (2 * SC);
+  for (int ch = c0; ch < c1; ++ch) {
+    const int lc = ch - c0;
+    const int buf = lc % (2 * SC);
     // the other SC buffers were last read before the barrier that ended the previous group
-    if (ch % SC == 0) {
+    if (lc % SC == 0) {
 #pragma unroll
       for (int j = 0; j < SC; ++j)
-        if (ch + SC + j < nch) fetch(ch + SC + j, (ch + SC + j) % (2 * SC));
+        if (ch + SC + j < c1) fetch(ch + SC + j, (lc + SC + j) % (2 * SC));
     }
-    if (lag && ch > 0) on_tile(ch - 1, (const f32x16*)acc);
+    if (lag && lc > 0) on_tile(ch - 1, (const f32x16*)acc);
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
 #pragma unroll
     for (int g = 0; g < FR; ++g) acc[g] = f32x16{};
@@ -211,12 +209,32 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
       }
     }
     if (!lag) on_tile(ch, (const f32x16*)acc);
-    if (ch % SC == SC - 1 || ch + 1 == nch) {
+    if (lc % SC == SC - 1 || ch + 1 == c1) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
     }
   }
-  if (lag) on_tile(nch - 1, (const f32x16*)acc);
+  if (lag) on_tile(c1 - 1, (const f32x16*)acc);
+}
+
+// Block b: pair (h, c) = b mod 2H (so each XCD only reads one pair's sub-keys), then the
+// split of the sub-key chunks, then the token tile.  A batch too small to give every CU a
+// block sweeps the sub-keys in `splits` ranges of `cps` chunks, one block each.
+struct BlockPos {
+  int pair, c0, c1, split;
+  int64_t tile;
+};
+__device__ __forceinline__ BlockPos block_pos(int H, int n, int splits, int cps) {
+  const int pairs = 2 * H;
+  const int64_t rest = blockIdx.x / pairs;
+  BlockPos p;
+  p.pair = blockIdx.x % pairs;
+  p.split = (int)(rest % splits);
+  p.tile = rest / splits;
+  const int nch = (n + CHUNK - 1) / CHUNK;
+  p.c0 = p.split * cps;
+  p.c1 = p.c0 + cps < nch ? p.c0 + cps : nch;
+  return p;
 }
 
 // Max over the 16 scores of one lane, or only over those of sub-keys < n.
@@ -235,14 +253,15 @@ __device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, 
 // barrier: 8 spilled there).
 template <typename DT, int DH, int GS, int NW, int FR>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
-                                                       int64_t T, int H, int n, float* __restrict__ gmax) {
+                                                       int64_t T, int H, int n, int splits, int cps,
+                                                       float* __restrict__ gmax, int32_t* __restrict__ zero_count) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
   constexpr int SPAN = GS <= 2 ? 1 : (1 << (GS - 2)); // chunks per group when a group spans chunks
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
-  const int pairs = 2 * H;
-  const int pair = blockIdx.x % pairs;
-  const int64_t tile = blockIdx.x / pairs;
+  const BlockPos bp = block_pos(H, n, splits, cps);
+  const int pair = bp.pair;
+  const int64_t tile = bp.tile;
   const int h = pair >> 1, c = pair & 1;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   constexpr int NB = NW == 8 ? 4 : 8;
@@ -261,9 +280,14 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   for (int g = 0; g < FR; ++g) {
     const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     live[g] = hi == 0 && t < T;
-    gm[g] = gmax + ((t * H + h) * 2 + c) * (int64_t)MAX_GROUPS;
+    const int64_t r2 = (t * H + h) * 2 + c;
+    gm[g] = gmax + r2 * (int64_t)MAX_GROUPS;
+    // with split sub-key ranges pass 2 counts every row's candidates with atomics: the
+    // first split clears the counts (both lane halves of the row)
+    if (zero_count && bp.split == 0 && t < T) zero_count[r2 * 2 + hi] = 0;
   }
-  int done = 0;  // groups written
+  // groups written: the split starts at a group boundary that is a multiple of NB groups
+  int done = GS <= 2 ? bp.c0 * GPC : bp.c0 / SPAN;
   auto push = [&](const float* m) {  // one finished group per token of this lane
 #pragma unroll
     for (int g = 0; g < FR; ++g) {
@@ -284,7 +308,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
       nbuf = 0;
     }
   };
-  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     float mg[FR][GPC];
 #pragma unroll
@@ -364,10 +388,11 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
 // Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
 // theta).  Each of a token's two lanes owns half of the row's CAND slots and counts its
 // own candidates.
-template <typename DT, int DH, int NW, int FR>
+template <typename DT, int DH, int NW, int FR, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
-                                                       int64_t T, int H, int n, int k, const float* __restrict__ theta,
-                                                       uint64_t* __restrict__ cand, int32_t* __restrict__ count) {
+                                                       int64_t T, int H, int n, int k, int splits, int cps,
+                                                       const float* __restrict__ theta, uint64_t* __restrict__ cand,
+                                                       int32_t* __restrict__ count) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int HALF = CAND / 2;
   // SROW floats per lane: the lane's 16 FR scores of the chunk, read back by position for
@@ -376,9 +401,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   constexpr int SROW = 16 * FR + 4;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
-  const int pairs = 2 * H;
-  const int pair = blockIdx.x % pairs;
-  const int64_t tile = blockIdx.x / pairs;
+  const BlockPos bp = block_pos(H, n, splits, cps);
+  const int pair = bp.pair;
+  const int64_t tile = bp.tile;
   const int h = pair >> 1, c = pair & 1;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   float thr[FR];
@@ -399,7 +424,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
 #pragma unroll
   for (int g = 0; g < FR; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
   float* my = stage + (wv * 64 + lane) * SROW;
-  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     // bit 16 g + r: score r of token fragment g reaches the bound.  The sign bits of the
     // differences are shifted in with v_alignbit: two VALU ops per score and no lane
@@ -442,7 +467,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       bool take = true;
       if (s == (g ? thr[FR - 1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
       if (take) {
-        if (cn < HALF) (g ? dst[FR - 1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
+        // split sub-key ranges share the row's lane-half list: a slot by an atomic count
+        const int slot = SPLIT ? atomicAdd(count + (g ? row[FR - 1] : row[0]) * 2 + hi, 1) : cn;
+        if (slot < HALF) (g ? dst[FR - 1] : dst[0])[slot] = make_key(s, (uint32_t)sub);
         ++cn;
       }
       if (g) {
@@ -454,10 +481,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       }
     }
   });
+  if (!SPLIT) {
 #pragma unroll
-  for (int g = 0; g < FR; ++g) {
-    const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
-    if (t < T) count[row[g] * 2 + hi] = cnt[g];
+    for (int g = 0; g < FR; ++g) {
+      const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
+      if (t < T) count[row[g] * 2 + hi] = cnt[g];
+    }
   }
 }
 
@@ -555,12 +584,27 @@ __global__ void __launch_bounds__(256) direct_kernel(const DT* __restrict__ qhat
 
 template <typename DT, int DH, int NW, int FR>
 hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax,
-                            float* theta, uint64_t* cand, int32_t* count, hipStream_t s) {
+                            float* theta, uint64_t* cand, int32_t* count, int cus, hipStream_t s) {
   const int64_t tiles = (T + 32 * FR * NW - 1) / (32 * FR * NW);
-  const dim3 grid((unsigned)(tiles * 2 * H));
   int gshift = 0;
   while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
   const int ngroups = (n + (8 << gshift) - 1) >> (3 + gshift);
+  // Sub-key splits for batches that leave CUs without a block: about one block per CU,
+  // each split a whole number of pass 1's store batches of NB groups (so its first group
+  // starts a 16-byte aligned batch)
+  const int nch = (n + CHUNK - 1) / CHUNK;
+  const int64_t blocks1 = tiles * 2 * H;
+  int splits = 1, cps = nch;
+  if (blocks1 < cus) {
+    const int NB = NW == 8 ? 4 : 8;
+    const int align = gshift <= 2 ? NB / (4 >> gshift) : (1 << (gshift - 2)) * NB;
+    const int want = (int)(cus / blocks1);
+    int c = (nch + want - 1) / want;
+    c = (c + align - 1) / align * align;
+    cps = c < nch ? c : nch;
+    splits = (nch + cps - 1) / cps;
+  }
+  const dim3 grid((unsigned)(tiles * splits * 2 * H));
   const int64_t rows = T * H * 2;
   hipError_t e;
   if (ngroups < 2 * k) {
@@ -568,7 +612,9 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
                                                                          k, cand, count);
     return hipGetLastError();
   }
-#define PKM_P1(G) pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, gmax)
+#define PKM_P1(G)                                                                                       \
+  pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, splits, cps, gmax, \
+                                                           splits > 1 ? count : nullptr)
   switch (gshift) {
     case 0: PKM_P1(0); break;
     case 1: PKM_P1(1); break;
@@ -583,7 +629,12 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   if ((e = hipGetLastError()) != hipSuccess) return e;
   theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  pass2_kernel<DT, DH, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, theta, cand, count);
+  if (splits > 1)
+    pass2_kernel<DT, DH, NW, FR, true><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, splits, cps,
+                                                                theta, cand, count);
+  else
+    pass2_kernel<DT, DH, NW, FR, false><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, 1, nch,
+                                                                 theta, cand, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t scan_waves = (rows + 63) / 64;
   const int64_t ob = (scan_waves + 3) / 4 < 1024 ? (scan_waves + 3) / 4 : 1024;
@@ -612,10 +663,10 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   }
   if constexpr (eight_waves_built<DT, DH>()) {
     if ((T + 511) / 512 * 2 * H >= cus)
-      return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
-    return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+      return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
+    return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
   } else {
-    return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s);
+    return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
   }
 }
 

@@ -209,6 +209,22 @@ def test_tiny_fp32_ragged_token_counts(T):
     wl.close()
 
 
+@pytest.mark.parametrize("name,T", [("memplus_16m_bf16", 200), ("memplus_64m_bf16", 77)])
+def test_small_batches_split_the_sub_keys(name, T):
+    """A batch far smaller than the chip (200 and 77 tokens over 4,096 and 8,192 sub-keys):
+    every block sweeps one range of the sub-keys and the ranges share each row's candidate
+    list through atomic counts."""
+    cfg = CONFIGS[name].with_(T=T)
+    say(f"{name} T={T}: sub-key splits")
+    wl = _G().Workload(cfg, T=T)
+    o = run_debug(wl)
+    full_check(wl, o)
+    wl.close()
+    del wl, o
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_pkm_1m_bf16_stagewise_ragged():
     cfg = CONFIGS["pkm_1m_bf16"]
     say(f"{cfg.name} T=300")
