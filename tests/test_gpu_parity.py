@@ -360,10 +360,11 @@ def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub):
     wl.close()
 
 
-def test_forward_is_deterministic_and_matches_plain_forward():
+@pytest.mark.parametrize("n_sub", [256, 1100])   # exhaustive rows; split sub-key ranges with atomic counts
+def test_forward_is_deterministic_and_matches_plain_forward(n_sub):
     import sparse_key_value_amd as P
-    cfg = CONFIGS["pkm_1m_bf16"].with_(n_sub=256, T=257, d_v=256)
-    say("determinism")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(n_sub=n_sub, T=257, d_v=256)
+    say(f"determinism n_sub={n_sub}")
     wl = _G().Workload(cfg, seed=8)
     outs = []
     for _ in range(2):
@@ -595,6 +596,7 @@ def test_largest_sub_key_lists():
 @pytest.mark.parametrize("shape", [
     dict(n_sub=256, T=300),             # few sub-keys: every row scored exhaustively
     dict(n_sub=1100, T=600, H=64),      # the two MFMA passes in 8-wave blocks, theta, overflow scan
+    dict(n_sub=1100, T=200),            # a small batch: split sub-key ranges, atomic candidate counts
 ])
 def test_forward_in_a_hip_graph(shape):
     """The forward allocates nothing and never waits on the host, so it can be captured in a
