@@ -711,6 +711,8 @@ def main():
                     help="time the value-table backward and sparse update instead of the forward")
     ap.add_argument("--tables", choices=["device", "host"], default="device",
                     help="Engram workloads: keep the tables in HBM or in pinned host memory (prefetched)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="product-key forward: a batch of this many tokens instead of the workload's (small batches)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the path has no multi-GPU execution; "
@@ -737,6 +739,8 @@ def main():
     from tests.gpu_util import Workload
 
     cfg = CONFIGS[a.workload]
+    if a.tokens > 0:
+        cfg = cfg.with_(T=a.tokens)
     T = cfg.T
     log(f"workload {cfg.name}: T={T}, N={cfg.N}, d_v={cfg.d_v}, {cfg.dtype}; filling the value table")
     host = a.tables == "host"
@@ -819,7 +823,9 @@ def main():
         cpu["gather_GBps_equivalent"] = cpu["value"] * alg_b / T / 1e9
 
     # the committed counters were taken with device-resident tables
-    traffic = counter_traffic(GATHER_COUNTERS[cfg.name]) if (not host and cfg.name in GATHER_COUNTERS) else None
+    # the counters were taken at the workload's own batch; another batch size has other bytes
+    traffic = (counter_traffic(GATHER_COUNTERS[cfg.name]) if (not host and cfg.name in GATHER_COUNTERS and a.tokens <= 0)
+               else None)
     res = {
         "metric": METRIC,
         "value": tok_s,
