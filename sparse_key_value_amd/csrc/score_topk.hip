@@ -37,6 +37,10 @@
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
 //    dealt round-robin to the 8 XCDs, so with 2H dividing 8 each XCD only ever reads
 //    one pair's sub-keys, which stay resident in that XCD's L2.
+//  * A batch too small to give every CU a block splits the sub-keys into ranges of whole
+//    chunks, one block per (tile, range, pair): pass 1 writes each range's group maxima,
+//    and pass 2's ranges share a row's candidate list through atomic counts (cleared by
+//    the first range's pass 1 blocks).
 #include "kernels.hpp"
 
 namespace pkm {
