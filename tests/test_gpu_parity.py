@@ -387,6 +387,51 @@ def test_forward_is_deterministic_and_matches_plain_forward(n_sub):
     wl.close()
 
 
+def test_forward_on_a_side_stream_follows_its_inputs():
+    """The forward enqueues every kernel (hipBLASLt's included) on the caller's stream: on a
+    side stream whose input is written late by earlier work on that same stream, the result
+    equals the default stream's bit for bit (a kernel on any other stream would read the
+    input before it is written)."""
+    import sparse_key_value_amd as P
+    cfg = CONFIGS["pkm_1m_bf16"].with_(n_sub=1100, T=700, d_v=256)
+    say("side stream")
+    wl = _G().Workload(cfg, seed=9)
+    x = wl.dev["x"]
+
+    def buffers():
+        return (torch.empty((wl.T, cfg.d_out), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda"),
+                torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda"))
+
+    ref = buffers()
+    P.pkm_forward(wl.pkm.handle, x, wl.T, *ref)
+    torch.cuda.synchronize()
+    ref = [r.view(torch.int16).cpu() if r.dtype == torch.bfloat16 else r.cpu() for r in ref]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    got = []
+    for explicit in (False, True):
+        with torch.cuda.stream(s):
+            a = torch.randn(4096, 4096, device="cuda")
+            for _ in range(8):   # about a millisecond of work ahead of the input's copy
+                a = torch.tanh(a @ a)
+            x2 = torch.zeros_like(x)
+            x2.copy_(x)
+            bufs = buffers()
+        if explicit:   # the stream passed by argument, from outside its context
+            P.pkm_forward(wl.pkm.handle, x2, wl.T, *bufs, stream=s)
+        else:          # the current stream
+            with torch.cuda.stream(s):
+                P.pkm_forward(wl.pkm.handle, x2, wl.T, *bufs)
+        s.synchronize()
+        got.append([b.view(torch.int16).cpu() if b.dtype == torch.bfloat16 else b.cpu() for b in bufs])
+    for g in got:
+        for r, b in zip(ref, g):
+            assert torch.equal(r, b)
+    wl.close()
+
+
 def _sample_rows(T, n=40, seed=1):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, n, replace=False)]))
