@@ -40,7 +40,8 @@
 //  * A batch too small to give every CU a block splits the sub-keys into ranges of whole
 //    chunks, one block per (tile, range, pair): pass 1 writes each range's group maxima,
 //    and pass 2's ranges share a row's candidate list through atomic counts (cleared by
-//    the first range's pass 1 blocks).
+//    the first range's pass 1 blocks), each lane staging up to eight candidates in LDS
+//    and taking their slots with one atomic.
 #include "kernels.hpp"
 
 namespace pkm {
@@ -403,8 +404,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   // the appends (36 or 20, not 32 or 16: 16-byte stores of 16 consecutive lanes then hit
   // distinct banks)
   constexpr int SROW = 16 * FR + 4;
+  // split sub-key ranges: a lane keeps up to STASH of its candidates in LDS and publishes
+  // them with one atomic count per stash (an atomic per candidate, waited for before its
+  // store, cost 15-17% of the four scoring kernels at 256-4,096 tokens)
+  constexpr int STASH = SPLIT ? 8 : 1;
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
+  __shared__ uint64_t stash[SPLIT ? STASH * FR * NW * 64 : 1];
   const BlockPos bp = block_pos(H, n, splits, cps);
   const int pair = bp.pair;
   const int64_t tile = bp.tile;
@@ -428,6 +434,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
 #pragma unroll
   for (int g = 0; g < FR; ++g) thz[g] = thr[g] == 0.f ? -0.f : thr[g];
   float* my = stage + (wv * 64 + lane) * SROW;
+  // stash slot i of fragment g: consecutive lanes at consecutive words
+  auto stash_at = [&](int g, int i) -> uint64_t& { return stash[((i * FR + g) * NW + wv) * 64 + lane]; };
+  // the row's lane-half list gets nst more keys: slots by one atomic count (a count beyond
+  // HALF sends the row to the overflow pass, as a full list does)
+  auto publish = [&](int g, int nst) {
+    const int base = atomicAdd(count + (g ? row[FR - 1] : row[0]) * 2 + hi, nst);
+    uint64_t* d = g ? dst[FR - 1] : dst[0];
+    for (int i = 0; i < nst; ++i)
+      if (base + i < HALF) d[base + i] = stash_at(g, i);
+  };
   sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     // bit 16 g + r: score r of token fragment g reaches the bound.  The sign bits of the
@@ -471,9 +487,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       bool take = true;
       if (s == (g ? thr[FR - 1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
       if (take) {
-        // split sub-key ranges share the row's lane-half list: a slot by an atomic count
-        const int slot = SPLIT ? atomicAdd(count + (g ? row[FR - 1] : row[0]) * 2 + hi, 1) : cn;
-        if (slot < HALF) (g ? dst[FR - 1] : dst[0])[slot] = make_key(s, (uint32_t)sub);
+        if constexpr (SPLIT) {  // split sub-key ranges share the row's lane-half list
+          if (cn == STASH) {
+            publish(g, cn);
+            cn = 0;
+          }
+          stash_at(g, cn) = make_key(s, (uint32_t)sub);
+        } else if (cn < HALF) {
+          (g ? dst[FR - 1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
+        }
         ++cn;
       }
       if (g) {
@@ -485,7 +507,11 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
       }
     }
   });
-  if (!SPLIT) {
+  if constexpr (SPLIT) {  // what is left in the stashes (rows past T have none)
+#pragma unroll
+    for (int g = 0; g < FR; ++g)
+      if (cnt[g] > 0) publish(g, cnt[g]);
+  } else {
 #pragma unroll
     for (int g = 0; g < FR; ++g) {
       const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
@@ -633,10 +659,14 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   if ((e = hipGetLastError()) != hipSuccess) return e;
   theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (splits > 1)
-    pass2_kernel<DT, DH, NW, FR, true><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, splits, cps,
-                                                                theta, cand, count);
-  else
+  if (splits > 1) {
+    // 8-wave blocks of 64-token waves are taken only when every CU gets one, so they never
+    // split (and their LDS leaves no room for the stashes)
+    if constexpr (NW == 8 && FR == 2) return hipErrorInvalidValue;
+    else
+      pass2_kernel<DT, DH, NW, FR, true><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, splits,
+                                                                  cps, theta, cand, count);
+  } else
     pass2_kernel<DT, DH, NW, FR, false><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, 1, nch,
                                                                  theta, cand, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
