@@ -40,7 +40,7 @@
 //  * A batch too small to give every CU a block splits the sub-keys into ranges of whole
 //    chunks, one block per (tile, range, pair): pass 1 writes each range's group maxima,
 //    and pass 2's ranges share a row's candidate list through atomic counts (cleared by
-//    the first range's pass 1 blocks), each lane staging up to eight candidates in LDS
+//    the first range's pass 1 blocks), each lane staging up to 9-16 candidates in LDS
 //    and taking their slots with one atomic.
 #include "kernels.hpp"
 
@@ -406,8 +406,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   constexpr int SROW = 16 * FR + 4;
   // split sub-key ranges: a lane keeps up to STASH of its candidates in LDS and publishes
   // them with one atomic count per stash (an atomic per candidate, waited for before its
-  // store, cost 15-17% of the four scoring kernels at 256-4,096 tokens)
-  constexpr int STASH = SPLIT ? 8 : 1;
+  // store, cost 15-17% of the four scoring kernels at 256-4,096 tokens); STASH fills what
+  // the block's share of the CU's 160 KiB of LDS leaves, up to 16
+  constexpr int LDS_USED = 2 * chunks_per_barrier(NW) * CHUNK * RB + NW * 64 * SROW * 4;
+  constexpr int STASH_FIT = (160 * 1024 / (8 / NW) - LDS_USED) / (FR * NW * 64 * 8);
+  constexpr int STASH = SPLIT ? (STASH_FIT < 16 ? STASH_FIT : 16) : 1;
+  static_assert(STASH >= 1, "no LDS left for the candidate stash");
   __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
   __shared__ uint64_t stash[SPLIT ? STASH * FR * NW * 64 : 1];
