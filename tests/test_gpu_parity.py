@@ -322,13 +322,19 @@ def test_eight_wave_scoring_blocks(case):
     wl.close()
 
 
-@pytest.mark.parametrize("dt,H,T,n_sub", [("f32", 2, 100, 96), ("bf16", 2, 100, 96),
-                                          # 64 heads x 520 tokens over 1,040 sub-keys: 8-wave scoring
-                                          # blocks with a ragged last block
-                                          ("bf16", 64, 520, 1040)])
-def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub):
+@pytest.mark.parametrize("dt,H,T,n_sub,d_q", [("f32", 2, 100, 96, 128), ("bf16", 2, 100, 96, 128),
+                                              # 64 heads x 520 tokens over 1,040 sub-keys: 8-wave scoring
+                                              # blocks with a ragged last block
+                                              ("bf16", 64, 520, 1040, 128),
+                                              # split sub-key ranges: the zero tokens tie k times per lane
+                                              # and range, more than a lane's LDS stash holds (64-, 256-wide
+                                              # bf16 and 64-wide fp32 sub-keys), and every such row
+                                              # overflows into the exhaustive pass
+                                              ("bf16", 4, 100, 1040, 128), ("bf16", 4, 200, 1040, 512),
+                                              ("f32", 4, 100, 1040, 128)])
+def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub, d_q):
     """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=n_sub, k=16, H=H, d_q=128, d_model=64,
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=n_sub, k=16, H=H, d_q=d_q, d_model=64,
                                         d_v=64, T=T, qk_norm=True)
     inp = S.make_inputs(cfg, seed=4)
     sk = inp["subkeys"].copy()
@@ -337,7 +343,7 @@ def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub):
     x = inp["x"].copy()
     x[::5] = 0                          # every fifth token is all zero: every score is 0
     inp["x"] = x
-    say(f"ties {dt} H={H} T={T}")
+    say(f"ties {dt} H={H} T={T} n_sub={n_sub} d_q={d_q}")
     wl = _G().Workload(cfg, seed=4, host_inputs=inp)
     o = run_debug(wl)
     # the oracle on every token of the small cases, on a spread (every fifth token, the zero
