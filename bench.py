@@ -123,9 +123,13 @@ def cpu_baseline(wl, cfg, target_s, max_tokens=None):
         return time.perf_counter() - t0
 
     run(4)
-    per_tok = run(16) / 16
-    n = int(max(16, min(max_tokens or wl.T, target_s / max(per_tok, 1e-9))))
-    log(f"oracle: {per_tok * 1e3:.1f} ms/token estimated, timing {n} tokens")
+    # a call has a fixed part (the sub-keys' normalisation and every step's setup): the
+    # per-token cost is taken from two sizes, so that the timing lands near target_s
+    t16, t64 = run(16), run(64)
+    per_tok = max((t64 - t16) / 48, t64 / 256, 1e-9)
+    fixed = max(t16 - 16 * per_tok, 0.0)
+    n = int(max(16, min(max_tokens or wl.T, (target_s - fixed) / per_tok)))
+    log(f"oracle: {per_tok * 1e3:.1f} ms/token + {fixed:.2f} s per call estimated, timing {n} tokens")
     dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(), **numeric_stack(),
             "sample": f"first {n} of {wl.T} tokens of {cfg.name}, float64 NumPy oracle, {dt:.1f} s" + note}
