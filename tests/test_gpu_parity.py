@@ -295,6 +295,9 @@ def _sample_tokens(T, n=96, tail=24):
          T=600),
     dict(name="eight_waves_dh128", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=1030, k=16, H=16, d_q=256,
          d_model=128, d_v=128, T=3700),
+    # more blocks than CUs (10 token tiles x 32 head halves = 320 blocks), ragged last tile
+    dict(name="eight_waves_320_blocks", dtype="bf16", qk_norm=True, n_sub=1030, k=16, H=16, d_q=256, d_model=128,
+         d_v=128, T=5000),
     dict(name="eight_waves_f32_dh64", dtype="f32", qk_norm=False, n_sub=1050, k=8, H=32, d_q=128, d_model=64, d_v=64,
          T=1600),
     dict(name="eight_waves_f32_dh128", dtype="f32", qk_norm=True, memory_plus=True, n_sub=1100, k=32, H=32, d_q=256,
