@@ -233,13 +233,6 @@ def bruteforce_topk(q1, q2, K1, K2, k: int):
     return topk_order(full, k)
 
 
-def cell_score(q1, q2, K1, K2, t: int, h: int, flat: int) -> float:
-    """Float64 score of one full key for one (token, head)."""
-    n_sub = K1.shape[1]
-    a, b = divmod(int(flat), n_sub)
-    return float(q1[t, h] @ K1[h, a] + q2[t, h] @ K2[h, b])
-
-
 def forward(inp: dict, cfg, rows_of) -> dict:
     """The whole forward for the tokens in ``inp['x']``.
 

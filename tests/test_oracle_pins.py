@@ -58,6 +58,46 @@ def test_hand_rmsnorm():
     np.testing.assert_allclose(O.rmsnorm(np.array(c["v"], float), 0.0), c["expect"], rtol=1e-14)
 
 
+def test_hand_rmsnorm_eps_inside_the_root():
+    c = GOLD["rmsnorm_eps_case"]
+    np.testing.assert_allclose(O.rmsnorm(np.array(c["v"], float), c["eps"]), c["expect"], rtol=1e-14)
+    # the worked closed form: v / sqrt(mean(v^2) + eps) = [3, 4] / sqrt(13)
+    np.testing.assert_allclose(c["expect"], np.array([3.0, 4.0]) / math.sqrt(13.0), rtol=1e-15)
+
+
+class _Cfg:
+    """The fields of a workload that the oracle's forward reads."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(dict(dtype="f32", qk_norm=False, norm_eps=1e-6, memory_plus=False), **kw)
+
+
+def _two_head_forward():
+    c = GOLD["two_head_forward_case"]
+    cfg = _Cfg(H=c["H"], d_q=c["d_q"], k=c["k"])
+    inp = {"x": np.array(c["x"], np.float32), "W_q": np.array(c["W_q"], np.float32),
+           "subkeys": np.array(c["subkeys"], np.float32)}
+    V = np.array(c["values"], dtype=np.float64)
+    return c, O.forward(inp, cfg, lambda r: V[np.asarray(r)])
+
+
+def test_hand_two_head_forward():
+    """Two heads through the whole forward: each head's own W_q columns and sub-key lists,
+    per-head softmax, and one bag over both heads' rows (a row picked twice counts twice)."""
+    c, r = _two_head_forward()
+    assert r["half_idx"][0].tolist() == c["expect_half_idx"]
+    np.testing.assert_allclose(r["half_score"][0], c["expect_half_score"], rtol=0, atol=1e-15)
+    assert r["idx"][0].tolist() == c["expect_idx"]
+    np.testing.assert_allclose(r["score"][0], c["expect_score"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r["w"][0], c["expect_w"], rtol=1e-15)
+    np.testing.assert_allclose(r["out"][0], c["expect_y"], rtol=1e-15)
+    # the stored weights are the logistic of each head's score gap (closed form)
+    for h, gap in enumerate(c["expect_gap"]):
+        np.testing.assert_allclose(c["expect_w"][h], [1 / (1 + math.exp(-gap)), 1 / (1 + math.exp(gap))], rtol=1e-15)
+    s = lambda z: 1 / (1 + math.exp(-z))
+    np.testing.assert_allclose(c["expect_y"], [s(0.5) + s(1.5), s(-0.5) + 2 * s(-1.5)], rtol=1e-15)
+
+
 def test_hand_memory_plus():
     c = GOLD["memory_plus_case"]
     out = O.memory_plus(np.array(c["y"], float), np.array(c["x"], float), np.array(c["W1"], float),
@@ -312,3 +352,28 @@ def test_pins_catch_planted_slips(slip):
             want, _ = O.bruteforce_topk(q1, q2, K1, K2, 4)
             caught |= not np.array_equal(got, want)
     assert caught, f"planted slip {slip} was not caught by the brute-force pin"
+
+
+def _project_query_interleaved(x, W_q, H, d_q):
+    """Slip: head h taken as every H-th column from h (a reshape in the wrong order)."""
+    q = x @ W_q
+    return q.reshape(x.shape[0], d_q, H).transpose(0, 2, 1)
+
+
+def _rmsnorm_eps_outside(v, eps):
+    """Slip: eps added after the square root."""
+    return v / (np.sqrt(np.mean(v * v, axis=-1, keepdims=True)) + eps)
+
+
+@pytest.mark.parametrize("slip,target,pin", [
+    ("head_split_transposed", "project_query", test_hand_two_head_forward),
+    ("eps_outside_the_root", "rmsnorm", test_hand_rmsnorm_eps_inside_the_root),
+])
+def test_pins_catch_planted_oracle_slips(monkeypatch, slip, target, pin):
+    """A wrong head split, or eps outside the square root, planted in the oracle's own step,
+    fails the hand-worked pin of that step."""
+    pin()   # the true oracle passes
+    monkeypatch.setattr(O, target, {"project_query": _project_query_interleaved,
+                                    "rmsnorm": _rmsnorm_eps_outside}[target])
+    with pytest.raises(AssertionError):
+        pin()
