@@ -54,10 +54,29 @@ def gather_bytes(cfg, T):
 
 
 def flops(cfg, T):
-    proj = 2 * T * cfg.d_model * cfg.H * cfg.d_q
+    """Algorithmic FLOPs of the forward's matrix stages, charged to the stage that runs them.
+
+    project: x [W_q | W1] -- with the Memory+ gate, z = x W1 runs in the same GEMM as the query
+    projection; score: both halves of every head against all sub-keys (each score once);
+    gate: (y * silu(z)) W2.
+    """
+    proj = 2 * T * cfg.d_model * (cfg.H * cfg.d_q + (cfg.d_v if cfg.memory_plus else 0))
     score = 2 * T * cfg.H * 2 * cfg.n_sub * cfg.d_h
-    gate = 4 * T * cfg.d_model * cfg.d_v if cfg.memory_plus else 0
+    gate = 2 * T * cfg.d_v * cfg.d_model if cfg.memory_plus else 0
     return proj, score, gate
+
+
+def stage_rates(cfg, T, stages):
+    """TFLOP/s of the matrix stages from their mean times in ms (None for a stage that did
+    not run), and the scoring's fraction of the matrix-core peak for the workload's dtype."""
+    proj, score, gate = flops(cfg, T)
+    ok = lambda ms: ms is not None and ms == ms and ms > 0
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12 if f and ok(ms) else None
+    peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    r = {"score_TFLOPs": tf(score, stages.get("score")), "project_TFLOPs": tf(proj, stages.get("project")),
+         "gate_TFLOPs": tf(gate, stages.get("gate"))}
+    r["score_mfma_frac"] = r["score_TFLOPs"] / peak if r["score_TFLOPs"] else None
+    return r
 
 
 def counter_traffic(counters_file=COUNTERS_FILE):
@@ -706,7 +725,6 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--chunks", type=int, default=0, help="token chunks the forward is pipelined over (0 = automatic)")
     ap.add_argument("--uniform", action="store_true",
                     help="time the gather alone with uniform random indices over the workload's table")
     ap.add_argument("--shard-columns", type=int, default=0,
@@ -764,7 +782,6 @@ def main():
     else:
         wl = Workload(cfg, seed=a.seed)
     h = wl.pkm.handle
-    P.pkm_set_pipeline_chunks(h, a.chunks)
     x = wl.dev["x"]
     out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
     stream = torch.cuda.current_stream()
@@ -813,12 +830,10 @@ def main():
         P.pkm_forward(h, x, T, out, stream=stream)
     torch.cuda.synchronize()
     stages = {n: sum(P.pkm_stage_times(h, n, n_bd)) / n_bd for n in P.STAGES}
+    stages = {n: (v if v == v else None) for n, v in stages.items()}   # NaN: the stage did not run
     rows_b, alg_b = gather_bytes(cfg, T)
     achieved = alg_b / (g_ms * 1e-3) / 1e9
-    proj, score, gate = flops(cfg, T)
-    tf = lambda f, ms: f / (ms * 1e-3) / 1e12 if ms > 0 else None
-    peak_t = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
-    log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+    log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items() if v is not None))
 
     cpu = None
     if not a.no_cpu_baseline and not host:
@@ -843,7 +858,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights; value table generated on the GPU)",
-        "config": {"workload": cfg.name, "tokens": T, "pipeline_chunks": a.chunks or "auto", "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
+        "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
                    "n_sub": cfg.n_sub, "n_keys": cfg.N, "d_value": cfg.d_v, "k": cfg.k, "qk_norm": cfg.qk_norm,
                    "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30,
                    "table_memory": "host (pinned)" if host else "device"},
@@ -858,10 +873,7 @@ def main():
         "stages_ms": stages,
         "stages_note": f"from {n_bd} forwards after the timed steps with every stage's events recorded (the events "
                        "slow a forward by about 2%; the timed steps record the gather's alone)",
-        "score_TFLOPs": tf(score, stages["score"]),
-        "score_mfma_frac": (tf(score, stages["score"]) or 0) / peak_t,
-        "project_TFLOPs": tf(proj, stages["project"]),
-        "gate_TFLOPs": tf(gate, stages["gate1"] + stages["gate2"]) if gate else None,
+        **stage_rates(cfg, T, stages),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -76,7 +76,8 @@ typedef struct {
   int32_t qk_norm;      /* 0 or 1: RMSNorm of the query (before the split) and of sub-key rows */
   int32_t memory_plus;  /* 0: out = y [T, d_value]; 1: gated out [T, d_model] */
   float norm_eps;       /* RMSNorm epsilon in [0, 1] (1e-6 in the shipped workloads) */
-  int64_t max_tokens;   /* largest T a forward may take, 1..2^24; sizes the workspace */
+  int64_t max_tokens;   /* largest T a forward may take, 1..2^24 with max_tokens * n_heads <= 2^24;
+                           sizes the workspace */
 } pkm_config;
 
 /* Stage ids for the optional per-stage timing. */
@@ -86,10 +87,9 @@ enum {
   PKM_STAGE_SCORE = 2,    /* sub-key scoring fused with the per-half top-k */
   PKM_STAGE_COMBINE = 3,  /* k x k combine, final top-k, softmax */
   PKM_STAGE_GATHER = 4,   /* weighted EmbeddingBag over the value table (Memory+: with y * silu(z)) */
-  PKM_STAGE_GATE1 = 5,    /* empty: z = x W1 is computed with the projection */
-  PKM_STAGE_GATE2 = 6,    /* (.) W2 (Memory+ only) */
-  PKM_STAGE_TOTAL = 7,    /* the whole forward */
-  PKM_NUM_STAGES = 8
+  PKM_STAGE_GATE = 5,     /* (y * silu(z)) W2 (Memory+ only; z = x W1 comes with the projection) */
+  PKM_STAGE_TOTAL = 6,    /* the whole forward */
+  PKM_NUM_STAGES = 7
 };
 
 typedef struct pkm_handle pkm_handle; /* opaque */
@@ -139,14 +139,7 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
                pkm_handle** out);
 
 /* The forward for T tokens (0 <= T <= max_tokens; T = 0 enqueues nothing).
- * By default every stage runs in order on `stream`.  With
- * pkm_set_pipeline_chunks(h, c > 1) the tokens are split into c chunks that are
- * pipelined over two internal streams of the handle (created at pkm_create,
- * default priority): one runs the matrix-core work (selection of every chunk,
- * then the gate of a chunk once its gather is done), the other the gathers, so
- * a chunk's HBM-bound gather runs beside its neighbours' matrix work.  Both
- * streams fork from `stream` after the work already queued there and join back
- * into it.  The results are bitwise the same for every chunk count.
+ * Every stage runs in order on `stream`.
  *   x        [T, d_model] dtype
  *   out      [T, d_model] dtype if memory_plus, else [T, d_value] dtype
  *   idx_out  [T, H, k] int32, optional (NULL): final flat indices
@@ -178,15 +171,13 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
                       const int32_t* idx, const float* w, int64_t n_bags, int32_t bag_size, float* y,
                       void* stream);
 
-/* Per-stage timing with HIP events recorded on the stream each stage runs on.
- * pkm_enable_stage_timing keeps the last `max_records` forwards (0 turns it off);
- * it allocates the events, so call it outside any timed or captured region.
- * pkm_stage_times waits for the recorded events, writes up to `n` durations in
- * milliseconds of stage `stage` (PKM_STAGE_*) for the recorded forwards, oldest
- * first, and returns how many it wrote (or a negative error code).  A stage's
- * duration is the sum over the forward's chunks of the time between the events
- * around that stage's launches; stages of different chunks can overlap, so
- * the stage times may add up to more than PKM_STAGE_TOTAL. */
+/* Per-stage timing with HIP events recorded on the forward's stream around each
+ * stage's launches.  pkm_enable_stage_timing keeps the last `max_records` forwards
+ * (0 turns it off); it allocates the events, so call it outside any timed or
+ * captured region.  pkm_stage_times waits for the recorded events, writes up to `n`
+ * durations in milliseconds of stage `stage` (PKM_STAGE_*) for the recorded
+ * forwards, oldest first, and returns how many it wrote (or a negative error code).
+ * PKM_STAGE_GATE reads NaN for a handle without the Memory+ gate. */
 int pkm_enable_stage_timing(pkm_handle* h, int32_t max_records);
 int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n);
 
@@ -196,10 +187,6 @@ int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n);
  * needs.  A stage left out of a recorded forward reads as NaN in pkm_stage_times.
  * Returns PKM_EINVAL for bits at or above PKM_NUM_STAGES. */
 int pkm_set_stage_timing_mask(pkm_handle* h, uint32_t mask);
-
-/* Number of token chunks pkm_forward pipelines a batch over: 0 (the default) or
- * 1 runs every stage on the caller's stream in order; 2..8 that many chunks. */
-int pkm_set_pipeline_chunks(pkm_handle* h, int32_t chunks);
 
 /* Release the handle's host state and events (the workspace stays the caller's). */
 int pkm_destroy(pkm_handle* h);

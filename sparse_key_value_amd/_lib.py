@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkm.so")
 
 PKM_OK, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_EHIP = 0, -1, -2, -3, -4
 PKM_F32, PKM_BF16 = 0, 1
-STAGES = ["project", "qnorm", "score", "combine", "gather", "gate1", "gate2", "total"]
+STAGES = ["project", "qnorm", "score", "combine", "gather", "gate", "total"]
 STAGE_ID = {n: i for i, n in enumerate(STAGES)}
 
 if not os.path.exists(LIB_PATH):
@@ -71,7 +71,6 @@ _sig = {
     "pkm_enable_stage_timing": (ctypes.c_int, [_vp, _i32]),
     "pkm_stage_times": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_float), _i32]),
     "pkm_set_stage_timing_mask": (ctypes.c_int, [_vp, ctypes.c_uint32]),
-    "pkm_set_pipeline_chunks": (ctypes.c_int, [_vp, _i32]),
     "pkm_destroy": (ctypes.c_int, [_vp]),
     "pkm_last_error": (ctypes.c_char_p, []),
     "engram_hash": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -186,10 +185,6 @@ def pkm_stage_times(h: int, stage, n: int) -> list[float]:
     buf = (ctypes.c_float * max(1, n))()
     got = _check(_lib.pkm_stage_times(h, sid, buf, n), "pkm_stage_times")
     return [buf[i] for i in range(got)]
-
-
-def pkm_set_pipeline_chunks(h: int, chunks: int) -> None:
-    _check(_lib.pkm_set_pipeline_chunks(h, chunks), "pkm_set_pipeline_chunks")
 
 
 def pkm_destroy(h: int) -> None:

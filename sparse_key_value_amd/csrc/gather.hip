@@ -49,9 +49,8 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
                                            int64_t z_ld);
 
 // Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bags blockIdx.x*BPB+g,
-// then + gridDim.x*BPB, ... (one block per group of bags, or, beside other kernels, a
-// persistent grid of two blocks per CU), and the 16-byte column slices
-// [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of their rows.
+// then + gridDim.x*BPB, ... (one block per group of bags up to a grid cap), and the
+// 16-byte column slices [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of their rows.
 template <int EB, int UNROLL, bool UNIFORM, bool GATE>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, int64_t n_rows,
                                                      int row_vecs, int tpr, int bags_per_block,
@@ -148,19 +147,11 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
 
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s,
-                         const float* z, bool persistent, int64_t z_ld) {
+                         const float* z, int64_t z_ld) {
   if (n_bags == 0) return hipSuccess;
-  // persistent: two blocks per CU loop over the bags, leaving room on every CU for kernels
-  // running beside the gather; otherwise one block per group of bags (on its own the
-  // gather is about 2% faster that way)
-  static int cu_blocks = 0;
-  if (cu_blocks == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cu_blocks = 2 * cus;
-  }
-  const int64_t max_blocks = persistent ? cu_blocks : ((int64_t)1 << 31) - 1;
+  // one block per group of bags; a grid of at most 2^22 blocks (of <= 256 lanes: far below
+  // the 2^32 work-items of one dispatch) loops over larger bag counts
+  constexpr int64_t max_blocks = (int64_t)1 << 22;
   const int eb = dtype == DT_BF16 ? 2 : 4;
   const int row_vecs = (int)((int64_t)dim * eb / 16);
   if (z_ld == 0) z_ld = dim;

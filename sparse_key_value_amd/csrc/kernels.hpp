@@ -40,10 +40,10 @@ hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T,
                           int32_t* half_idx, float* half_score, int32_t* idx, float* score, float* w, hipStream_t s);
 // Weighted EmbeddingBag: y[b] = sum_j w[b,j] table[idx[b,j]]; y fp32 or dtype.  With z
 // (fp32, row b at z + b * z_ld, dim elements) it writes g[b] = y[b] * silu(z[b]) in dtype
-// instead.  persistent: a grid of two blocks per CU (for running beside other kernels).
+// instead.
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s,
-                         const float* z = nullptr, bool persistent = false, int64_t z_ld = 0);
+                         const float* z = nullptr, int64_t z_ld = 0);
 
 hipError_t launch_convert_f32(const float* in, void* out, int64_t n, int dtype, hipStream_t s);
 

@@ -50,6 +50,9 @@ inline std::string check_config(const pkm_config* c) {
   if (c->memory_plus != 0 && c->memory_plus != 1) return "memory_plus must be 0 or 1";
   if (!(c->norm_eps >= 0.0f) || c->norm_eps > 1.0f) return "norm_eps must be in [0, 1]";
   if (c->max_tokens < 1 || c->max_tokens > ((int64_t)1 << 24)) return "max_tokens must be in [1, 2^24]";
+  // the selection kernels run one wave per (token, head, half): 2^25 rows of 64 lanes keep a
+  // launch within the 2^32 work-items of one dispatch
+  if (c->max_tokens * c->n_heads > ((int64_t)1 << 24)) return "max_tokens * n_heads must be <= 2^24";
   return "";
 }
 

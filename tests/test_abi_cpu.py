@@ -74,6 +74,8 @@ def test_workspace_size_matches_layout(P):
     (dict(d_value=12), "d_value"),
     (dict(qk_norm=2), "qk_norm"),
     (dict(max_tokens=0), "max_tokens"),
+    (dict(max_tokens=1 << 25), "max_tokens"),
+    (dict(max_tokens=1 << 23, n_heads=4), "max_tokens * n_heads"),   # 2^25 selection rows of 64 lanes
 ])
 def test_invalid_configs_are_rejected(P, bad, needle):
     c = _cfg(P)

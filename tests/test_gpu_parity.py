@@ -513,35 +513,6 @@ def test_combine_rounding_tie_takes_exhaustive_path():
     pk.close()
 
 
-@pytest.mark.parametrize("memory_plus,shape", [
-    (False, dict(n_sub=128, T=1000)), (True, dict(n_sub=128, T=1000)),
-    # the two MFMA passes: 8-wave blocks for the whole batch, 4-wave ones per chunk
-    (True, dict(n_sub=1100, T=1500, H=64)),
-])
-def test_pipelined_chunks_match_single_stream(memory_plus, shape):
-    """Pipelining over token chunks (two internal streams) gives bitwise the same forward."""
-    import sparse_key_value_amd as P
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name="chunks", d_v=256, d_model=256, memory_plus=memory_plus, **shape)
-    say(f"pipelined chunks memory_plus={memory_plus} {shape}")
-    wl = _G().Workload(cfg, seed=12)
-    res = {}
-    for chunks in (1, 3, 8):
-        P.pkm_set_pipeline_chunks(wl.pkm.handle, chunks)
-        out = torch.empty((wl.T, cfg.d_out), dtype=torch.bfloat16, device="cuda")
-        idx = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda")
-        w = torch.empty((wl.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda")
-        P.pkm_forward(wl.pkm.handle, wl.dev["x"], wl.T, out, idx, w)
-        torch.cuda.synchronize()
-        res[chunks] = (out.view(torch.int16).cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy())
-    for chunks in (3, 8):
-        for a, b in zip(res[1], res[chunks]):
-            np.testing.assert_array_equal(a, b)
-    P.pkm_set_pipeline_chunks(wl.pkm.handle, 0)
-    o = run_debug(wl)
-    full_check(wl, o, rows=None if cfg.H < 64 else _sample_tokens(wl.T))
-    wl.close()
-
-
 def test_candidate_overflow_takes_exhaustive_path():
     """Scores rising with the sub-key index make the group-maximum bound loose.
 
