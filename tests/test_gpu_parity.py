@@ -56,8 +56,24 @@ def check_order_valid(idx, score, what):
     assert (np.diff(i, axis=1)[eq] > 0).all(), f"{what}: equal scores not in ascending index order"
 
 
-def full_check(wl, o, rows=None, strict_e2e=None):
-    """Stage-wise and end-to-end parity of one debug forward `o` (numpy dict) for token subset `rows`."""
+def table_rows(wl, needed, n_check=256):
+    """``rows_of`` over the value rows in `needed`, copied out of the device table in one gather.
+
+    The table is an input: the seeded device generator filled it.  A random sample of the
+    copied rows is compared bitwise with the host generator's rows before they are used.
+    """
+    G = _G()
+    uniq = np.unique(np.asarray(needed, dtype=np.int64).ravel())
+    host = G.to_host(wl.values.index_select(0, torch.from_numpy(uniq).to(wl.values.device)))
+    pick = np.random.default_rng(len(uniq)).choice(len(uniq), min(n_check, len(uniq)), replace=False)
+    np.testing.assert_array_equal(host[pick], wl.host_rows(uniq[pick]))
+    dt = wl.cfg.dtype
+    return lambda r: O.to_f64(host[np.searchsorted(uniq, np.asarray(r, dtype=np.int64))], dt)
+
+
+def full_check(wl, o, rows=None, e2e_rows=None):
+    """Stage-wise parity of one debug forward `o` (numpy dict) on the token subset `rows`, and
+    end-to-end parity on `e2e_rows` (a subset of `rows`; default: all of them)."""
     cfg, dt = wl.cfg, wl.cfg.dtype
     G = _G()
     tok = np.arange(wl.T) if rows is None else np.asarray(rows)
@@ -103,7 +119,7 @@ def full_check(wl, o, rows=None, strict_e2e=None):
     np.testing.assert_allclose(gw, O.softmax(gsc.astype(np.float64)), rtol=2e-6, atol=1e-7)
 
     # a7 stage-wise: oracle gather of the GPU's indices and weights
-    rows_of = lambda r: O.to_f64(wl.host_rows(r), dt)
+    rows_of = table_rows(wl, gidx)
     y_st = O.weighted_bag(rows_of, gidx.astype(np.int64), gw.astype(np.float64))
     PAR.check_rows(o["y"][tok], y_st, 1e-4, "gather (stage)")
 
@@ -114,6 +130,10 @@ def full_check(wl, o, rows=None, strict_e2e=None):
         PAR.check_rows(O.to_f64(o["out"][tok], dt), out_st, PAR.TOL[dt], "Memory+ gate (stage)")
 
     # end to end from x: the oracle's own q, khat; indices under the near-tie rule, outputs re-evaluated
+    if e2e_rows is not None:
+        sub = np.searchsorted(tok, np.asarray(e2e_rows))
+        assert (tok[sub] == np.asarray(e2e_rows)).all(), "e2e_rows must be a subset of rows"
+        tok, x, q1o, q2o, gidx = tok[sub], x[sub], q1o[sub], q2o[sub], gidx[sub]
     ora = O.select(q1o, q2o, K1o, K2o, cfg.k)
     tau_scale = 1.0 if dt == "f32" else 100.0   # bf16: qhat may round the other way (about 4e-3 in a score)
     old = PAR.TAU
@@ -127,8 +147,8 @@ def full_check(wl, o, rows=None, strict_e2e=None):
     out_ref = (O.memory_plus(y_ref, x, O.to_f64(wl.inp["W1"], dt), O.to_f64(wl.inp["W2"], dt), dt)
                if cfg.memory_plus else y_ref)
     rel = PAR.check_rows(O.to_f64(o["out"][tok], dt), out_ref, PAR.TOL[dt], "output (end to end)")
-    say(f"{cfg.name}: tokens {len(tok)}, excused per-half {ex_h}, final {ex_f}, end-to-end {ex_e}, "
-        f"worst out rel err {rel:.2e}")
+    say(f"{cfg.name}: stage-wise on {len(gsc)} tokens: excused per-half {ex_h}, final {ex_f}; end to end on "
+        f"{len(tok)} tokens: excused {ex_e}, worst out rel err {rel:.2e}")
     return ex_e
 
 
@@ -447,10 +467,22 @@ def _sample_rows(T, n=40, seed=1):
     return rows
 
 
+def _benchmark_block_rows(T, n_random=256, seed=1):
+    """The first 512-token scoring block (both groups of four waves), the last 256 tokens (the end
+    of the last block) and random tokens: 1,024 tokens in all at 16,384 tokens."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(min(512, T)), np.arange(max(0, T - 256), T),
+                                     rng.choice(T, n_random, replace=False)]))
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["memplus_16m_bf16", "memplus_64m_bf16", "pkm_1m_bf16"])
-def test_full_size_sampled_tokens(name):
-    """The headline, the largest and the 1M-key workload at full size, as the benchmark runs
-    them (the 1M-key batch takes the 32-token waves of the scoring passes)."""
+def test_full_size_as_benchmarked(name):
+    """The headline, the largest and the 1M-key workload at full size, run exactly as the
+    benchmark runs them.  Properties on every token; the oracle on 1,024 tokens of the 16M- and
+    64M-key batches (a whole 512-token scoring block, the end of the last block and random
+    tokens), and stage-wise on all 8,192 tokens of the 1M-key batch (which takes the 32-token
+    waves of the scoring passes) with end to end on a sample."""
     cfg = CONFIGS[name]
     say(f"{name}: filling {cfg.N} x {cfg.d_v} value table on the GPU")
     wl = _G().Workload(cfg)
@@ -460,9 +492,12 @@ def test_full_size_sampled_tokens(name):
     assert (o["idx"] >= 0).all() and (o["idx"] < cfg.N).all()
     np.testing.assert_allclose(o["w"].sum(axis=-1), 1.0, atol=1e-5)
     check_order_valid(o["idx"], o["score"], "final lists (all tokens)")
-    rows = _sample_rows(cfg.T)
-    say(f"{name}: oracle on {len(rows)} sampled tokens")
-    full_check(wl, o, rows=rows)
+    if cfg.T <= 8192:
+        rows, e2e = None, _sample_rows(cfg.T)
+    else:
+        rows, e2e = _benchmark_block_rows(cfg.T), None
+    say(f"{name}: oracle stage-wise on {cfg.T if rows is None else len(rows)} tokens")
+    full_check(wl, o, rows=rows, e2e_rows=e2e)
     wl.close()
     del wl, o
     gc.collect()
