@@ -45,7 +45,7 @@ typedef struct {
   const int32_t* idx;     /* [n_bags, bag_size] */
   const float* w;         /* [n_bags, bag_size] */
   const float* dy;        /* [n_bags, dim] fp32, 16-byte aligned */
-  int64_t n_bags;         /* n_bags * bag_size < 2^31 */
+  int64_t n_bags;         /* < 2^24, and n_bags * bag_size < 2^31 */
   int32_t bag_size;       /* 1 .. 2048 */
   float* dw;              /* [n_bags, bag_size] or NULL */
   float* ds;              /* [n_bags, bag_size] or NULL (needs the weights to be a group softmax) */

@@ -482,7 +482,9 @@ int sort_space(int64_t n, int64_t n_rows, SortSpace& S) {
 
 int check_sizes(int64_t n_bags, int32_t bag_size, int64_t n_rows) {
   using pkm_abi::fail;
-  if (n_bags < 0) return fail(PKM_EINVAL, "n_bags must be >= 0");
+  // one block per bag (dw and the update pass): 2^24 blocks of <= 256 lanes keep a launch within
+  // the 2^32 work-items of one dispatch
+  if (n_bags < 0 || n_bags >= ((int64_t)1 << 24)) return fail(PKM_EINVAL, "n_bags must be in [0, 2^24)");
   if (bag_size < 1 || bag_size > MAX_BAG) return fail(PKM_EINVAL, "bag_size must be in [1, 2048]");
   if (n_bags * bag_size >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_bags * bag_size must be < 2^31");
   if (n_rows < 1 || n_rows >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_rows must be in [1, 2^31)");
@@ -638,9 +640,10 @@ int pkm_bag_backward(const pkm_bag_backward_args* a, void* workspace, size_t ws_
   tb = S.temp_bytes;
   PKM_HIP(rocprim::exclusive_scan(ws + S.temp, tb, (const uint32_t*)U(S.counts), U(S.offsets), 0u, (size_t)n,
                                   rocprim::plus<uint32_t>(), s));
-  // one block per possible run (at most n): a block's rows form a chain of dependent loads,
-  // so many resident blocks are what hides the latency; blocks past the run count exit
-  const dim3 grid((unsigned)n);
+  // one block per possible run (at most n, the grid capped at 2^22 blocks, which then loop): a
+  // block's rows form a chain of dependent loads, so many resident blocks are what hides the
+  // latency; blocks past the run count exit
+  const dim3 grid((unsigned)(n < ((int64_t)1 << 22) ? n : ((int64_t)1 << 22)));
 #define PKM_GRAD(EBV)                                                                                          \
   PKM_LAUNCH((pkm::bag_grad_kernel<EBV><<<grid, 256, 0, s>>>(U(S.unique), U(S.counts), U(S.offsets), U(S.runs), \
                                                              U(S.vals_sorted), a->w, a->dy, a->bag_size, a->dim, \

@@ -201,7 +201,9 @@ def test_bag_backward_argument_errors_before_any_device_call(P):
     assert lib.pkm_bag_backward_workspace_size(-1, 4, 100) == 0
     assert lib.pkm_bag_backward_workspace_size(10, 0, 100) == 0 and "bag_size" in P.pkm_last_error()
     assert lib.pkm_bag_backward_workspace_size(10, 4096, 100) == 0
-    assert lib.pkm_bag_backward_workspace_size(1 << 30, 4, 100) == 0 and "2^31" in P.pkm_last_error()
+    assert lib.pkm_bag_backward_workspace_size(1 << 23, 512, 100) == 0 and "2^31" in P.pkm_last_error()
+    # one block per bag: 2^24 bags of 256 lanes would exceed a dispatch's 2^32 work-items
+    assert lib.pkm_bag_backward_workspace_size(1 << 24, 1, 100) == 0 and "2^24" in P.pkm_last_error()
     assert lib.pkm_bag_backward_workspace_size(10, 4, 0) == 0 and "n_rows" in P.pkm_last_error()
 
     def args(**kw):

@@ -467,7 +467,7 @@ def _sample_rows(T, n=40, seed=1):
     return rows
 
 
-def _benchmark_block_rows(T, n_random=256, seed=1):
+def _benchmark_block_rows(T, n_random=272, seed=1):
     """The first 512-token scoring block (both groups of four waves), the last 256 tokens (the end
     of the last block) and random tokens: 1,024 tokens in all at 16,384 tokens."""
     rng = np.random.default_rng(seed)
