@@ -70,6 +70,22 @@ size_t pkm_bag_backward_workspace_size(int64_t n_bags, int32_t bag_size, int64_t
  * call until the stream reaches its end. */
 int pkm_bag_backward(const pkm_bag_backward_args* args, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the fixed sort buffers pkm_bag_backward_noalloc uses: enough for 2^21 entries
+ * (n_bags * bag_size; e.g. 16,384 tokens x 4 heads x k = 32) over any table. */
+#define PKM_BAG_BACKWARD_NOALLOC_BYTES ((size_t)96 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving or training loops, harnesses that forbid hipMalloc): pkm_bag_backward without a
+ * workspace argument.  Its sort buffers are a fixed device array of
+ * PKM_BAG_BACKWARD_NOALLOC_BYTES that the library holds on every GPU it runs on until the
+ * process ends; the call itself allocates nothing.  Sizes whose
+ * pkm_bag_backward_workspace_size exceeds that array are refused with PKM_EWORKSPACE before
+ * anything is enqueued (pkm_bag_backward with a caller workspace takes any size).  Results
+ * are bitwise those of pkm_bag_backward.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams or from different threads) race, so
+ * the caller orders them (e.g. one stream per GPU). */
+int pkm_bag_backward_noalloc(const pkm_bag_backward_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkm.so")
 
 PKM_OK, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_EHIP = 0, -1, -2, -3, -4
 PKM_F32, PKM_BF16 = 0, 1
+PKM_BAG_BACKWARD_NOALLOC_BYTES = 96 << 20   # the fixed sort buffers of pkm_bag_backward_noalloc (bag_backward.h)
 STAGES = ["project", "qnorm", "score", "combine", "gather", "gate", "total"]
 STAGE_ID = {n: i for i, n in enumerate(STAGES)}
 
@@ -80,6 +81,7 @@ _sig = {
     "engram_forward_staged": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
     "pkm_bag_backward_workspace_size": (_sz, [_i64, _i32, _i64]),
     "pkm_bag_backward": (ctypes.c_int, [ctypes.POINTER(pkm_bag_backward_args), _vp, _sz, _vp]),
+    "pkm_bag_backward_noalloc": (ctypes.c_int, [ctypes.POINTER(pkm_bag_backward_args), _vp]),
     "ma_fold_table": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
     "ma_values": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -247,3 +249,13 @@ def pkm_bag_backward(table, n_rows: int, dim: int, dtype, idx, w, dy, n_bags: in
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pkm_bag_backward(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)), "pkm_bag_backward")
+
+
+def pkm_bag_backward_noalloc(table, n_rows: int, dim: int, dtype, idx, w, dy, n_bags: int, bag_size: int, dw=None,
+                             ds=None, softmax_group: int = 0, rows=None, grad=None, n_unique=None,
+                             update: bool = False, lr: float = 0.0, stream=None) -> None:
+    dt = {"f32": PKM_F32, "bf16": PKM_BF16}.get(dtype, dtype)
+    a = pkm_bag_backward_args(_ptr(table), int(n_rows), int(dim), int(dt), _ptr(idx), _ptr(w), _ptr(dy), int(n_bags),
+                              int(bag_size), _ptr(dw), _ptr(ds), int(softmax_group), _ptr(rows), _ptr(grad),
+                              _ptr(n_unique), int(bool(update)), float(lr))
+    _check(_lib.pkm_bag_backward_noalloc(ctypes.byref(a), _stream(stream)), "pkm_bag_backward_noalloc")

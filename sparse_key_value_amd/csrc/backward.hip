@@ -24,6 +24,8 @@
 #include <rocprim/device/device_run_length_encode.hpp>
 #include <rocprim/device/device_scan.hpp>
 
+#include <mutex>
+
 #include "../../include/bag_backward.h"
 #include "abi.hpp"
 #include "common.hpp"
@@ -547,6 +549,145 @@ int launch_update(const pkm_bag_backward_args* a, uint8_t* table, int slices, co
   return PKM_OK;
 }
 
+// Sort buffers for callers that cannot allocate device memory (pkm_bag_backward_noalloc):
+// a fixed array that every GPU the library runs on holds until the process ends.  In host
+// code the name `scratch` stands for the array but is not its device address: kernels and
+// copies are given the address hipGetSymbolAddress returns for the current device, which
+// is looked up once per device and kept.  Every call on one GPU shares that GPU's array.
+// Nothing in it has to start at zero: the kernels and the rocPRIM primitives write every
+// byte of it they later read.
+static __device__ __align__(256) uint8_t scratch[PKM_BAG_BACKWARD_NOALLOC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch` (looked up on the device's first call).
+int scratch_address(void** out) {
+  using pkm_abi::fail;
+  int dev = 0;
+  PKM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(PKM_EUNSUPPORTED, "device index %d is not below %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKM_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKM_OK;
+}
+
+// The backward on `s`.  The sort buffers are the caller's workspace (ws, ws_bytes), or, with
+// `fixed`, the library's scratch array of ws_bytes on the current device.  Every argument and
+// size is checked before anything is enqueued.
+int run_bag_backward(const pkm_bag_backward_args* a, uint8_t* ws, size_t ws_bytes, bool fixed, hipStream_t s) {
+  using pkm_abi::fail;
+  if (!a) return fail(PKM_EINVAL, "args is NULL");
+  int rc = check_sizes(a->n_bags, a->bag_size, a->n_rows);
+  if (rc != PKM_OK) return rc;
+  if (a->dtype != PKM_F32 && a->dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
+  const int eb = a->dtype == PKM_BF16 ? 2 : 4;
+  if (a->dim < 1 || a->dim > 2048 || ((int64_t)a->dim * eb) % 16 != 0)
+    return fail(PKM_EINVAL, "dim must be in [1, 2048] with dim * sizeof(dtype) a multiple of 16");
+  if (a->ds && (a->softmax_group < 1 || a->bag_size % a->softmax_group != 0))
+    return fail(PKM_EINVAL, "softmax_group must divide bag_size");
+  if (a->update != 0 && a->update != 1) return fail(PKM_EINVAL, "update must be 0 or 1");
+  if (a->n_bags == 0) return PKM_OK;
+  if (!a->table || !a->idx || !a->w || !a->dy) return fail(PKM_EINVAL, "table, idx, w and dy must not be NULL");
+  if ((((uintptr_t)a->table | (uintptr_t)a->dy | (uintptr_t)a->grad) & 15) != 0)
+    return fail(PKM_EINVAL, "table, dy and grad must be 16-byte aligned");
+  const bool need_sort = a->rows || a->grad || a->n_unique || a->update;
+  if ((rc = device_ok()) != PKM_OK) return rc;
+  const void* tview = nullptr;
+  if ((rc = pkm_abi::device_view(a->table, "table", &tview)) != PKM_OK) return rc;
+  const int slices = a->dim * eb / 16;
+  const int64_t n = a->n_bags * a->bag_size;
+  SortSpace S;
+  if (need_sort) {
+    if ((rc = sort_space(n, a->n_rows, S)) != PKM_OK) return rc;
+    if (fixed) {
+      if (S.total > ws_bytes)
+        return fail(PKM_EWORKSPACE, "these sizes need %zu bytes of sort buffers, more than the library's fixed %zu "
+                    "(pkm_bag_backward with a workspace takes any size)", S.total, ws_bytes);
+      void* p = nullptr;
+      if ((rc = scratch_address(&p)) != PKM_OK) return rc;
+      ws = (uint8_t*)p;
+    } else {
+      if (!ws || ws_bytes < S.total)
+        return fail(PKM_EWORKSPACE, "workspace has %zu bytes, these sizes need %zu", ws ? ws_bytes : (size_t)0,
+                    S.total);
+      if (((uintptr_t)ws & 255) != 0) return fail(PKM_EINVAL, "workspace must be 256-byte aligned");
+      if ((rc = pkm_abi::require_device(ws, "workspace")) != PKM_OK) return rc;
+    }
+  }
+
+  // without the update, dw and ds come from their own pass over the rows; with it, from
+  // the rows the update reads (before writing them)
+  if ((a->dw || a->ds) && !a->update) {
+    if (a->dtype == PKM_BF16) rc = launch_dw<2>(a, (const uint8_t*)tview, slices, s);
+    else rc = launch_dw<4>(a, (const uint8_t*)tview, slices, s);
+    if (rc != PKM_OK) return rc;
+  }
+  if (!need_sort) return PKM_OK;
+  auto U = [&](size_t o) { return (uint32_t*)(ws + o); };
+  PKM_LAUNCH((bag_keys_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a->idx, n, a->n_rows,
+                                                                                   U(S.keys), U(S.vals)),
+              hipGetLastError()));
+  size_t tb = S.temp_bytes;
+  PKM_HIP(rocprim::radix_sort_pairs(ws + S.temp, tb, (const uint32_t*)U(S.keys), U(S.keys_sorted),
+                                    (const uint32_t*)U(S.vals), U(S.vals_sorted), (uint32_t)n, 0u,
+                                    key_bits(a->n_rows), s));
+  if (a->update) {
+    // roles into the unsorted-key buffer and, when only ds is asked for, dw into the
+    // unsorted-position buffer: the sort has finished with both
+    int32_t* role = (int32_t*)U(S.keys);
+    float* dwp = a->dw ? a->dw : (a->ds ? (float*)U(S.vals) : nullptr);
+    const uint32_t* ks = U(S.keys_sorted);
+    const uint32_t* ps = U(S.vals_sorted);
+    PKM_LAUNCH((bag_owner_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(ks, ps, n, (uint32_t)a->n_rows,
+                                                                                      role, dwp),
+                hipGetLastError()));
+    if (a->dtype == PKM_BF16) rc = launch_update<2>(a, (uint8_t*)tview, slices, role, ks, ps, dwp, s);
+    else rc = launch_update<4>(a, (uint8_t*)tview, slices, role, ks, ps, dwp, s);
+    if (rc != PKM_OK) return rc;
+    if (a->ds)
+      PKM_LAUNCH((bag_ds_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a->w, dwp, n, a->softmax_group,
+                                                                                     a->ds),
+                  hipGetLastError()));
+  }
+  if (!a->rows && !a->grad && !a->n_unique) return PKM_OK;
+  tb = S.temp_bytes;
+  PKM_HIP(rocprim::run_length_encode(ws + S.temp, tb, (const uint32_t*)U(S.keys_sorted), (unsigned)n, U(S.unique),
+                                     U(S.counts), U(S.runs), s));
+  if (!a->grad) {
+    PKM_LAUNCH((bag_rows_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(
+                   U(S.unique), U(S.runs), n, (uint32_t)a->n_rows, a->rows, a->n_unique),
+                hipGetLastError()));
+    return PKM_OK;
+  }
+  tb = S.temp_bytes;
+  PKM_HIP(rocprim::exclusive_scan(ws + S.temp, tb, (const uint32_t*)U(S.counts), U(S.offsets), 0u, (size_t)n,
+                                  rocprim::plus<uint32_t>(), s));
+  // one block per possible run (at most n, the grid capped at 2^22 blocks, which then loop): a
+  // block's rows form a chain of dependent loads, so many resident blocks are what hides the
+  // latency; blocks past the run count exit
+  const dim3 grid((unsigned)(n < ((int64_t)1 << 22) ? n : ((int64_t)1 << 22)));
+#define PKM_GRAD(EBV)                                                                                          \
+  PKM_LAUNCH((bag_grad_kernel<EBV><<<grid, 256, 0, s>>>(U(S.unique), U(S.counts), U(S.offsets), U(S.runs), \
+                                                             U(S.vals_sorted), a->w, a->dy, a->bag_size, a->dim, \
+                                                             slices, (uint32_t)a->n_rows, a->rows, a->grad,      \
+                                                             a->n_unique),                                       \
+              hipGetLastError()))
+  if (a->dtype == PKM_BF16) PKM_GRAD(2);
+  else PKM_GRAD(4);
+#undef PKM_GRAD
+  return PKM_OK;
+}
+
+
 }  // namespace
 
 }  // namespace pkm
@@ -561,99 +702,11 @@ size_t pkm_bag_backward_workspace_size(int64_t n_bags, int32_t bag_size, int64_t
 }
 
 int pkm_bag_backward(const pkm_bag_backward_args* a, void* workspace, size_t ws_bytes, void* stream) {
-  using pkm_abi::fail;
-  if (!a) return fail(PKM_EINVAL, "args is NULL");
-  int rc = pkm::check_sizes(a->n_bags, a->bag_size, a->n_rows);
-  if (rc != PKM_OK) return rc;
-  if (a->dtype != PKM_F32 && a->dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
-  const int eb = a->dtype == PKM_BF16 ? 2 : 4;
-  if (a->dim < 1 || a->dim > 2048 || ((int64_t)a->dim * eb) % 16 != 0)
-    return fail(PKM_EINVAL, "dim must be in [1, 2048] with dim * sizeof(dtype) a multiple of 16");
-  if (a->ds && (a->softmax_group < 1 || a->bag_size % a->softmax_group != 0))
-    return fail(PKM_EINVAL, "softmax_group must divide bag_size");
-  if (a->update != 0 && a->update != 1) return fail(PKM_EINVAL, "update must be 0 or 1");
-  if (a->n_bags == 0) return PKM_OK;
-  if (!a->table || !a->idx || !a->w || !a->dy) return fail(PKM_EINVAL, "table, idx, w and dy must not be NULL");
-  if ((((uintptr_t)a->table | (uintptr_t)a->dy | (uintptr_t)a->grad) & 15) != 0)
-    return fail(PKM_EINVAL, "table, dy and grad must be 16-byte aligned");
-  const bool need_sort = a->rows || a->grad || a->n_unique || a->update;
-  if ((rc = pkm::device_ok()) != PKM_OK) return rc;
-  const void* tview = nullptr;
-  if ((rc = pkm_abi::device_view(a->table, "table", &tview)) != PKM_OK) return rc;
-  const int slices = a->dim * eb / 16;
-  hipStream_t s = (hipStream_t)stream;
+  return pkm::run_bag_backward(a, (uint8_t*)workspace, ws_bytes, false, (hipStream_t)stream);
+}
 
-  // without the update, dw and ds come from their own pass over the rows; with it, from
-  // the rows the update reads (before writing them)
-  if ((a->dw || a->ds) && !a->update) {
-    if (a->dtype == PKM_BF16) rc = pkm::launch_dw<2>(a, (const uint8_t*)tview, slices, s);
-    else rc = pkm::launch_dw<4>(a, (const uint8_t*)tview, slices, s);
-    if (rc != PKM_OK) return rc;
-  }
-  if (!need_sort) return PKM_OK;
-
-  const int64_t n = a->n_bags * a->bag_size;
-  pkm::SortSpace S;
-  if ((rc = pkm::sort_space(n, a->n_rows, S)) != PKM_OK) return rc;
-  if (!workspace || ws_bytes < S.total)
-    return fail(PKM_EWORKSPACE, "workspace has %zu bytes, these sizes need %zu", workspace ? ws_bytes : (size_t)0,
-                S.total);
-  if (((uintptr_t)workspace & 255) != 0) return fail(PKM_EINVAL, "workspace must be 256-byte aligned");
-  if ((rc = pkm_abi::require_device(workspace, "workspace")) != PKM_OK) return rc;
-  uint8_t* ws = (uint8_t*)workspace;
-  auto U = [&](size_t o) { return (uint32_t*)(ws + o); };
-  PKM_LAUNCH((pkm::bag_keys_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a->idx, n, a->n_rows,
-                                                                                   U(S.keys), U(S.vals)),
-              hipGetLastError()));
-  size_t tb = S.temp_bytes;
-  PKM_HIP(rocprim::radix_sort_pairs(ws + S.temp, tb, (const uint32_t*)U(S.keys), U(S.keys_sorted),
-                                    (const uint32_t*)U(S.vals), U(S.vals_sorted), (uint32_t)n, 0u,
-                                    pkm::key_bits(a->n_rows), s));
-  if (a->update) {
-    // roles into the unsorted-key buffer and, when only ds is asked for, dw into the
-    // unsorted-position buffer: the sort has finished with both
-    int32_t* role = (int32_t*)U(S.keys);
-    float* dwp = a->dw ? a->dw : (a->ds ? (float*)U(S.vals) : nullptr);
-    const uint32_t* ks = U(S.keys_sorted);
-    const uint32_t* ps = U(S.vals_sorted);
-    PKM_LAUNCH((pkm::bag_owner_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(ks, ps, n, (uint32_t)a->n_rows,
-                                                                                      role, dwp),
-                hipGetLastError()));
-    if (a->dtype == PKM_BF16) rc = pkm::launch_update<2>(a, (uint8_t*)tview, slices, role, ks, ps, dwp, s);
-    else rc = pkm::launch_update<4>(a, (uint8_t*)tview, slices, role, ks, ps, dwp, s);
-    if (rc != PKM_OK) return rc;
-    if (a->ds)
-      PKM_LAUNCH((pkm::bag_ds_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(a->w, dwp, n, a->softmax_group,
-                                                                                     a->ds),
-                  hipGetLastError()));
-  }
-  if (!a->rows && !a->grad && !a->n_unique) return PKM_OK;
-  tb = S.temp_bytes;
-  PKM_HIP(rocprim::run_length_encode(ws + S.temp, tb, (const uint32_t*)U(S.keys_sorted), (unsigned)n, U(S.unique),
-                                     U(S.counts), U(S.runs), s));
-  if (!a->grad) {
-    PKM_LAUNCH((pkm::bag_rows_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(
-                   U(S.unique), U(S.runs), n, (uint32_t)a->n_rows, a->rows, a->n_unique),
-                hipGetLastError()));
-    return PKM_OK;
-  }
-  tb = S.temp_bytes;
-  PKM_HIP(rocprim::exclusive_scan(ws + S.temp, tb, (const uint32_t*)U(S.counts), U(S.offsets), 0u, (size_t)n,
-                                  rocprim::plus<uint32_t>(), s));
-  // one block per possible run (at most n, the grid capped at 2^22 blocks, which then loop): a
-  // block's rows form a chain of dependent loads, so many resident blocks are what hides the
-  // latency; blocks past the run count exit
-  const dim3 grid((unsigned)(n < ((int64_t)1 << 22) ? n : ((int64_t)1 << 22)));
-#define PKM_GRAD(EBV)                                                                                          \
-  PKM_LAUNCH((pkm::bag_grad_kernel<EBV><<<grid, 256, 0, s>>>(U(S.unique), U(S.counts), U(S.offsets), U(S.runs), \
-                                                             U(S.vals_sorted), a->w, a->dy, a->bag_size, a->dim, \
-                                                             slices, (uint32_t)a->n_rows, a->rows, a->grad,      \
-                                                             a->n_unique),                                       \
-              hipGetLastError()))
-  if (a->dtype == PKM_BF16) PKM_GRAD(2);
-  else PKM_GRAD(4);
-#undef PKM_GRAD
-  return PKM_OK;
+int pkm_bag_backward_noalloc(const pkm_bag_backward_args* a, void* stream) {
+  return pkm::run_bag_backward(a, nullptr, PKM_BAG_BACKWARD_NOALLOC_BYTES, true, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -220,3 +220,15 @@ def test_bag_backward_argument_errors_before_any_device_call(P):
     assert bb(args(table=None)) == P.PKM_EINVAL
     assert bb(args(dy=8)) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
     assert bb(args(n_bags=0, table=None, idx=None, w=None, dy=None)) == P.PKM_OK
+    # the entry point without a workspace checks the same arguments before touching the device
+    na = lambda a: lib.pkm_bag_backward_noalloc(ctypes.byref(a), None)
+    assert lib.pkm_bag_backward_noalloc(None, None) == P.PKM_EINVAL
+    assert na(args(dtype=3)) == P.PKM_EINVAL and "dtype" in P.pkm_last_error()
+    assert na(args(n_bags=1 << 24)) == P.PKM_EINVAL and "2^24" in P.pkm_last_error()
+    assert na(args(dy=8)) == P.PKM_EINVAL and "aligned" in P.pkm_last_error()
+    assert na(args(n_bags=0, table=None, idx=None, w=None, dy=None)) == P.PKM_OK
+    # the binding's size of the fixed buffers is the header's
+    import re
+    hdr = open(os.path.join(ROOT, "include", "bag_backward.h")).read()
+    m = re.search(r"#define PKM_BAG_BACKWARD_NOALLOC_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == P.PKM_BAG_BACKWARD_NOALLOC_BYTES
