@@ -133,7 +133,8 @@ def pkm_last_error() -> str:
 def pkm_workspace_size(cfg: pkm_config) -> int:
     n = _lib.pkm_workspace_size(ctypes.byref(cfg))
     if n == 0:
-        raise PkmError(PKM_EINVAL, "pkm_workspace_size")
+        code = PKM_EUNSUPPORTED if pkm_last_error().startswith("unsupported") else PKM_EINVAL
+        raise PkmError(code, "pkm_workspace_size")
     return n
 
 

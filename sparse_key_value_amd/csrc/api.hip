@@ -78,7 +78,8 @@ using pkm_abi::fail;
 
 struct pkm_handle {
   pkm_config cfg;
-  int d_h = 0;
+  int d_h = 0;   // d_query / 2
+  int d_hp = 0;  // d_h padded for scoring: the stored width of query halves and sub-key rows
   const void* values = nullptr;
   uint8_t* ws = nullptr;
   pkm::Layout L;
@@ -127,7 +128,7 @@ int run_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* hidx, float*
   const pkm_config& c = h->cfg;
   const pkm::Layout& L = h->L;
   if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, 0, s));
-  PKM_LAUNCH(pkm::launch_score_candidates(qhat, h->at(L.khat), T, c.n_heads, h->d_h, c.n_sub, c.k, c.dtype,
+  PKM_LAUNCH(pkm::launch_score_candidates(qhat, h->at(L.khat), T, c.n_heads, h->d_hp, c.n_sub, c.k, c.dtype,
                                           h->at<float>(L.gmax), h->at<float>(L.theta), h->at<uint64_t>(L.cand),
                                           h->at<int32_t>(L.count), s));
   if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, 1, s));
@@ -166,9 +167,11 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, 0, s));
   PKM_LAUNCH(pkm::launch_gemm(x, h->at(L.wqT), q, T, (int)L.qz_cols, c.d_model, c.dtype, pkm::EPI_STORE_F32, s));
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, 1, s));
-  // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves
+  // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves,
+  // each stored in d_hp elements (zeros after d_h)
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, 0, s));
-  PKM_LAUNCH(pkm::launch_rownorm(q, 1, h->at(L.qhat), c.dtype, T * H, dq, c.qk_norm, c.norm_eps, s, H, L.qz_cols));
+  PKM_LAUNCH(pkm::launch_rownorm(q, 1, h->at(L.qhat), c.dtype, T * H, dq, c.qk_norm, c.norm_eps, s, H, L.qz_cols,
+                                 h->d_h, h->d_hp));
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, 1, s));
   // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
   int rc = run_select(h, h->at(L.qhat), T, halves ? h->at<int32_t>(L.hidx) : nullptr,
@@ -201,7 +204,9 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   if (idx_out) PKM_HIP(hipMemcpyAsync(idx_out, idx, nsel * 4, hipMemcpyDeviceToDevice, s));
   if (w_out) PKM_HIP(hipMemcpyAsync(w_out, w, nsel * 4, hipMemcpyDeviceToDevice, s));
   if (dbg) {
-    if (dbg->qhat) PKM_HIP(hipMemcpyAsync(dbg->qhat, h->at(L.qhat), (size_t)T * H * dq * eb, hipMemcpyDeviceToDevice, s));
+    if (dbg->qhat)  // [T, H, 2, d_h] from the padded rows
+      PKM_HIP(hipMemcpy2DAsync(dbg->qhat, h->d_h * eb, h->at(L.qhat), h->d_hp * eb, h->d_h * eb, (size_t)T * H * 2,
+                               hipMemcpyDeviceToDevice, s));
     if (dbg->half_idx) PKM_HIP(hipMemcpyAsync(dbg->half_idx, h->at(L.hidx), 2 * nsel * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->half_score) PKM_HIP(hipMemcpyAsync(dbg->half_score, h->at(L.hsc), 2 * nsel * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->idx) PKM_HIP(hipMemcpyAsync(dbg->idx, idx, nsel * 4, hipMemcpyDeviceToDevice, s));
@@ -223,6 +228,11 @@ size_t pkm_workspace_size(const pkm_config* cfg) {
     fail(PKM_EINVAL, "invalid config: %s", why.c_str());
     return 0;
   }
+  why = pkm::unsupported_reason(cfg);
+  if (!why.empty()) {
+    fail(PKM_EUNSUPPORTED, "unsupported config: %s", why.c_str());
+    return 0;
+  }
   return pkm::make_layout(cfg).total;
 }
 
@@ -232,6 +242,8 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   *out = nullptr;
   std::string why = pkm::check_config(cfg);
   if (!why.empty()) return fail(PKM_EINVAL, "invalid config: %s", why.c_str());
+  why = pkm::unsupported_reason(cfg);
+  if (!why.empty()) return fail(PKM_EUNSUPPORTED, "unsupported config: %s", why.c_str());
   if (!W_q || !subkeys || !values || !workspace) return fail(PKM_EINVAL, "W_q, subkeys, values and workspace must not be NULL");
   if (cfg->memory_plus && (!W1 || !W2)) return fail(PKM_EINVAL, "memory_plus needs W1 and W2");
   if (((uintptr_t)values & 15) != 0) return fail(PKM_EINVAL, "values must be 16-byte aligned");
@@ -253,6 +265,7 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   if (!h) return fail(PKM_EINVAL, "out of host memory");
   h->cfg = *cfg;
   h->d_h = cfg->d_query / 2;
+  h->d_hp = pkm::padded_half(h->d_h);
   const void* vview = nullptr;
   if ((rc = pkm_abi::device_view(values, "values", &vview)) != PKM_OK) {
     delete h;
@@ -271,9 +284,9 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   // W_q [d_model, H*d_q] -> [H*d_q, d_model]
   if ((e = pkm::launch_transpose(W_q, h->at(L.wqT), c.d_model, c.n_heads * c.d_query, c.dtype, s)) != hipSuccess)
     return bail(fail(PKM_EHIP, "repack of W_q failed: %s", hipGetErrorString(e)));
-  // fold qk-norm into the sub-keys: one row per (head, half, sub-key)
+  // fold qk-norm into the sub-keys: one row per (head, half, sub-key), stored in d_hp elements
   if ((e = pkm::launch_rownorm(subkeys, c.dtype == PKM_F32, h->at(L.khat), c.dtype, (int64_t)c.n_heads * 2 * c.n_sub,
-                               h->d_h, c.qk_norm, c.norm_eps, s)) != hipSuccess)
+                               h->d_h, c.qk_norm, c.norm_eps, s, 1, 0, h->d_h, h->d_hp)) != hipSuccess)
     return bail(fail(PKM_EHIP, "sub-key normalisation failed: %s", hipGetErrorString(e)));
   if (c.memory_plus) {
     if ((e = pkm::launch_transpose(W1, h->at(L.w1T), c.d_model, c.d_value, c.dtype, s)) != hipSuccess ||
@@ -299,16 +312,22 @@ int pkm_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* half_idx, fl
   if (T == 0) return PKM_OK;
   if (!qhat) return fail(PKM_EINVAL, "qhat must not be NULL");
   const pkm::Layout& L = h->L;
+  hipStream_t s = (hipStream_t)stream;
+  if (h->d_hp != h->d_h) {  // the caller's [T, H, 2, d_h] rows, padded to the scoring width
+    PKM_LAUNCH(pkm::launch_pad_rows(qhat, h->at(L.qhat), T * h->cfg.n_heads * 2, h->d_h, h->d_hp, h->cfg.dtype, s));
+    qhat = h->at(L.qhat);
+  }
   return run_select(h, qhat, T, half_idx ? half_idx : h->at<int32_t>(L.hidx), half_score ? half_score : h->at<float>(L.hsc),
                     idx ? idx : h->at<int32_t>(L.idx), score ? score : h->at<float>(L.sc), w ? w : h->at<float>(L.w),
-                    (hipStream_t)stream, nullptr);
+                    s, nullptr);
 }
 
 int pkm_copy_normalized_subkeys(pkm_handle* h, void* dst, void* stream) {
   if (!h || !dst) return fail(PKM_EINVAL, "handle and dst must not be NULL");
   const size_t eb = h->cfg.dtype == PKM_BF16 ? 2 : 4;
-  const size_t bytes = (size_t)h->cfg.n_heads * 2 * h->cfg.n_sub * h->d_h * eb;
-  PKM_HIP(hipMemcpyAsync(dst, h->at(h->L.khat), bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  // [H, 2, n_sub, d_h] from the padded rows
+  PKM_HIP(hipMemcpy2DAsync(dst, h->d_h * eb, h->at(h->L.khat), h->d_hp * eb, h->d_h * eb,
+                           (size_t)h->cfg.n_heads * 2 * h->cfg.n_sub, hipMemcpyDeviceToDevice, (hipStream_t)stream));
   return PKM_OK;
 }
 

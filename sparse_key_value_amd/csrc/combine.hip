@@ -10,7 +10,7 @@
 // of the two fp32 half scores.
 //
 // One wave per (token, head).  First the two per-half lists: each half's candidates
-// (at most CAND keys from the scoring kernel, a superset of its top-k) are ranked by
+// (at most cand_slots(k) keys from the scoring kernel, a superset of its top-k) are ranked by
 // comparing every key with every other (v_readlane broadcasts), and the k best are
 // written, in order, to LDS (and to the per-half outputs when asked for).  Both lists are
 // then sorted, so the pair of positions (i, j) is beaten by every (i', j') with i' <= i,
@@ -22,7 +22,9 @@
 // then breaks the other way, so the cells off the staircase are checked against the
 // k-th key found (one check per row of the grid, by monotonicity); if any could reach
 // it (a rounding tie, about never with real data) the wave redoes the selection over
-// all k*k pairs.
+// all k*k pairs.  k = 33..64 (more staircase cells than two per lane: 280 for k = 64) takes
+// a kernel of its own that keeps up to five cells per lane and selects the k best by k
+// rounds of a wave-wide maximum.
 #include "kernels.hpp"
 
 namespace pkm {
@@ -91,12 +93,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   // per-half top-k from the candidates, sorted by rank
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    // candidates: lane half 0 in slots [0, CAND/2), half 1 in [CAND/2, CAND)
+    // candidates: lane half 0 in slots [0, 64), half 1 in [64, 128) (cand_slots(k) = 128)
     const int64_t r2 = row * 2 + c;
-    const int na = count[2 * r2], nb = count[2 * r2 + 1];  // <= CAND / 2 after the overflow pass
-    const uint64_t* cr = cand + r2 * CAND;
+    const int na = count[2 * r2], nb = count[2 * r2 + 1];  // <= 64 after the overflow pass
+    const uint64_t* cr = cand + r2 * 128;
     const uint64_t x0 = lane < na ? cr[lane] : 0ull;
-    const uint64_t x1 = lane < nb ? cr[CAND / 2 + lane] : 0ull;
+    const uint64_t x1 = lane < nb ? cr[64 + lane] : 0ull;
     // rank = the number of candidates with a larger key; two broadcasts per step so that
     // the compares of one step do not wait on each other's carry
     int r0 = 0, r1 = 0, q0 = 0, q1 = 0;
@@ -233,12 +235,141 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
   }
 }
 
+// The staircase of k = 33..64: (i + 1)(j + 1) <= k holds at most 280 cells (k = 64).
+struct StairWide {
+  uint16_t pos[320];      // (i << 8) | j for slot s (lane s % 64 holds slots s, s + 64, ...), 0xFFFF = empty
+  uint8_t first_off[64];  // row a's first column off the staircase: floor(k / (a + 1))
+};
+
+// The combine for k = 33..64: per-half ranking over up to 128 candidates per lane half (four
+// per lane), the staircase cells five per lane, the k best by k rounds of a wave-wide maximum,
+// the off-staircase check with an exhaustive redo, and the softmax.
+__global__ void __launch_bounds__(256) combine_wide_kernel(const uint64_t* __restrict__ cand,
+                                                           const int32_t* __restrict__ count, int64_t rows, int n,
+                                                           int k, StairWide st, int32_t* __restrict__ half_idx,
+                                                           float* __restrict__ half_score, int32_t* __restrict__ idx,
+                                                           float* __restrict__ score, float* __restrict__ w) {
+  constexpr int CS = 256, HALF = CS / 2;  // cand_slots(k) for k > 32
+  __shared__ uint64_t lists[4][2][MAX_K];
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;  // row = t * H + h
+  if (row >= rows) return;
+
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t r2 = row * 2 + c;
+    const int na = count[2 * r2], nb = count[2 * r2 + 1];  // <= HALF after the overflow pass
+    const uint64_t* cr = cand + r2 * CS;
+    // candidate q of this lane: slot lane + 64 q of lane half 0 (q < 2) or of lane half 1
+    uint64_t x[4];
+    x[0] = lane < na ? cr[lane] : 0ull;
+    x[1] = 64 + lane < na ? cr[64 + lane] : 0ull;
+    x[2] = lane < nb ? cr[HALF + lane] : 0ull;
+    x[3] = 64 + lane < nb ? cr[HALF + 64 + lane] : 0ull;
+    // rank = the number of candidates with a larger key (keys are distinct; empty slots are 0)
+    int r[4] = {0, 0, 0, 0};
+    auto count_above = [&](uint64_t y) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] += y > x[q];
+    };
+    for (int i = 0; i < na && i < 64; ++i) count_above(readlane_u64(x[0], i));
+    for (int i = 64; i < na; ++i) count_above(readlane_u64(x[1], i - 64));
+    for (int i = 0; i < nb && i < 64; ++i) count_above(readlane_u64(x[2], i));
+    for (int i = 64; i < nb; ++i) count_above(readlane_u64(x[3], i - 64));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (x[q] != 0ull && r[q] < k) lists[wv][c][r[q]] = x[q];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  if (half_idx) {  // the per-half lists, when asked for
+    for (int e = lane; e < 2 * k; e += 64) {
+      const int c = e / k, j = e - c * k;
+      const uint64_t key = lists[wv][c][j];
+      const int64_t o = (row * 2 + c) * k + j;
+      half_idx[o] = (int32_t)key_index(key);
+      half_score[o] = key_score(key);
+    }
+  }
+  const uint64_t* L0 = lists[wv][0];
+  const uint64_t* L1 = lists[wv][1];
+  auto cell_key = [&](int a, int b) -> uint64_t {
+    return make_key(key_score(L0[a]) + key_score(L1[b]), key_index(L0[a]) * (uint32_t)n + key_index(L1[b]));
+  };
+
+  // the staircase cells, five slots per lane; the k best by rounds of a wave-wide maximum
+  uint64_t x[5];
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const uint16_t p = st.pos[lane + 64 * m];
+    x[m] = p != 0xFFFF ? cell_key(p >> 8, p & 0xFF) : 0ull;
+  }
+  uint64_t mine = 0ull, kth = 0ull;  // lane j < k ends up with the j-th best key
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = x[0];
+#pragma unroll
+    for (int m = 1; m < 5; ++m) best = x[m] > best ? x[m] : best;
+    const uint64_t win = wave_max_u64(best);
+#pragma unroll
+    for (int m = 0; m < 5; ++m) x[m] = x[m] == win ? 0ull : x[m];
+    if (lane == j) mine = win;
+    kth = win;
+  }
+
+  // nothing off the staircase may beat the k-th key (see the k <= 32 kernel): row a's largest
+  // off-staircase sum is at column floor(k / (a + 1)); a row that could reach it sends the
+  // wave to an exhaustive selection over all k*k cells, k rounds of a wave-wide maximum
+  // below the previous winner (the keys are distinct)
+  const float kth_score = key_score(kth);
+  bool beaten = false;
+  if (lane < k) {
+    const int b0 = st.first_off[lane];
+    if (b0 < k) beaten = key_score(L0[lane]) + key_score(L1[b0]) >= kth_score;
+  }
+  if (__ballot(beaten) != 0) {
+    uint64_t prev = ~0ull;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0ull;
+      for (int a = 0; a < k; ++a) {
+        const uint64_t key = lane < k ? cell_key(a, lane) : 0ull;
+        best = key < prev && key > best ? key : best;
+      }
+      const uint64_t win = wave_max_u64(best);
+      if (lane == j) mine = win;
+      prev = win;
+    }
+  }
+
+  // softmax over the k winners (max = the first one)
+  const float top = key_score(shfl_u64(mine, 0));
+  const float sc = key_score(mine);
+  const float e = lane < k ? __expf(sc - top) : 0.f;
+  const float z = wave_sum_f32(e);
+  if (lane < k) {
+    const int64_t o = row * k + lane;
+    idx[o] = (int32_t)key_index(mine);
+    score[o] = sc;
+    w[o] = e / z;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T, int H, int n, int k,
                           int32_t* half_idx, float* half_score, int32_t* idx, float* score, float* w, hipStream_t s) {
   const int64_t rows = T * H;
   if (rows == 0) return hipSuccess;
+  if (k > 32) {
+    StairWide st;
+    int m = 0;
+    for (int a = 0; a < k; ++a)
+      for (int b = 0; (a + 1) * (b + 1) <= k; ++b) st.pos[m++] = (uint16_t)((a << 8) | b);
+    for (; m < 320; ++m) st.pos[m] = 0xFFFF;
+    for (int a = 0; a < 64; ++a) st.first_off[a] = (uint8_t)(a < k ? k / (a + 1) : 0);
+    combine_wide_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(cand, count, rows, n, k, st, half_idx,
+                                                                         half_score, idx, score, w);
+    return hipGetLastError();
+  }
   Stair st;
   int m = 0;
   for (int a = 0; a < k; ++a)

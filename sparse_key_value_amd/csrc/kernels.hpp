@@ -12,7 +12,10 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 
 // Selection buffers per row (token, head, half): group maxima and candidate keys.
 constexpr int MAX_GROUPS = 128;
-constexpr int CAND = 128;
+constexpr int MAX_K = 64;
+// Candidate slots per row: half for each of a token's two lanes in the scoring passes; a
+// larger k leaves more candidates above the bound.
+constexpr int cand_slots(int k) { return k <= 32 ? 128 : 256; }
 
 // GEMM epilogues: C = A[M,K] * Bt[N,K]^T, fp32 accumulation.
 enum {
@@ -22,15 +25,21 @@ enum {
 
 hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s);
 // Row r of `rows` is element r % per_tok of token r / per_tok: input at token stride in_ld
-// elements (0: per_tok * width, rows back to back), output rows back to back.
+// elements (0: per_tok * width, rows back to back).  Output rows back to back, each cut into
+// segments of `seg` elements stored in `seg_ld` elements with zeros after them (seg = 0: one
+// unpadded segment).
 hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtype, int64_t rows, int width,
-                          int norm, float eps, hipStream_t s, int per_tok = 1, int64_t in_ld = 0);
+                          int norm, float eps, hipStream_t s, int per_tok = 1, int64_t in_ld = 0, int seg = 0,
+                          int seg_ld = 0);
+// dst [rows, ld] = src [rows, width] with zeros in columns [width, ld).
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int width, int ld, int dtype, hipStream_t s);
 hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N, int K, int dtype, int epi,
                        hipStream_t s);
-// Sub-key scoring: per row (t, h, c) of qhat [T, H, 2, d_h] against khat [H, 2, n, d_h],
-// the candidates of its top-k.  Scratch gmax [T*H*2, MAX_GROUPS] fp32, theta [T*H*2];
-// outputs cand [T*H*2, CAND] 64-bit keys and count [T*H*2, 2] (candidates in slots
-// [0, CAND/2) and [CAND/2, CAND); each count <= CAND/2 on return).
+// Sub-key scoring: per row (t, h, c) of qhat [T, H, 2, d_h] against khat [H, 2, n, d_h]
+// (d_h: the stored, padded width), the candidates of its top-k.  Scratch gmax
+// [T*H*2, MAX_GROUPS] fp32, theta [T*H*2]; outputs cand [T*H*2, C] 64-bit keys, C =
+// cand_slots(k), and count [T*H*2, 2] (candidates in slots [0, C/2) and [C/2, C); each count
+// <= C/2 on return).
 hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k,
                                    int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
                                    hipStream_t s);
@@ -47,6 +56,5 @@ hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, 
 
 hipError_t launch_convert_f32(const float* in, void* out, int64_t n, int dtype, hipStream_t s);
 
-bool score_topk_supported(int d_h, int dtype);
 
 }  // namespace pkm

@@ -38,12 +38,9 @@ inline std::string check_config(const pkm_config* c) {
     return "d_value must be a multiple of 32 for the bf16 Memory+ gate (GEMM K-tile)";
   if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
   if (c->d_query <= 0 || c->d_query % 2 != 0) return "d_query must be positive and even";
-  const int d_h = c->d_query / 2;
-  if (d_h != 64 && d_h != 128 && d_h != 256) return "d_query / 2 must be 64, 128 or 256";
-  if (d_h == 256 && c->dtype == PKM_F32) return "d_query / 2 = 256 is built for bf16 only (fp32: 64 or 128)";
   if (c->n_sub < 1) return "n_sub must be >= 1";
   if ((int64_t)c->n_sub * (int64_t)c->n_sub >= ((int64_t)1 << 31)) return "n_sub^2 must be < 2^31 (int32 flat index)";
-  if (c->k < 1 || c->k > 32 || c->k > c->n_sub) return "k must satisfy 1 <= k <= min(n_sub, 32)";
+  if (c->k < 1 || c->k > 64 || c->k > c->n_sub) return "k must satisfy 1 <= k <= min(n_sub, 64)";
   if (c->d_value <= 0 || ((int64_t)c->d_value * eb) % 16 != 0)
     return "d_value * sizeof(dtype) must be a positive multiple of 16";
   if (c->qk_norm != 0 && c->qk_norm != 1) return "qk_norm must be 0 or 1";
@@ -56,10 +53,26 @@ inline std::string check_config(const pkm_config* c) {
   return "";
 }
 
+// Widest query half the scoring kernels take (d_query <= 512); a valid config beyond it is
+// refused with PKM_EUNSUPPORTED rather than PKM_EINVAL.
+constexpr int MAX_HALF = 256;
+
+// Returns an empty string if the kernels are built for a valid config, else the reason.
+inline std::string unsupported_reason(const pkm_config* c) {
+  if (c->d_query / 2 > MAX_HALF) return "d_query / 2 must be <= 256 (the widest query half the scoring kernels hold)";
+  return "";
+}
+
+// Width of a query half and a sub-key row as stored for scoring: d_query / 2 padded with zeros
+// to the next width the scoring kernels are built for (64, 128 or 256).  Zero products leave
+// every fp32 dot product unchanged.
+inline int padded_half(int d_h) { return d_h <= 64 ? 64 : (d_h <= 128 ? 128 : 256); }
+
 inline Layout make_layout(const pkm_config* c) {
   Layout L;
   const size_t eb = c->dtype == PKM_BF16 ? 2 : 4;
   const size_t H = c->n_heads, dq = c->d_query, dm = c->d_model, dv = c->d_value, n = c->n_sub, k = c->k;
+  const size_t dhp = (size_t)padded_half(c->d_query / 2);
   const size_t T = (size_t)c->max_tokens;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -70,13 +83,13 @@ inline Layout make_layout(const pkm_config* c) {
   L.qz_cols = (int64_t)(H * dq + (c->memory_plus ? dv : 0));
   L.wqT = take((size_t)L.qz_cols * dm * eb);
   if (c->memory_plus) L.w1T = L.wqT + H * dq * dm * eb;
-  L.khat = take(H * 2 * n * (dq / 2) * eb);
+  L.khat = take(H * 2 * n * dhp * eb);
   if (c->memory_plus) L.w2T = take(dm * dv * eb);
   L.q = take(T * (size_t)L.qz_cols * 4);
-  L.qhat = take(T * H * dq * eb);
+  L.qhat = take(T * H * 2 * dhp * eb);
   L.gmax = take(T * H * 2 * 128 * 4);   // MAX_GROUPS group maxima per row
   L.theta = take(T * H * 2 * 4);
-  L.cand = take(T * H * 2 * 128 * 8);   // CAND candidate keys per row
+  L.cand = take(T * H * 2 * (k <= 32 ? 128 : 256) * 8);   // candidate keys per row (cand_slots)
   L.count = take(T * H * 2 * 2 * 4);   // candidates per lane half
   L.hidx = take(T * H * 2 * k * 4);
   L.hsc = take(T * H * 2 * k * 4);

@@ -55,17 +55,21 @@ __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, size_t i, floa
 // One wave per row of `width` elements: out = norm ? v / sqrt(mean(v^2) + eps) : v.
 // Input element type TI (fp32 accumulator or stored dtype), output type TO.  Row r is
 // element (r % per_tok) of token r / per_tok: it starts at (r / per_tok) * in_ld +
-// (r % per_tok) * width in the input (in_ld elements per token) and at r * width in the
-// output.  VEC: fp32 input read four elements (16 bytes) per lane at a time.
+// (r % per_tok) * width in the input (in_ld elements per token).  The output row is the
+// input row cut into segments of `seg` elements, each stored in `seg_ld` >= seg elements
+// followed by zeros (seg_ld = seg: rows back to back, nothing padded); output row r starts at
+// r * (width / seg) * seg_ld.  VEC: fp32 input read four elements (16 bytes) per lane at a
+// time, unpadded output only.
 template <typename TI, typename TO, bool VEC>
 __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in, TO* __restrict__ out,
                                                       int64_t rows, int width, int per_tok, int64_t in_ld, int norm,
-                                                      float eps) {
+                                                      float eps, int seg, int seg_ld) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
   const TI* src = in + (row / per_tok) * in_ld + (row % per_tok) * (int64_t)width;
-  TO* dst = out + row * width;
+  const int nseg = width / seg;
+  TO* dst = out + row * (int64_t)nseg * seg_ld;
   float scale = 1.0f;
   if constexpr (VEC) {
     // width is a multiple of 256: every lane holds width / 256 groups of four
@@ -100,18 +104,27 @@ __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in,
       ss = wave_sum_f32(ss);
       scale = 1.0f / __fsqrt_rn(ss / (float)width + eps);
     }
-    for (int i = lane; i < width; i += 64) store_elem<TO>(dst, i, load_elem<TI>(src, i) * scale);
+    if (seg == seg_ld) {
+      for (int i = lane; i < width; i += 64) store_elem<TO>(dst, i, load_elem<TI>(src, i) * scale);
+    } else {
+      for (int i = lane; i < width; i += 64) store_elem<TO>(dst, (i / seg) * seg_ld + i % seg, load_elem<TI>(src, i) * scale);
+      const int pad = seg_ld - seg;
+      for (int i = lane; i < nseg * pad; i += 64) store_elem<TO>(dst, (i / pad) * seg_ld + seg + i % pad, 0.0f);
+    }
   }
 }
 
 hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtype, int64_t rows, int width,
-                          int norm, float eps, hipStream_t s, int per_tok, int64_t in_ld) {
+                          int norm, float eps, hipStream_t s, int per_tok, int64_t in_ld, int seg, int seg_ld) {
   if (rows == 0) return hipSuccess;
   if (in_ld == 0) in_ld = (int64_t)per_tok * width;
+  if (seg == 0) seg = seg_ld = width;
   dim3 grid((unsigned)((rows + 3) / 4));
-  const bool vec = in_is_f32 && width % 256 == 0 && width <= 1024 && in_ld % 4 == 0 && ((uintptr_t)in & 15) == 0;
-#define PKM_RN(TI, TO, V) \
-  rownorm_kernel<TI, TO, V><<<grid, 256, 0, s>>>((const TI*)in, (TO*)out, rows, width, per_tok, in_ld, norm, eps)
+  const bool vec = in_is_f32 && width % 256 == 0 && width <= 1024 && in_ld % 4 == 0 && ((uintptr_t)in & 15) == 0 &&
+                   seg == seg_ld;
+#define PKM_RN(TI, TO, V)                                                                                          \
+  rownorm_kernel<TI, TO, V><<<grid, 256, 0, s>>>((const TI*)in, (TO*)out, rows, width, per_tok, in_ld, norm, eps, seg, \
+                                                 seg_ld)
   if (in_is_f32) {
     if (out_dtype == DT_BF16) {
       if (vec) PKM_RN(float, uint16_t, true); else PKM_RN(float, uint16_t, false);
@@ -123,6 +136,28 @@ hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtyp
     else PKM_RN(uint16_t, float, false);
   }
 #undef PKM_RN
+  return hipGetLastError();
+}
+
+// dst row r = src row r (width elements) followed by zeros up to ld elements; a capped grid
+// loops over the rows * ld outputs.
+template <typename T>
+__global__ void __launch_bounds__(256) pad_rows_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t rows,
+                                                       int width, int ld) {
+  const int64_t total = rows * ld;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / ld;
+    const int c = (int)(i - r * ld);
+    dst[i] = c < width ? src[r * width + c] : T(0);
+  }
+}
+
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int width, int ld, int dtype, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows * ld + 255) / 256;
+  const dim3 grid((unsigned)(blocks < ((int64_t)1 << 20) ? blocks : ((int64_t)1 << 20)));
+  if (dtype == DT_BF16) pad_rows_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, rows, width, ld);
+  else pad_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, rows, width, ld);
   return hipGetLastError();
 }
 

@@ -25,13 +25,13 @@
 //      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring
 //             above the bound, and of those scoring exactly the bound the first k each
 //             lane sees (lowest indices first), as 64-bit keys to the row's candidate
-//             list (CAND slots, half per lane).  With random-like data about 37 of
-//             4,096 per row.
-//    A lane's count may exceed its CAND / 2 slots (structured data); that row is then
+//             list (cand_slots(k) slots, half per lane).  With random-like data and
+//             k = 32 about 37 of 4,096 per row.
+//    A lane's count may exceed its half of the slots (structured data); that row is then
 //    scored exhaustively by the overflow kernel before the combine kernel reads it.
-//  * With fewer than 2k groups (few sub-keys for the k asked for) the bound prunes little
-//    and most rows would overflow: every row is then scored exhaustively, one wave per
-//    row, instead of the two passes.
+//  * With fewer than 2k groups (k + 32 for k > 32: few sub-keys for the k asked for) the
+//    bound prunes little and most rows would overflow: every row is then scored
+//    exhaustively, one wave per row, instead of the two passes.
 //  * Keys are 64-bit (ordered score << 32 | ~index): ties resolve to the lower index
 //    and every key is distinct.
 //  * Blocks are numbered so that block b works on pair (h, c) = b mod 2H; blocks are
@@ -391,15 +391,14 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
 }
 
 // Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
-// theta).  Each of a token's two lanes owns half of the row's CAND slots and counts its
-// own candidates.
+// theta).  Each of a token's two lanes owns `half` of the row's 2 * half slots and counts
+// its own candidates.
 template <typename DT, int DH, int NW, int FR, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, int k, int splits, int cps,
                                                        const float* __restrict__ theta, uint64_t* __restrict__ cand,
-                                                       int32_t* __restrict__ count) {
+                                                       int32_t* __restrict__ count, int half) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
-  constexpr int HALF = CAND / 2;
   // SROW floats per lane: the lane's 16 FR scores of the chunk, read back by position for
   // the appends (36 or 20, not 32 or 16: 16-byte stores of 16 consecutive lanes then hit
   // distinct banks)
@@ -430,7 +429,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
     const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
     row[g] = (t * H + h) * 2 + c;
     thr[g] = t < T ? theta[row[g]] : __builtin_inff();
-    dst[g] = cand + row[g] * CAND + hi * HALF;
+    dst[g] = cand + row[g] * (2 * half) + hi * half;
   }
   // thz: the bound with a zero bound taken as -0, so that the sign of (score - thz) is
   // set exactly when score < bound, -0 scores included (x - x is +0; finite values)
@@ -441,12 +440,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   // stash slot i of fragment g: consecutive lanes at consecutive words
   auto stash_at = [&](int g, int i) -> uint64_t& { return stash[((i * FR + g) * NW + wv) * 64 + lane]; };
   // the row's lane-half list gets nst more keys: slots by one atomic count (a count beyond
-  // HALF sends the row to the overflow pass, as a full list does)
+  // `half` sends the row to the overflow pass, as a full list does)
   auto publish = [&](int g, int nst) {
     const int base = atomicAdd(count + (g ? row[FR - 1] : row[0]) * 2 + hi, nst);
     uint64_t* d = g ? dst[FR - 1] : dst[0];
     for (int i = 0; i < nst; ++i)
-      if (base + i < HALF) d[base + i] = stash_at(g, i);
+      if (base + i < half) d[base + i] = stash_at(g, i);
   };
   sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
@@ -497,7 +496,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
             cn = 0;
           }
           stash_at(g, cn) = make_key(s, (uint32_t)sub);
-        } else if (cn < HALF) {
+        } else if (cn < half) {
           (g ? dst[FR - 1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
         }
         ++cn;
@@ -525,22 +524,23 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
 }
 
 // The exact top-k of one row (t, h, c) by exhaustive scoring in plain fp32 FMAs (d in
-// ascending order): each lane keeps the best 32 keys of its share of the sub-keys in
+// ascending order): each lane keeps the best LK >= k keys of its share of the sub-keys in
 // registers, the 64 lane lists are merged by k rounds of a wave-wide maximum, and the
-// row's candidate list becomes exactly its top-k (count k in the first lane half, 0 in
-// the second).  qs: this wave's LDS row of DH floats.
-template <typename DT, int DH>
+// row's candidate list (cs slots) becomes exactly its top-k (count k in the first lane
+// half, 0 in the second).  qs: this wave's LDS row of DH floats.
+template <typename DT, int DH, int LK>
 __device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t r2, int H, int n,
-                               int k, uint64_t* __restrict__ cand, int32_t* __restrict__ count, float* qs, int lane) {
+                               int k, uint64_t* __restrict__ cand, int cs, int32_t* __restrict__ count, float* qs,
+                               int lane) {
   constexpr int VE = 16 / (int)sizeof(DT);  // elements per 16-byte load
   const int pair = (int)(r2 % (2 * H));
   const DT* q = qhat + r2 * DH;
   for (int d = lane; d < DH; d += 64) qs[d] = load_elem_f32(q, d);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  uint64_t L[32];
+  uint64_t L[LK];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) L[j] = 0ull;
+  for (int j = 0; j < LK; ++j) L[j] = 0ull;
   const DT* kb = khat + (size_t)pair * n * DH;
   for (int i = lane; i < n; i += 64) {
     const u32x4* kr = (const u32x4*)(kb + (size_t)i * DH);
@@ -557,9 +557,9 @@ __device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict
       }
     }
     uint64_t key = make_key(s, (uint32_t)i);
-    if (key > L[31]) {
+    if (key > L[LK - 1]) {
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
+      for (int j = 0; j < LK; ++j) {
         const uint64_t lo = key > L[j] ? L[j] : key;
         L[j] = key > L[j] ? key : L[j];
         key = lo;
@@ -570,10 +570,10 @@ __device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict
     const uint64_t win = wave_max_u64(L[0]);
     if (L[0] == win) {
 #pragma unroll
-      for (int i = 0; i < 31; ++i) L[i] = L[i + 1];
-      L[31] = 0ull;
+      for (int i = 0; i < LK - 1; ++i) L[i] = L[i + 1];
+      L[LK - 1] = 0ull;
     }
-    if (lane == 0) cand[r2 * CAND + j] = win;
+    if (lane == 0) cand[r2 * cs + j] = win;
   }
   if (lane == 0) {
     count[2 * r2] = k;
@@ -582,38 +582,52 @@ __device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict
   __builtin_amdgcn_wave_barrier();
 }
 
-// Rows whose candidates overflowed (more than CAND / 2 in either lane's half: structured
+// Rows whose candidates overflowed (more than cs / 2 in either lane's half: structured
 // data with many sub-keys above the bound) are scored again exhaustively.  A persistent
 // grid scans the counts; with no overflow it only reads them.
-template <typename DT, int DH>
+template <typename DT, int DH, int LK>
 __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
-                                                       int32_t* __restrict__ count) {
+                                                       int cs, int32_t* __restrict__ count) {
   __shared__ float qs[4][DH];
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t waves = (int64_t)gridDim.x * 4;
   for (int64_t base = ((int64_t)blockIdx.x * 4 + wv) * 64; base < rows2; base += waves * 64) {
     const int64_t r = base + lane;
-    uint64_t over = __ballot(r < rows2 && (count[2 * r] > CAND / 2 || count[2 * r + 1] > CAND / 2));
+    uint64_t over = __ballot(r < rows2 && (count[2 * r] > cs / 2 || count[2 * r + 1] > cs / 2));
     while (over) {
       const int64_t r2 = base + __builtin_ctzll(over);
       over &= over - 1;
-      exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
+      exhaustive_row<DT, DH, LK>(qhat, khat, r2, H, n, k, cand, cs, count, qs[wv], lane);
     }
   }
 }
 
 // Few sub-keys per row (fewer than 2k groups, so the group-maximum bound prunes little and
 // most rows would overflow): every row exhaustively, one wave per row.
-template <typename DT, int DH>
+template <typename DT, int DH, int LK>
 __global__ void __launch_bounds__(256) direct_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                      int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
-                                                     int32_t* __restrict__ count) {
+                                                     int cs, int32_t* __restrict__ count) {
   __shared__ float qs[4][DH];
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r2 = (int64_t)blockIdx.x * 4 + wv;
   if (r2 >= rows2) return;
-  exhaustive_row<DT, DH>(qhat, khat, r2, H, n, k, cand, count, qs[wv], lane);
+  exhaustive_row<DT, DH, LK>(qhat, khat, r2, H, n, k, cand, cs, count, qs[wv], lane);
+}
+
+// Every row exhaustively (few sub-keys for k, or query halves wider than the two MFMA passes
+// are built for); lists of 32 keys per lane for k <= 32, else 64.
+template <typename DT, int DH>
+hipError_t launch_direct(const void* qhat, const void* khat, int64_t rows, int H, int n, int k, uint64_t* cand,
+                         int32_t* count, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  const int cs = cand_slots(k);
+  if (k <= 32)
+    direct_kernel<DT, DH, 32><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand, cs, count);
+  else
+    direct_kernel<DT, DH, MAX_K><<<grid, 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand, cs, count);
+  return hipGetLastError();
 }
 
 template <typename DT, int DH, int NW, int FR>
@@ -640,12 +654,12 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   }
   const dim3 grid((unsigned)(tiles * splits * 2 * H));
   const int64_t rows = T * H * 2;
+  const int cs = cand_slots(k);
   hipError_t e;
-  if (ngroups < 2 * k) {
-    direct_kernel<DT, DH><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n,
-                                                                         k, cand, count);
-    return hipGetLastError();
-  }
+  // too few groups for k and the bound prunes little: every row exhaustively.  k > 32 takes the
+  // passes from k + 32 groups (at most 128 are formed), where the bound still leaves about
+  // 100-190 candidates per row against 256 slots
+  if (ngroups < (k <= 32 ? 2 * k : k + 32)) return launch_direct<DT, DH>(qhat, khat, rows, H, n, k, cand, count, s);
 #define PKM_P1(G)                                                                                       \
   pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, splits, cps, gmax, \
                                                            splits > 1 ? count : nullptr)
@@ -669,14 +683,19 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
     if constexpr (NW == 8 && FR == 2) return hipErrorInvalidValue;
     else
       pass2_kernel<DT, DH, NW, FR, true><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, splits,
-                                                                  cps, theta, cand, count);
+                                                                  cps, theta, cand, count, cs / 2);
   } else
     pass2_kernel<DT, DH, NW, FR, false><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, k, 1, nch,
-                                                                 theta, cand, count);
+                                                                 theta, cand, count, cs / 2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t scan_waves = (rows + 63) / 64;
   const int64_t ob = (scan_waves + 3) / 4 < 1024 ? (scan_waves + 3) / 4 : 1024;
-  overflow_kernel<DT, DH><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand, count);
+  if (k <= 32)
+    overflow_kernel<DT, DH, 32><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k, cand,
+                                                                   cs, count);
+  else
+    overflow_kernel<DT, DH, MAX_K><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k,
+                                                                      cand, cs, count);
   return hipGetLastError();
 }
 
@@ -710,10 +729,6 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
 
 }  // namespace
 
-bool score_topk_supported(int d_h, int dtype) {
-  return d_h == 64 || d_h == 128 || (d_h == 256 && dtype == DT_BF16);
-}
-
 hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k,
                                    int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
                                    hipStream_t s) {
@@ -729,6 +744,9 @@ hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T
     switch (d_h) {
       case 64: PKM_PASSES(float, 64);
       case 128: PKM_PASSES(float, 128);
+      // fp32 halves wider than 128: the two MFMA passes would hold 256 query floats per lane,
+      // so every row is scored exhaustively instead
+      case 256: return launch_direct<float, 256>(qhat, khat, T * H * 2, H, n, k, cand, count, s);
     }
   }
 #undef PKM_PASSES

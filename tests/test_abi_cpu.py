@@ -65,11 +65,11 @@ def test_workspace_size_matches_layout(P):
     (dict(d_model=1020), "d_model"),
     (dict(n_heads=0), "n_heads"),
     (dict(d_query=511), "d_query"),
-    (dict(d_query=96), "d_query / 2"),
     (dict(n_sub=0), "n_sub"),
     (dict(n_sub=46341), "2^31"),
     (dict(k=0), "k must"),
-    (dict(k=33), "k must"),
+    (dict(k=65), "k must"),
+    (dict(k=64, n_sub=63), "k must"),
     (dict(k=9, n_sub=8), "k must"),
     (dict(d_value=12), "d_value"),
     (dict(qk_norm=2), "qk_norm"),
@@ -87,6 +87,36 @@ def test_invalid_configs_are_rejected(P, bad, needle):
     rc = P._lib._lib.pkm_create(ctypes.byref(c), 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 40, None,
                                 ctypes.byref(ctypes.c_void_p()))
     assert rc == P.PKM_EINVAL and needle in P.pkm_last_error()
+
+
+@pytest.mark.parametrize("d_query,k", [(96, 32), (6, 3), (130, 48), (512, 64), (2, 1), (258, 33)])
+def test_workspace_of_padded_query_halves_and_wide_k(P, d_query, k):
+    """Any even d_query up to 512 and any k up to 64: query halves and sub-key rows are stored
+    padded to the next scoring width (64, 128 or 256), and k > 32 takes 256 candidate slots
+    per row instead of 128."""
+    a = lambda v: (v + 255) // 256 * 256
+    T, H, dm, dv, n = 1000, 3, 256, 128, 700
+    c = _cfg(P, d_query=d_query, k=k, n_heads=H, d_model=dm, d_value=dv, n_sub=n, max_tokens=T, memory_plus=0)
+    d_h = d_query // 2
+    dhp = 64 if d_h <= 64 else (128 if d_h <= 128 else 256)
+    cs = 128 if k <= 32 else 256
+    want = (a(H * d_query * dm * 2) + a(H * 2 * n * dhp * 2) + a(T * H * d_query * 4) + a(T * H * 2 * dhp * 2) +
+            a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * cs * 8) + a(T * H * 2 * 2 * 4) +
+            2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4))
+    assert P.pkm_workspace_size(c) == want
+
+
+def test_query_halves_wider_than_the_scoring_kernels_are_unsupported(P):
+    """d_query = 514 is a valid config (even) that the scoring kernels are not built for:
+    PKM_EUNSUPPORTED, not PKM_EINVAL."""
+    c = _cfg(P, d_query=514)
+    with pytest.raises(P.PkmError) as e:
+        P.pkm_workspace_size(c)
+    assert e.value.code == P.PKM_EUNSUPPORTED and "256" in str(e.value)
+    rc = P._lib._lib.pkm_create(ctypes.byref(c), 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 40, None,
+                                ctypes.byref(ctypes.c_void_p()))
+    assert rc == P.PKM_EUNSUPPORTED
+    assert P.pkm_workspace_size(_cfg(P, d_query=512)) > 0
 
 
 def test_create_argument_errors_before_any_device_call(P):

@@ -345,20 +345,24 @@ def test_eight_wave_scoring_blocks(case):
     wl.close()
 
 
-@pytest.mark.parametrize("dt,H,T,n_sub,d_q", [("f32", 2, 100, 96, 128), ("bf16", 2, 100, 96, 128),
-                                              # 64 heads x 520 tokens over 1,040 sub-keys: 8-wave scoring
-                                              # blocks with a ragged last block
-                                              ("bf16", 64, 520, 1040, 128),
-                                              # split sub-key ranges: the zero tokens tie k times per lane
-                                              # and range, more than a lane's LDS stash holds (64-, 256-wide
-                                              # bf16 and 64-wide fp32 sub-keys), and every such row
-                                              # overflows into the exhaustive pass
-                                              ("bf16", 4, 100, 1040, 128), ("bf16", 4, 200, 1040, 512),
-                                              ("f32", 4, 100, 1040, 128)])
-def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub, d_q):
+@pytest.mark.parametrize("dt,H,T,n_sub,d_q,k", [("f32", 2, 100, 96, 128, 16), ("bf16", 2, 100, 96, 128, 16),
+                                                # 64 heads x 520 tokens over 1,040 sub-keys: 8-wave scoring
+                                                # blocks with a ragged last block
+                                                ("bf16", 64, 520, 1040, 128, 16),
+                                                # split sub-key ranges: the zero tokens tie k times per lane
+                                                # and range, more than a lane's LDS stash holds (64-, 256-wide
+                                                # bf16 and 64-wide fp32 sub-keys), and every such row
+                                                # overflows into the exhaustive pass
+                                                ("bf16", 4, 100, 1040, 128, 16), ("bf16", 4, 200, 1040, 512, 16),
+                                                ("f32", 4, 100, 1040, 128, 16),
+                                                # k > 32: the two MFMA passes (8-wave blocks), the split
+                                                # ranges and the exhaustive rows, 64-key lane lists
+                                                ("bf16", 64, 520, 1024, 128, 64), ("bf16", 4, 100, 2048, 512, 48),
+                                                ("f32", 2, 100, 96, 128, 40)])
+def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub, d_q, k):
     """Duplicated sub-keys give bitwise-equal scores; zero tokens give all-zero scores."""
-    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}", dtype=dt, n_sub=n_sub, k=16, H=H, d_q=d_q, d_model=64,
-                                        d_v=64, T=T, qk_norm=True)
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"ties_{dt}_h{H}_k{k}", dtype=dt, n_sub=n_sub, k=k, H=H, d_q=d_q,
+                                        d_model=64, d_v=64, T=T, qk_norm=True)
     inp = S.make_inputs(cfg, seed=4)
     sk = inp["subkeys"].copy()
     sk[:, :, 1::2] = sk[:, :, 0::2]      # sub-key 2i+1 duplicates 2i in every codebook
@@ -366,7 +370,7 @@ def test_exact_ties_resolve_to_lowest_index(dt, H, T, n_sub, d_q):
     x = inp["x"].copy()
     x[::5] = 0                          # every fifth token is all zero: every score is 0
     inp["x"] = x
-    say(f"ties {dt} H={H} T={T} n_sub={n_sub} d_q={d_q}")
+    say(f"ties {dt} H={H} T={T} n_sub={n_sub} d_q={d_q} k={k}")
     wl = _G().Workload(cfg, seed=4, host_inputs=inp)
     o = run_debug(wl)
     # the oracle on every token of the small cases, on a spread (every fifth token, the zero
@@ -548,16 +552,18 @@ def test_combine_rounding_tie_takes_exhaustive_path():
     pk.close()
 
 
-def test_candidate_overflow_takes_exhaustive_path():
+@pytest.mark.parametrize("k", [32, 64])
+def test_candidate_overflow_takes_exhaustive_path(k):
     """Scores rising with the sub-key index make the group-maximum bound loose.
 
-    With s_i = i over 2,048 sub-keys in groups of 16, the 32nd largest group maximum is
-    1551, so about 500 sub-keys reach the bound and overflow the candidate list; that row
-    is then scored exhaustively.  Every score is an exact small integer, so the result
-    must equal the oracle's exactly: per-half lists 2047..2016, final cells by sum.
+    With s_i = i over 2,048 sub-keys in groups of 16, the k-th largest group maximum is
+    2047 - 16 (k - 1) (1551 for k = 32), so about 500 (k = 64: 1,000) sub-keys reach the bound
+    and overflow the candidate list; that row is then scored exhaustively.  Every score is
+    an exact small integer, so the result must equal the oracle's exactly: per-half lists
+    2047 .. 2048 - k, final cells by sum.
     """
     import sparse_key_value_amd as P
-    n, dh, k = 2048, 64, 32
+    n, dh = 2048, 64
     K = np.zeros((1, 2, n, dh), dtype=np.float32)
     K[0, 0, :, 0] = np.arange(n, dtype=np.float32)
     K[0, 1, :, 1] = np.arange(n, dtype=np.float32)[::-1] * 0.5   # half 1: best at low indices
@@ -650,6 +656,98 @@ def test_largest_sub_key_lists():
     np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"])
     np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"])
     np.testing.assert_array_equal(sc.cpu().numpy(), sel["score"].astype(np.float32))
+    pk.close()
+
+
+@pytest.mark.parametrize("case", [
+    # k > 32 (the pages' "about thirty" values, up to 64): the two MFMA passes with 256
+    # candidate slots per row, the per-row exhaustive path, the wide combine
+    dict(name="k33_two_pass", dtype="bf16", qk_norm=True, n_sub=1100, k=33, H=4, d_q=256, d_model=128, d_v=128, T=300),
+    dict(name="k48_exhaustive_rows", dtype="bf16", qk_norm=True, n_sub=300, k=48, H=2, d_q=128, d_model=64, d_v=64,
+         T=150),
+    dict(name="k64_eight_waves", dtype="bf16", qk_norm=True, n_sub=2048, k=64, H=64, d_q=512, d_model=64, d_v=64,
+         T=600),
+    dict(name="k64_split_ranges_gate", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=4096, k=64, H=4, d_q=512,
+         d_model=256, d_v=256, T=150),
+    dict(name="k64_eq_n_sub", dtype="f32", qk_norm=False, n_sub=64, k=64, H=2, d_q=128, d_model=64, d_v=64, T=40),
+    dict(name="k40_f32_two_pass", dtype="f32", qk_norm=True, n_sub=2000, k=40, H=4, d_q=256, d_model=64, d_v=64, T=260),
+    # any even d_query: halves stored padded with zeros to 64, 128 or 256
+    dict(name="dq96_two_pass", dtype="bf16", qk_norm=True, n_sub=1100, k=32, H=4, d_q=96, d_model=64, d_v=64, T=300),
+    dict(name="dq6_exhaustive", dtype="bf16", qk_norm=True, n_sub=50, k=8, H=2, d_q=6, d_model=64, d_v=64, T=64),
+    dict(name="dq200_gate_eight_waves", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=1030, k=16, H=32, d_q=200,
+         d_model=128, d_v=128, T=1100),
+    dict(name="dq258_k64", dtype="bf16", qk_norm=True, n_sub=2048, k=64, H=4, d_q=258, d_model=64, d_v=64, T=300),
+    dict(name="dq2_k1", dtype="f32", qk_norm=True, n_sub=40, k=1, H=3, d_q=2, d_model=64, d_v=64, T=33),
+    dict(name="dq300_f32_exhaustive", dtype="f32", qk_norm=True, n_sub=500, k=40, H=2, d_q=300, d_model=64, d_v=64,
+         T=100),
+    dict(name="dq62_f32_two_pass", dtype="f32", qk_norm=False, n_sub=1050, k=8, H=8, d_q=62, d_model=64, d_v=64,
+         T=500),
+])
+def test_wide_k_and_any_even_query_width(case):
+    """The boundary's full range: 1 <= k <= min(n_sub, 64) and any even d_query up to 512.
+    Stage-wise and end to end against the oracle (on a spread of tokens for the large batches),
+    and pkm_select from the forward's own normalised query (given in the caller's unpadded
+    layout) bitwise equal to the forward's selection."""
+    import sparse_key_value_amd as P
+    case = dict(case)
+    name = case.pop("name")
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=name, memory_plus=case.pop("memory_plus", False), **case)
+    say(f"boundary {cfg.name}")
+    wl = _G().Workload(cfg, seed=13)
+    o = run_debug(wl)
+    full_check(wl, o, rows=None if cfg.T * cfg.H <= 4096 else _sample_tokens(cfg.T))
+    q = _G().to_dev(o["qhat"], cfg.dtype)
+    idx = torch.empty((cfg.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((cfg.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda")
+    w = torch.empty((cfg.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda")
+    P.pkm_select(wl.pkm.handle, q, cfg.T, None, None, idx, sc, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), o["idx"])
+    np.testing.assert_array_equal(w.cpu().numpy(), o["w"])
+    wl.close()
+
+
+def test_wide_combine_rounding_tie_takes_exhaustive_path():
+    """k = 34 (the combine for k > 32) with an fp32 rounding tie off the staircase.
+
+    Half 0: sub-key 10 scores 2^25, sub-key 3 scores 2^25 - 2, every other one -1000; half 1:
+    sub-key b scores 1.5 - 0.4 b / 64, all in (1.1, 1.5].  Every cell of sub-keys 10 and 3 then
+    sums to 2^25 in fp32, so by flat index (a * 64 + b) the top-34 cells are (3, 0..33); the
+    half-0 list is (10, 3, ...), which puts (3, 17..33) off the staircase (2 (j + 1) > 34), so
+    only the exhaustive redo finds them.  The float64 oracle orders by the exact sums, (10,
+    0..33); the two lists differ only inside the near-tie margin.
+    """
+    import sparse_key_value_amd as P
+    n, dh, k = 64, 64, 34
+    K = np.zeros((1, 2, n, dh), dtype=np.float32)
+    K[0, 0, :, 0] = -1000.0
+    K[0, 0, 10, 0], K[0, 0, 3, 0] = 2.0 ** 25, 2.0 ** 25 - 2
+    K[0, 1, :, 1] = (1.5 - 0.4 * np.arange(n) / 64).astype(np.float32)
+    wq = torch.zeros((64, 2 * dh), dtype=torch.float32, device="cuda")
+    vals = torch.zeros((n * n, 4), dtype=torch.float32, device="cuda")
+    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=2 * dh, n_sub=n, k=k, d_value=4, dtype="f32", qk_norm=0,
+                            memory_plus=0, max_tokens=4, W_q=wq, subkeys=torch.from_numpy(K).cuda(), values=vals)
+    q = np.zeros((1, 1, 2, dh), dtype=np.float32)
+    q[0, 0, 0, 0] = 1.0
+    q[0, 0, 1, 1] = 1.0
+    hi_ = torch.empty((1, 1, 2, k), dtype=torch.int32, device="cuda")
+    hs_ = torch.empty((1, 1, 2, k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((1, 1, k), dtype=torch.float32, device="cuda")
+    w = torch.empty((1, 1, k), dtype=torch.float32, device="cuda")
+    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), 1, hi_, hs_, idx, sc, w)
+    torch.cuda.synchronize()
+    assert hi_.cpu().numpy()[0, 0, 0, :2].tolist() == [10, 3]
+    assert hi_.cpu().numpy()[0, 0, 1].tolist() == list(range(k))
+    assert idx.cpu().numpy()[0, 0].tolist() == [3 * n + b for b in range(k)]
+    assert (sc.cpu().numpy() == 2.0 ** 25).all()
+    np.testing.assert_allclose(w.cpu().numpy(), 1.0 / k, rtol=1e-6)
+    q64 = q.astype(np.float64).reshape(1, 1, 2 * dh)
+    K64 = K.astype(np.float64)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K64[:, 0], K64[:, 1], k)
+    assert sel["idx"][0, 0].tolist() == [10 * n + b for b in range(k)]
+    ch = PAR.cell_choice_scores(q64[..., :dh], q64[..., dh:], K64[:, 0], K64[:, 1], idx.cpu().numpy())
+    PAR.check_lists(idx.cpu().numpy(), sel["idx"], sel["score"], ch, "wide rounding-tie case")
     pk.close()
 
 
