@@ -58,7 +58,7 @@ extern "C" {
 enum {
   PKM_OK = 0,
   PKM_EINVAL = -1,        /* bad argument or shape */
-  PKM_EUNSUPPORTED = -2,  /* device is not gfx950, or a shape outside the built kernels */
+  PKM_EUNSUPPORTED = -2,  /* device is not gfx950, or a valid shape outside the built kernels (d_query > 512) */
   PKM_EWORKSPACE = -3,    /* workspace too small */
   PKM_EHIP = -4           /* a HIP runtime call failed (message has the HIP error) */
 };
@@ -68,9 +68,9 @@ typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 typedef struct {
   int32_t d_model;      /* width of x; a multiple of 32 for bf16 (4 for fp32) */
   int32_t n_heads;      /* 1 <= H <= 64 */
-  int32_t d_query;      /* per-head query width d_q; d_q / 2 in {64, 128, 256} (256: bf16 only) */
+  int32_t d_query;      /* per-head query width d_q: even, 2..512 (larger: PKM_EUNSUPPORTED) */
   int32_t n_sub;        /* sub-keys per half; the table has N = n_sub^2 < 2^31 rows */
-  int32_t k;            /* per-half and final top-k, 1 <= k <= min(n_sub, 32) */
+  int32_t k;            /* per-half and final top-k, 1 <= k <= min(n_sub, 64) */
   int32_t d_value;      /* value width; d_value * sizeof(dtype) a multiple of 16 (bf16 Memory+: of 64) */
   int32_t dtype;        /* pkm_dtype of x, W_q, subkeys, values, W1, W2 and out */
   int32_t qk_norm;      /* 0 or 1: RMSNorm of the query (before the split) and of sub-key rows */
@@ -133,7 +133,7 @@ size_t pkm_workspace_size(const pkm_config* cfg);
  *            aligned, owned by the caller, used exclusively by this handle.
  * W_q, subkeys, W1, W2 and the workspace must be device memory (checked).
  * Errors: PKM_EINVAL (bad config, NULL or non-device pointer), PKM_EWORKSPACE,
- * PKM_EUNSUPPORTED (device not gfx950), PKM_EHIP. */
+ * PKM_EUNSUPPORTED (device not gfx950, or d_query > 512), PKM_EHIP. */
 int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, const void* values,
                const void* W1, const void* W2, void* workspace, size_t ws_bytes, void* stream,
                pkm_handle** out);
