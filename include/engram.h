@@ -55,7 +55,8 @@ typedef struct {
   float norm_eps;     /* RMSNorm epsilon, in [0, 1] */
 } engram_config;
 /* Limits: d = n_heads * head_dim with d * sizeof(dtype) <= 4096 bytes (one wave holds a
- * token's d values, four 16-byte slices per lane). */
+ * token's d values, four 16-byte slices per lane); 0 <= T <= 2^25 tokens per call (one wave
+ * per token); seq_len >= 1. */
 
 /* Rows of the stacked table for every (token, head, order), per the formulas above.
  *   ids      [T] int32; seq_len >= 1 tokens per sequence (T need not be a multiple)

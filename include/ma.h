@@ -30,14 +30,14 @@ extern "C" {
  * and stored in dtype (RNE for bf16).
  *   E, E_bar [vocab, d_v] dtype (E_bar may equal E: in place); gain [d_v] float or NULL (1)
  *   d_v * sizeof(dtype) a multiple of 16; d_v a multiple of n_heads, and
- *   (d_v / n_heads) * sizeof(dtype) a multiple of 16; eps in [0, 1]. */
+ *   (d_v / n_heads) * sizeof(dtype) a multiple of 16; eps in [0, 1]; vocab * n_heads <= 2^38. */
 int ma_fold_table(const void* E, int64_t vocab, int32_t d_v, int32_t n_heads, const float* gain, float eps,
                   int32_t dtype, void* E_bar, void* stream);
 
 /* V[t] = K[t] + E_bar[ids[t]] for t < T (fp32 add, stored in dtype); an id outside
  * [0, vocab) reads no row (V[t] = K[t]).
  *   E_bar [vocab, d_v], K and V [T, d_v] dtype, 16-byte aligned; ids [T] int32.
- *   T = 0 is a no-op. */
+ *   vocab >= 1; T * d_v * sizeof(dtype) / 16 <= 2^38.  T = 0 is a no-op. */
 int ma_values(const void* E_bar, int64_t vocab, int32_t d_v, int32_t dtype, const int32_t* ids, int64_t T,
               const void* K, void* V, void* stream);
 

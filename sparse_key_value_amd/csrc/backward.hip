@@ -28,13 +28,14 @@
 
 #include "../../include/bag_backward.h"
 #include "abi.hpp"
+#include "checks.hpp"
 #include "common.hpp"
 
 namespace pkm {
 
 namespace {
 
-constexpr int MAX_BAG = 2048;
+constexpr int MAX_BAG = BAG_MAX;
 
 template <int EB>
 struct BV;
@@ -483,14 +484,8 @@ int sort_space(int64_t n, int64_t n_rows, SortSpace& S) {
 }
 
 int check_sizes(int64_t n_bags, int32_t bag_size, int64_t n_rows) {
-  using pkm_abi::fail;
-  // one block per bag (dw and the update pass): 2^24 blocks of <= 256 lanes keep a launch within
-  // the 2^32 work-items of one dispatch
-  if (n_bags < 0 || n_bags >= ((int64_t)1 << 24)) return fail(PKM_EINVAL, "n_bags must be in [0, 2^24)");
-  if (bag_size < 1 || bag_size > MAX_BAG) return fail(PKM_EINVAL, "bag_size must be in [1, 2048]");
-  if (n_bags * bag_size >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_bags * bag_size must be < 2^31");
-  if (n_rows < 1 || n_rows >= ((int64_t)1 << 31)) return fail(PKM_EINVAL, "n_rows must be in [1, 2^31)");
-  return PKM_OK;
+  const std::string why = check_bag_sizes(n_bags, bag_size, n_rows);
+  return why.empty() ? PKM_OK : pkm_abi::fail(PKM_EINVAL, "%s", why.c_str());
 }
 
 int device_ok() {

@@ -16,15 +16,15 @@
 
 #include "../../include/engram.h"
 #include "abi.hpp"
+#include "checks.hpp"
 #include "common.hpp"
 
 namespace pkm {
 
 namespace {
 
-constexpr int MAX_ORDER = 8;   // largest n-gram order
-constexpr int MAX_ORDERS = 4;  // orders per lookup
-constexpr int MAX_SPL = 4;     // 16-byte slices of a token per lane (d * sizeof <= 4096 bytes)
+constexpr int MAX_ORDER = ENGRAM_MAX_ORDER;
+constexpr int MAX_ORDERS = ENGRAM_MAX_ORDERS;
 
 struct EngramArgs {
   const uint8_t* tables;
@@ -248,11 +248,8 @@ __global__ void __launch_bounds__(256) engram_forward_kernel(EngramArgs a) {
   if (a.alpha_out && lane == 0) a.alpha_out[t] = alpha;
 }
 
-// One thread per (token, head, order): rows[t, k, o].
-__global__ void __launch_bounds__(256) engram_hash_kernel(EngramArgs a, int32_t* __restrict__ rows) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = a.T * a.heads * a.n_orders;
-  if (i >= total) return;
+// rows[i] of the hash, i = (t * heads + k) * n_orders + o.
+__device__ __forceinline__ void hash_one(const EngramArgs& a, int32_t* __restrict__ rows, int64_t i) {
   const int o = (int)(i % a.n_orders);
   const int k = (int)((i / a.n_orders) % a.heads);
   const int64_t t = i / ((int64_t)a.n_orders * a.heads);
@@ -264,33 +261,20 @@ __global__ void __launch_bounds__(256) engram_hash_kernel(EngramArgs a, int32_t*
   rows[i] = (int32_t)(((int64_t)o * a.heads + k) * a.P + (int64_t)mod_p(hh, a));
 }
 
-std::string check_engram(const engram_config* c) {
-  if (!c) return "config is NULL";
-  if (c->dtype != PKM_F32 && c->dtype != PKM_BF16) return "dtype must be PKM_F32 (0) or PKM_BF16 (1)";
-  const int64_t eb = c->dtype == PKM_BF16 ? 2 : 4;
-  if (c->min_order < 1) return "min_order must be >= 1";
-  if (c->n_orders < 1 || c->n_orders > MAX_ORDERS) return "n_orders must be in [1, 4]";
-  if (c->min_order + c->n_orders - 1 > MAX_ORDER) return "the largest order min_order + n_orders - 1 must be <= 8";
-  if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
-  if (c->head_dim < 1 || (c->head_dim * eb) % 16 != 0) return "head_dim * sizeof(dtype) must be a positive multiple of 16";
-  if ((int64_t)c->n_heads * c->head_dim * eb > 64 * 16 * MAX_SPL)
-    return "n_heads * head_dim * sizeof(dtype) must be <= 4096 bytes";
-  if (c->table_rows < 1) return "table_rows must be >= 1";
-  if ((int64_t)c->n_orders * c->n_heads * c->table_rows >= ((int64_t)1 << 31))
-    return "n_orders * n_heads * table_rows must be < 2^31 (int32 rows)";
-  if (c->vocab < 1) return "vocab must be >= 1";
-  if (c->residual != 0 && c->residual != 1) return "residual must be 0 or 1";
-  if (!(c->norm_eps >= 0.0f) || c->norm_eps > 1.0f) return "norm_eps must be in [0, 1]";
-  return "";
+// One thread per (token, head, order): rows[t, k, o]; a capped grid loops.
+__global__ void __launch_bounds__(256) engram_hash_kernel(EngramArgs a, int32_t* __restrict__ rows) {
+  const int64_t total = a.T * a.heads * a.n_orders;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
+    hash_one(a, rows, i);
 }
 
 // Argument checks shared by both entry points; fills `a` on success.
 int prepare(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t seq_len, const int32_t* compress,
             const uint64_t* mult, EngramArgs& a) {
-  const std::string why = check_engram(cfg);
+  std::string why = check_engram(cfg);
   if (!why.empty()) return pkm_abi::fail(PKM_EINVAL, "invalid engram config: %s", why.c_str());
-  if (T < 0 || T > ((int64_t)1 << 31) - 1) return pkm_abi::fail(PKM_EINVAL, "T must be in [0, 2^31)");
-  if (seq_len < 1) return pkm_abi::fail(PKM_EINVAL, "seq_len must be >= 1");
+  why = check_engram_tokens(T, seq_len);
+  if (!why.empty()) return pkm_abi::fail(PKM_EINVAL, "%s", why.c_str());
   if (T > 0 && (!ids || !mult)) return pkm_abi::fail(PKM_EINVAL, "ids and mult must not be NULL");
   const int eb = cfg->dtype == PKM_BF16 ? 2 : 4;
   a = EngramArgs{};
@@ -363,8 +347,8 @@ int engram_hash(const engram_config* cfg, const int32_t* ids, int64_t T, int64_t
   if (!rows) return pkm_abi::fail(PKM_EINVAL, "rows must not be NULL");
   if ((rc = pkm::device_ok()) != PKM_OK) return rc;
   const int64_t total = T * a.heads * a.n_orders;
-  if ((total + 255) / 256 > ((int64_t)1 << 31) - 1) return pkm_abi::fail(PKM_EINVAL, "T * n_heads * n_orders too large");
-  PKM_LAUNCH((pkm::engram_hash_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, (hipStream_t)stream>>>(a, rows),
+  const int64_t blocks = (total + 255) / 256 < ((int64_t)1 << 20) ? (total + 255) / 256 : ((int64_t)1 << 20);
+  PKM_LAUNCH((pkm::engram_hash_kernel<<<dim3((unsigned)blocks), 256, 0, (hipStream_t)stream>>>(a, rows),
               hipGetLastError()));
   return PKM_OK;
 }

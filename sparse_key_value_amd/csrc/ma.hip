@@ -10,6 +10,7 @@
 // last-level cache) and writing the slice of V.
 #include "../../include/ma.h"
 #include "abi.hpp"
+#include "checks.hpp"
 #include "common.hpp"
 
 namespace pkm {
@@ -47,14 +48,13 @@ struct Vec<4> {
   }
 };
 
+// Slice (row, head) = i of the fold.
 template <int EB>
-__global__ void __launch_bounds__(256) fold_kernel(const uint8_t* __restrict__ E, int64_t vocab, int slices,
-                                                   int head_vecs, int n_heads, const float* __restrict__ gain,
-                                                   float eps, uint8_t* __restrict__ out) {
+__device__ __forceinline__ void fold_one(const uint8_t* __restrict__ E, int slices, int head_vecs, int n_heads,
+                                         const float* __restrict__ gain, float eps, uint8_t* __restrict__ out,
+                                         int64_t i) {
   using V = Vec<EB>;
   constexpr int NE = V::E;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= vocab * n_heads) return;
   const int64_t row = i / n_heads;
   const int h = (int)(i - row * n_heads);
   const uint8_t* src = E + ((size_t)row * slices + (size_t)h * head_vecs) * 16;
@@ -77,14 +77,22 @@ __global__ void __launch_bounds__(256) fold_kernel(const uint8_t* __restrict__ E
   }
 }
 
+// One thread per (row, head) slice; a capped grid loops.
 template <int EB>
-__global__ void __launch_bounds__(256) values_kernel(const uint8_t* __restrict__ Ebar, int64_t vocab, int slices,
-                                                     const int32_t* __restrict__ ids, int64_t T,
-                                                     const uint8_t* __restrict__ K, uint8_t* __restrict__ Vout) {
+__global__ void __launch_bounds__(256) fold_kernel(const uint8_t* __restrict__ E, int64_t vocab, int slices,
+                                                   int head_vecs, int n_heads, const float* __restrict__ gain,
+                                                   float eps, uint8_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < vocab * n_heads; i += (int64_t)gridDim.x * 256)
+    fold_one<EB>(E, slices, head_vecs, n_heads, gain, eps, out, i);
+}
+
+// Slice i = t * slices + s of V = K + E_bar[ids[t]].
+template <int EB>
+__device__ __forceinline__ void value_one(const uint8_t* __restrict__ Ebar, int64_t vocab, int slices,
+                                          const int32_t* __restrict__ ids, const uint8_t* __restrict__ K,
+                                          uint8_t* __restrict__ Vout, int64_t i) {
   using V = Vec<EB>;
   constexpr int NE = V::E;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * slices) return;
   const int64_t t = i / slices;
   const int s = (int)(i - t * slices);
   const int32_t id = ids[t];
@@ -97,6 +105,15 @@ __global__ void __launch_bounds__(256) values_kernel(const uint8_t* __restrict__
     for (int x = 0; x < NE; ++x) k[x] += e[x];
   }
   __builtin_nontemporal_store(V::pack(k), (u32x4*)(Vout + (size_t)i * 16));
+}
+
+// One thread per 16-byte slice of a token; a capped grid loops.
+template <int EB>
+__global__ void __launch_bounds__(256) values_kernel(const uint8_t* __restrict__ Ebar, int64_t vocab, int slices,
+                                                     const int32_t* __restrict__ ids, int64_t T,
+                                                     const uint8_t* __restrict__ K, uint8_t* __restrict__ Vout) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * slices; i += (int64_t)gridDim.x * 256)
+    value_one<EB>(Ebar, vocab, slices, ids, K, Vout, i);
 }
 
 int device_ok() {
@@ -118,13 +135,9 @@ extern "C" {
 int ma_fold_table(const void* E, int64_t vocab, int32_t d_v, int32_t n_heads, const float* gain, float eps,
                   int32_t dtype, void* E_bar, void* stream) {
   using pkm_abi::fail;
-  if (dtype != PKM_F32 && dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
+  const std::string why = pkm::check_ma_fold(vocab, d_v, n_heads, eps, dtype);
+  if (!why.empty()) return fail(PKM_EINVAL, "%s", why.c_str());
   const int eb = dtype == PKM_BF16 ? 2 : 4;
-  if (d_v <= 0 || ((int64_t)d_v * eb) % 16 != 0) return fail(PKM_EINVAL, "d_v * sizeof(dtype) must be a positive multiple of 16");
-  if (n_heads < 1 || d_v % n_heads != 0 || ((int64_t)(d_v / n_heads) * eb) % 16 != 0)
-    return fail(PKM_EINVAL, "n_heads must divide d_v with (d_v / n_heads) * sizeof(dtype) a multiple of 16");
-  if (vocab < 0 || vocab * n_heads > ((int64_t)1 << 38)) return fail(PKM_EINVAL, "vocab * n_heads must be <= 2^38");
-  if (!(eps >= 0.0f) || eps > 1.0f) return fail(PKM_EINVAL, "eps must be in [0, 1]");
   if (vocab == 0) return PKM_OK;
   if (!E || !E_bar) return fail(PKM_EINVAL, "E and E_bar must not be NULL");
   if ((((uintptr_t)E | (uintptr_t)E_bar) & 15) != 0) return fail(PKM_EINVAL, "E and E_bar must be 16-byte aligned");
@@ -132,7 +145,7 @@ int ma_fold_table(const void* E, int64_t vocab, int32_t d_v, int32_t n_heads, co
   if (rc != PKM_OK) return rc;
   const int slices = d_v * eb / 16, head_vecs = slices / n_heads;
   const int64_t n = vocab * n_heads;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const dim3 grid((unsigned)((n + 255) / 256 < ((int64_t)1 << 20) ? (n + 255) / 256 : ((int64_t)1 << 20)));
   hipStream_t s = (hipStream_t)stream;
   if (dtype == PKM_BF16)
     PKM_LAUNCH((pkm::fold_kernel<2><<<grid, 256, 0, s>>>((const uint8_t*)E, vocab, slices, head_vecs, n_heads, gain,
@@ -146,11 +159,9 @@ int ma_fold_table(const void* E, int64_t vocab, int32_t d_v, int32_t n_heads, co
 int ma_values(const void* E_bar, int64_t vocab, int32_t d_v, int32_t dtype, const int32_t* ids, int64_t T,
               const void* K, void* V, void* stream) {
   using pkm_abi::fail;
-  if (dtype != PKM_F32 && dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
+  const std::string why = pkm::check_ma_values(vocab, d_v, dtype, T);
+  if (!why.empty()) return fail(PKM_EINVAL, "%s", why.c_str());
   const int eb = dtype == PKM_BF16 ? 2 : 4;
-  if (d_v <= 0 || ((int64_t)d_v * eb) % 16 != 0) return fail(PKM_EINVAL, "d_v * sizeof(dtype) must be a positive multiple of 16");
-  if (vocab < 1) return fail(PKM_EINVAL, "vocab must be >= 1");
-  if (T < 0 || T * ((int64_t)d_v * eb / 16) > ((int64_t)1 << 38)) return fail(PKM_EINVAL, "T * d_v must be <= 2^38 16-byte slices");
   if (T == 0) return PKM_OK;
   if (!E_bar || !ids || !K || !V) return fail(PKM_EINVAL, "E_bar, ids, K and V must not be NULL");
   if ((((uintptr_t)E_bar | (uintptr_t)K | (uintptr_t)V) & 15) != 0)
@@ -159,7 +170,7 @@ int ma_values(const void* E_bar, int64_t vocab, int32_t d_v, int32_t dtype, cons
   if (rc != PKM_OK) return rc;
   const int slices = d_v * eb / 16;
   const int64_t n = T * slices;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  const dim3 grid((unsigned)((n + 255) / 256 < ((int64_t)1 << 20) ? (n + 255) / 256 : ((int64_t)1 << 20)));
   hipStream_t s = (hipStream_t)stream;
   if (dtype == PKM_BF16)
     PKM_LAUNCH((pkm::values_kernel<2><<<grid, 256, 0, s>>>((const uint8_t*)E_bar, vocab, slices, ids, T,
