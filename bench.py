@@ -733,6 +733,8 @@ def main():
                     help="time the value-table backward and sparse update instead of the forward")
     ap.add_argument("--tables", choices=["device", "host"], default="device",
                     help="Engram workloads: keep the tables in HBM or in pinned host memory (prefetched)")
+    ap.add_argument("--bound", choices=["auto", "exact"], default="auto",
+                    help="the scoring's bound pass: fp8 estimate where built (auto) or exact in the stored type")
     ap.add_argument("--tokens", type=int, default=0,
                     help="product-key forward: a batch of this many tokens instead of the workload's (small batches)")
     a = ap.parse_args()
@@ -782,6 +784,7 @@ def main():
     else:
         wl = Workload(cfg, seed=a.seed)
     h = wl.pkm.handle
+    P.pkm_set_score_bound(h, a.bound)
     x = wl.dev["x"]
     out = torch.empty((T, cfg.d_out), dtype=x.dtype, device="cuda")
     stream = torch.cuda.current_stream()
@@ -860,7 +863,7 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights; value table generated on the GPU)",
         "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.d_model, "heads": cfg.H, "d_query": cfg.d_q,
                    "n_sub": cfg.n_sub, "n_keys": cfg.N, "d_value": cfg.d_v, "k": cfg.k, "qk_norm": cfg.qk_norm,
-                   "memory_plus": cfg.memory_plus, "table_GiB": tbytes / 2**30,
+                   "memory_plus": cfg.memory_plus, "score_bound": a.bound, "table_GiB": tbytes / 2**30,
                    "table_memory": "host (pinned)" if host else "device"},
         "roofline": {"bound": "host-link" if host else "hbm", "kernel": "gather (weighted EmbeddingBag)",
                      "achieved": achieved, "peak": HOST_LINK_PEAK_GBPS if host else HBM_PEAK_GBPS, "unit": "GB/s",

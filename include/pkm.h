@@ -188,6 +188,16 @@ int pkm_stage_times(pkm_handle* h, int32_t stage, float* ms, int32_t n);
  * Returns PKM_EINVAL for bits at or above PKM_NUM_STAGES. */
 int pkm_set_stage_timing_mask(pkm_handle* h, uint32_t mask);
 
+/* How the scoring bounds the k-th best score of every (token, head, half) before it collects
+ * candidates.  PKM_BOUND_AUTO (the default): bf16 workloads whose query halves are stored 256
+ * wide (d_query / 2 in 129..256) estimate it from the group maxima of fp8 (OCP e4m3) scores
+ * lowered by a margin, and every other workload takes PKM_BOUND_EXACT: the group maxima of the
+ * scores in the stored type.  The result is the same either way: the candidates are the exact
+ * scores at or above the bound, and a row left with fewer than k is scored exhaustively, so
+ * the bound only decides how much work the selection does. */
+enum { PKM_BOUND_AUTO = 0, PKM_BOUND_EXACT = 1 };
+int pkm_set_score_bound(pkm_handle* h, int32_t mode);
+
 /* Release the handle's host state and events (the workspace stays the caller's). */
 int pkm_destroy(pkm_handle* h);
 

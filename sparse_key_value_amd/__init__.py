@@ -13,10 +13,10 @@ marshals arguments (``_lib``) and manages device memory with PyTorch
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PKM_BAG_BACKWARD_NOALLOC_BYTES, PKM_BF16, PKM_EHIP, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_F32, PKM_OK, STAGES,
+    EXPORTED, LIB_PATH, PKM_BAG_BACKWARD_NOALLOC_BYTES, PKM_BF16, PKM_BOUND_AUTO, PKM_BOUND_EXACT, PKM_EHIP, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_F32, PKM_OK, STAGES,
     PkmError, make_config, pkm_config, pkm_copy_normalized_subkeys, pkm_create, pkm_debug_ptrs, pkm_destroy,
     pkm_embedding_bag, pkm_enable_stage_timing, pkm_forward, pkm_forward_debug, pkm_last_error, pkm_select,
-    pkm_set_stage_timing_mask, pkm_stage_times, pkm_workspace_size,
+    pkm_set_score_bound, pkm_set_stage_timing_mask, pkm_stage_times, pkm_workspace_size,
     engram_config, engram_forward, engram_forward_staged, engram_hash, engram_prefetch, make_engram_config,
     ma_fold_table, ma_values, pkm_bag_backward, pkm_bag_backward_args, pkm_bag_backward_noalloc, pkm_bag_backward_workspace_size,
 )

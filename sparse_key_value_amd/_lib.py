@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkm.so")
 
 PKM_OK, PKM_EINVAL, PKM_EUNSUPPORTED, PKM_EWORKSPACE, PKM_EHIP = 0, -1, -2, -3, -4
 PKM_F32, PKM_BF16 = 0, 1
+PKM_BOUND_AUTO, PKM_BOUND_EXACT = 0, 1
 PKM_BAG_BACKWARD_NOALLOC_BYTES = 96 << 20   # the fixed sort buffers of pkm_bag_backward_noalloc (bag_backward.h)
 STAGES = ["project", "qnorm", "score", "combine", "gather", "gate", "total"]
 STAGE_ID = {n: i for i, n in enumerate(STAGES)}
@@ -72,6 +73,7 @@ _sig = {
     "pkm_enable_stage_timing": (ctypes.c_int, [_vp, _i32]),
     "pkm_stage_times": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_float), _i32]),
     "pkm_set_stage_timing_mask": (ctypes.c_int, [_vp, ctypes.c_uint32]),
+    "pkm_set_score_bound": (ctypes.c_int, [_vp, _i32]),
     "pkm_destroy": (ctypes.c_int, [_vp]),
     "pkm_last_error": (ctypes.c_char_p, []),
     "engram_hash": (ctypes.c_int, [ctypes.POINTER(engram_config), _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -173,6 +175,12 @@ def pkm_embedding_bag(table, n_rows: int, dim: int, dtype, idx, w, n_bags: int, 
 
 def pkm_enable_stage_timing(h: int, max_records: int) -> None:
     _check(_lib.pkm_enable_stage_timing(h, max_records), "pkm_enable_stage_timing")
+
+
+def pkm_set_score_bound(h: int, mode) -> None:
+    """PKM_BOUND_AUTO / "auto" (fp8 estimate where built) or PKM_BOUND_EXACT / "exact"."""
+    m = {"auto": PKM_BOUND_AUTO, "exact": PKM_BOUND_EXACT}.get(mode, mode)
+    _check(_lib.pkm_set_score_bound(h, int(m)), "pkm_set_score_bound")
 
 
 def pkm_set_stage_timing_mask(h: int, stages) -> None:

@@ -80,6 +80,7 @@ struct pkm_handle {
   pkm_config cfg;
   int d_h = 0;   // d_query / 2
   int d_hp = 0;  // d_h padded for scoring: the stored width of query halves and sub-key rows
+  bool fp8 = false;  // the bound pass scores in fp8 (pkm_set_score_bound)
   const void* values = nullptr;
   uint8_t* ws = nullptr;
   pkm::Layout L;
@@ -128,9 +129,16 @@ int run_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* hidx, float*
   const pkm_config& c = h->cfg;
   const pkm::Layout& L = h->L;
   if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, 0, s));
+  pkm::Fp8Bound fb;
+  if (h->fp8) {
+    fb.q8 = h->at(L.q8);
+    fb.k8 = h->at(L.khat8);
+    fb.qn = h->at<float>(L.qn);
+    fb.kmax = h->at<float>(L.kmax);
+  }
   PKM_LAUNCH(pkm::launch_score_candidates(qhat, h->at(L.khat), T, c.n_heads, h->d_hp, c.n_sub, c.k, c.dtype,
                                           h->at<float>(L.gmax), h->at<float>(L.theta), h->at<uint64_t>(L.cand),
-                                          h->at<int32_t>(L.count), s));
+                                          h->at<int32_t>(L.count), fb, s));
   if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_SCORE, 1, s));
   if (tm) PKM_LAUNCH(tm->stage(PKM_STAGE_COMBINE, 0, s));
   PKM_LAUNCH(pkm::launch_combine(h->at<uint64_t>(L.cand), h->at<int32_t>(L.count), T, c.n_heads, c.n_sub, c.k, hidx,
@@ -168,10 +176,12 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
   PKM_LAUNCH(pkm::launch_gemm(x, h->at(L.wqT), q, T, (int)L.qz_cols, c.d_model, c.dtype, pkm::EPI_STORE_F32, s));
   PKM_LAUNCH(tm.stage(PKM_STAGE_PROJECT, 1, s));
   // a2: qk-norm over each head's d_q, stored in dtype; the halves are the two contiguous halves,
-  // each stored in d_hp elements (zeros after d_h)
+  // each stored in d_hp elements (zeros after d_h); for the fp8 bound also their e4m3 copies
+  // and norms
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, 0, s));
   PKM_LAUNCH(pkm::launch_rownorm(q, 1, h->at(L.qhat), c.dtype, T * H, dq, c.qk_norm, c.norm_eps, s, H, L.qz_cols,
-                                 h->d_h, h->d_hp));
+                                 h->d_h, h->d_hp, h->fp8 ? h->at<uint8_t>(L.q8) : nullptr,
+                                 h->fp8 ? h->at<float>(L.qn) : nullptr));
   PKM_LAUNCH(tm.stage(PKM_STAGE_QNORM, 1, s));
   // a3-a6: scoring + per-half top-k, combine + final top-k + softmax
   int rc = run_select(h, h->at(L.qhat), T, halves ? h->at<int32_t>(L.hidx) : nullptr,
@@ -266,6 +276,7 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   h->cfg = *cfg;
   h->d_h = cfg->d_query / 2;
   h->d_hp = pkm::padded_half(h->d_h);
+  h->fp8 = pkm::fp8_bound(cfg);
   const void* vview = nullptr;
   if ((rc = pkm_abi::device_view(values, "values", &vview)) != PKM_OK) {
     delete h;
@@ -288,6 +299,11 @@ int pkm_create(const pkm_config* cfg, const void* W_q, const void* subkeys, cons
   if ((e = pkm::launch_rownorm(subkeys, c.dtype == PKM_F32, h->at(L.khat), c.dtype, (int64_t)c.n_heads * 2 * c.n_sub,
                                h->d_h, c.qk_norm, c.norm_eps, s, 1, 0, h->d_h, h->d_hp)) != hipSuccess)
     return bail(fail(PKM_EHIP, "sub-key normalisation failed: %s", hipGetErrorString(e)));
+  // the fp8 copy of the normalised sub-keys, their norms and the largest norm per (head, half)
+  if (pkm::fp8_bound(cfg) &&
+      (e = pkm::launch_fp8_rows(h->at(L.khat), h->at<uint8_t>(L.khat8), h->at<float>(L.knorm),
+                                (int64_t)c.n_heads * 2 * c.n_sub, h->d_hp, h->at<float>(L.kmax), c.n_sub, s)) != hipSuccess)
+    return bail(fail(PKM_EHIP, "fp8 sub-keys failed: %s", hipGetErrorString(e)));
   if (c.memory_plus) {
     if ((e = pkm::launch_transpose(W1, h->at(L.w1T), c.d_model, c.d_value, c.dtype, s)) != hipSuccess ||
         (e = pkm::launch_transpose(W2, h->at(L.w2T), c.d_value, c.d_model, c.dtype, s)) != hipSuccess)
@@ -317,6 +333,9 @@ int pkm_select(pkm_handle* h, const void* qhat, int64_t T, int32_t* half_idx, fl
     PKM_LAUNCH(pkm::launch_pad_rows(qhat, h->at(L.qhat), T * h->cfg.n_heads * 2, h->d_h, h->d_hp, h->cfg.dtype, s));
     qhat = h->at(L.qhat);
   }
+  if (h->fp8)  // the e4m3 copy and the norms of the query halves, for the bound pass
+    PKM_LAUNCH(pkm::launch_fp8_rows(qhat, h->at<uint8_t>(L.q8), h->at<float>(L.qn), T * h->cfg.n_heads * 2, h->d_hp,
+                                    nullptr, 1, s));
   return run_select(h, qhat, T, half_idx ? half_idx : h->at<int32_t>(L.hidx), half_score ? half_score : h->at<float>(L.hsc),
                     idx ? idx : h->at<int32_t>(L.idx), score ? score : h->at<float>(L.sc), w ? w : h->at<float>(L.w),
                     s, nullptr);
@@ -391,6 +410,13 @@ int pkm_set_stage_timing_mask(pkm_handle* h, uint32_t mask) {
   if (!h) return fail(PKM_EINVAL, "handle is NULL");
   if (mask >> PKM_NUM_STAGES) return fail(PKM_EINVAL, "mask has bits above stage %d", PKM_NUM_STAGES - 1);
   h->stage_mask = mask;
+  return PKM_OK;
+}
+
+int pkm_set_score_bound(pkm_handle* h, int32_t mode) {
+  if (!h) return fail(PKM_EINVAL, "handle is NULL");
+  if (mode != PKM_BOUND_AUTO && mode != PKM_BOUND_EXACT) return fail(PKM_EINVAL, "mode must be PKM_BOUND_AUTO or PKM_BOUND_EXACT");
+  h->fp8 = mode == PKM_BOUND_AUTO && pkm::fp8_bound(&h->cfg);
   return PKM_OK;
 }
 

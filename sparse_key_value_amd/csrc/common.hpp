@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int WAVE = 64;
 
@@ -24,6 +25,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Four fp32 values to OCP fp8 e4m3 (round to nearest even), packed in one word, first value
+// in the low byte.  The conversion turns values beyond the format's 448 into NaN, so they are
+// clamped to +-448 first.
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
+  auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
 }
 
 // ---- ordered selection keys ---------------------------------------------------

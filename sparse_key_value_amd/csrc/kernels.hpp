@@ -23,18 +23,40 @@ enum {
   EPI_STORE_DT = 1      // C -> dtype
 };
 
+// fp8 copies for the bound pass: dst8 [rows, d] = e4m3(src [rows, d] bf16), and norms [rows] =
+// the fp32 norm of every row (nullable); kmax (nullable): the largest norm of every group of
+// `group` consecutive rows, [rows / group].
+hipError_t launch_fp8_rows(const void* src, uint8_t* dst8, float* norms, int64_t rows, int d, float* kmax, int group,
+                           hipStream_t s);
 hipError_t launch_transpose(const void* src, void* dst, int rows, int cols, int dtype, hipStream_t s);
 // Row r of `rows` is element r % per_tok of token r / per_tok: input at token stride in_ld
 // elements (0: per_tok * width, rows back to back).  Output rows back to back, each cut into
 // segments of `seg` elements stored in `seg_ld` elements with zeros after them (seg = 0: one
 // unpadded segment).
+// With q8 (bf16 output, 256-wide segments): also the fp8 copy of the output and the norm of every
+// segment, qn [rows * (width / seg)].
 hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtype, int64_t rows, int width,
                           int norm, float eps, hipStream_t s, int per_tok = 1, int64_t in_ld = 0, int seg = 0,
-                          int seg_ld = 0);
+                          int seg_ld = 0, uint8_t* q8 = nullptr, float* qn = nullptr);
 // dst [rows, ld] = src [rows, width] with zeros in columns [width, ld).
 hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int width, int ld, int dtype, hipStream_t s);
 hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N, int K, int dtype, int epi,
                        hipStream_t s);
+// The bound pass from fp8 scores (bf16 workloads with 256-wide halves; every pointer NULL: the
+// exact bound from the stored type): q8 [T, H, 2, d_h] and k8 [H, 2, n, d_h] OCP e4m3 copies of
+// qhat and khat, qn [T, H, 2] the norms of the query halves, kmax [H, 2] the largest sub-key
+// norm of every (head, half).
+struct Fp8Bound {
+  const void* q8 = nullptr;
+  const void* k8 = nullptr;
+  const float* qn = nullptr;
+  const float* kmax = nullptr;
+};
+// Margin of the fp8 bound in units of |q half| * max |sub-key|: the fp8 rounding error of a score
+// has a standard deviation of about 0.0024 of that product with qk-normalised rows.
+constexpr float FP8_BOUND_ETA = 0.006f;
+constexpr bool fp8_bound_for(int d_h_stored, int dtype) { return dtype == DT_BF16 && d_h_stored == 256; }
+
 // Sub-key scoring: per row (t, h, c) of qhat [T, H, 2, d_h] against khat [H, 2, n, d_h]
 // (d_h: the stored, padded width), the candidates of its top-k.  Scratch gmax
 // [T*H*2, MAX_GROUPS] fp32, theta [T*H*2]; outputs cand [T*H*2, C] 64-bit keys, C =
@@ -42,7 +64,7 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N,
 // <= C/2 on return).
 hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k,
                                    int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
-                                   hipStream_t s);
+                                   const Fp8Bound& fb, hipStream_t s);
 // Per-half top-k from the candidates, k x k combine, final top-k and softmax.
 // Outputs half_idx/half_score [T, H, 2, k] (both NULL: not written), idx/score/w [T, H, k].
 hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T, int H, int n, int k,

@@ -19,6 +19,9 @@ struct Layout {
   int64_t qz_cols = 0;
   size_t q = 0, qhat = 0, hidx = 0, hsc = 0;          // per-forward intermediates
   size_t gmax = 0, theta = 0, cand = 0, count = 0;    // selection scratch
+  // the bound pass from fp8 scores (fp8_bound): e4m3 copies of the sub-keys and the query
+  // halves, the sub-key row norms and their largest per (head, half), the query half norms
+  size_t khat8 = 0, knorm = 0, kmax = 0, q8 = 0, qn = 0;
   size_t idx = 0, sc = 0, w = 0, g = 0;
   size_t total = 0;
 };
@@ -68,6 +71,9 @@ inline std::string unsupported_reason(const pkm_config* c) {
 // every fp32 dot product unchanged.
 inline int padded_half(int d_h) { return d_h <= 64 ? 64 : (d_h <= 128 ? 128 : 256); }
 
+// Whether the bound pass scores in fp8: bf16 workloads whose halves are stored 256 wide.
+inline bool fp8_bound(const pkm_config* c) { return c->dtype == PKM_BF16 && padded_half(c->d_query / 2) == 256; }
+
 inline Layout make_layout(const pkm_config* c) {
   Layout L;
   const size_t eb = c->dtype == PKM_BF16 ? 2 : 4;
@@ -97,6 +103,13 @@ inline Layout make_layout(const pkm_config* c) {
   L.sc = take(T * H * k * 4);
   L.w = take(T * H * k * 4);
   if (c->memory_plus) L.g = take(T * dv * eb);   // y * silu(x W1), the input of the W2 product
+  if (fp8_bound(c)) {
+    L.khat8 = take(H * 2 * n * dhp);
+    L.knorm = take(H * 2 * n * 4);
+    L.kmax = take(H * 2 * 4);
+    L.q8 = take(T * H * 2 * dhp);
+    L.qn = take(T * H * 2 * 4);
+  }
   L.total = off;
   return L;
 }

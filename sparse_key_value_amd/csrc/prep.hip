@@ -59,11 +59,13 @@ __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, size_t i, floa
 // input row cut into segments of `seg` elements, each stored in `seg_ld` >= seg elements
 // followed by zeros (seg_ld = seg: rows back to back, nothing padded); output row r starts at
 // r * (width / seg) * seg_ld.  VEC: fp32 input read four elements (16 bytes) per lane at a
-// time, unpadded output only.
-template <typename TI, typename TO, bool VEC>
+// time, unpadded output only.  Q8 (VEC with 256-wide segments): also the fp8 copy of the output
+// row (q8, same layout, one byte per element) and the fp32 norm of every segment (qn).
+template <typename TI, typename TO, bool VEC, bool Q8 = false>
 __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in, TO* __restrict__ out,
                                                       int64_t rows, int width, int per_tok, int64_t in_ld, int norm,
-                                                      float eps, int seg, int seg_ld) {
+                                                      float eps, int seg, int seg_ld, uint8_t* __restrict__ q8 = nullptr,
+                                                      float* __restrict__ qn = nullptr) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
@@ -94,6 +96,17 @@ __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in,
       if (i < nv)
 #pragma unroll
         for (int e = 0; e < 4; ++e) store_elem<TO>(dst, i * 256 + lane * 4 + e, v[i][e] * scale);
+    if constexpr (Q8) {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        if (i < nv) {
+          const f32x4 w = v[i] * scale;
+          *(uint32_t*)(q8 + row * (int64_t)width + i * 256 + lane * 4) = f32x4_to_fp8(w[0], w[1], w[2], w[3]);
+          const float h = wave_sum_f32(w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3]);
+          if (lane == 0) qn[row * nv + i] = __fsqrt_rn(h);
+        }
+      }
+    }
   } else {
     if (norm) {
       float ss = 0.f;
@@ -115,7 +128,8 @@ __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in,
 }
 
 hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtype, int64_t rows, int width,
-                          int norm, float eps, hipStream_t s, int per_tok, int64_t in_ld, int seg, int seg_ld) {
+                          int norm, float eps, hipStream_t s, int per_tok, int64_t in_ld, int seg, int seg_ld,
+                          uint8_t* q8, float* qn) {
   if (rows == 0) return hipSuccess;
   if (in_ld == 0) in_ld = (int64_t)per_tok * width;
   if (seg == 0) seg = seg_ld = width;
@@ -125,6 +139,17 @@ hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtyp
 #define PKM_RN(TI, TO, V)                                                                                          \
   rownorm_kernel<TI, TO, V><<<grid, 256, 0, s>>>((const TI*)in, (TO*)out, rows, width, per_tok, in_ld, norm, eps, seg, \
                                                  seg_ld)
+  if (q8) {  // fp8 copy and segment norms with the bf16 rows: 256-wide segments, fp32 input
+    if (!vec || seg != 256 || out_dtype != DT_BF16 || !in_is_f32) {
+      const hipError_t e =
+          launch_rownorm(in, in_is_f32, out, out_dtype, rows, width, norm, eps, s, per_tok, in_ld, seg, seg_ld);
+      if (e != hipSuccess) return e;
+      return launch_fp8_rows(out, q8, qn, rows * (width / seg), seg_ld, nullptr, 1, s);
+    }
+    rownorm_kernel<float, uint16_t, true, true><<<grid, 256, 0, s>>>((const float*)in, (uint16_t*)out, rows, width,
+                                                                     per_tok, in_ld, norm, eps, seg, seg_ld, q8, qn);
+    return hipGetLastError();
+  }
   if (in_is_f32) {
     if (out_dtype == DT_BF16) {
       if (vec) PKM_RN(float, uint16_t, true); else PKM_RN(float, uint16_t, false);
@@ -136,6 +161,47 @@ hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtyp
     else PKM_RN(uint16_t, float, false);
   }
 #undef PKM_RN
+  return hipGetLastError();
+}
+
+// One wave per row of d bf16 elements (d a multiple of 4): dst8 = e4m3 of the row, norms[row] =
+// its fp32 norm (if norms).
+__global__ void __launch_bounds__(256) fp8_rows_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst8,
+                                                       float* __restrict__ norms, int64_t rows, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* r = src + row * d;
+  float ss = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    const uint2 p = *(const uint2*)(r + i);
+    const float a = bf16_lo(p.x), b = bf16_hi(p.x), c = bf16_lo(p.y), e = bf16_hi(p.y);
+    ss += a * a + b * b + c * c + e * e;
+    *(uint32_t*)(dst8 + row * d + i) = f32x4_to_fp8(a, b, c, e);
+  }
+  ss = wave_sum_f32(ss);
+  if (norms && lane == 0) norms[row] = __fsqrt_rn(ss);
+}
+
+// kmax[g] = the largest of norms[g * group .. g * group + group - 1]; one block per group.
+__global__ void __launch_bounds__(256) group_max_kernel(const float* __restrict__ norms, int group,
+                                                        float* __restrict__ kmax) {
+  __shared__ float part[4];
+  const float* p = norms + (int64_t)blockIdx.x * group;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < group; i += 256) m = fmaxf(m, p[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) kmax[blockIdx.x] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+hipError_t launch_fp8_rows(const void* src, uint8_t* dst8, float* norms, int64_t rows, int d, float* kmax, int group,
+                           hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  fp8_rows_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>((const uint16_t*)src, dst8, norms, rows, d);
+  if (kmax) group_max_kernel<<<dim3((unsigned)(rows / group)), 256, 0, s>>>(norms, group, kmax);
   return hipGetLastError();
 }
 

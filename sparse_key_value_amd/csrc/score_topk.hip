@@ -54,7 +54,8 @@ namespace {
 constexpr int CHUNK = 32;       // sub-keys per LDS chunk (one 32-row MFMA tile)
 // chunks loaded per barrier: 8-wave blocks (one per CU, LDS to spare) take two chunks
 // between barriers, which halves the barriers and the skew every one of them absorbs
-constexpr int chunks_per_barrier(int nw) { return nw == 8 ? 2 : 1; }
+// (fp8 chunks, half the bytes and half the MFMA time of bf16 ones, go four to a barrier)
+constexpr int chunks_per_barrier(int nw, int eb = 2) { return nw == 8 ? (eb == 1 ? 4 : 2) : 1; }
 
 template <typename DT, int DH>
 struct Mma;
@@ -89,6 +90,28 @@ struct Mma<float, DH> {
     return *(const float*)(row + ((((e >> 2) ^ swz) << 4) | ((e & 3) << 2)));
   }
   __device__ static f32x16 mma(frag a, frag b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
+};
+
+// fp8 (OCP e4m3), the bound pass of bf16 workloads: A = 32 sub-keys x 64 dims (lane: row l%32,
+// 32 consecutive dims from (l/32)*32 of each 64-dim k-step), B = 64 dims x 32 tokens, the same
+// dims per lane; v_mfma_f32_32x32x64_f8f6f4 without scaling, the 32 x 32 fp32 result laid out
+// as for bf16.
+template <int DH>
+struct Mma<uint8_t, DH> {
+  static constexpr int KSTEP = 64;
+  static constexpr int NK = DH / KSTEP;
+  static constexpr int EB = 1;
+  typedef i32x8 frag;
+  __device__ static frag load_q(const uint8_t* q, int kk, int hi) { return *(const i32x8*)(q + kk * KSTEP + hi * 32); }
+  // 16-byte units 4 kk + 2 hi and the next one of the lane's row
+  __device__ static frag lds_k(const uint8_t* row, int swz, int kk, int hi) {
+    const u32x4 lo = *(const u32x4*)(row + (((4 * kk + 2 * hi) ^ swz) << 4));
+    const u32x4 up = *(const u32x4*)(row + (((4 * kk + 2 * hi + 1) ^ swz) << 4));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+  }
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
 };
 
 __device__ __forceinline__ float load_elem_f32(const float* p, size_t i) { return p[i]; }
@@ -162,7 +185,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   // The block sweeps chunks [c0, c1).  SC chunks per barrier: the chunk at position lc =
   // ch - c0 lives in LDS buffer lc % (2 SC); the SC chunks after a barrier are loaded into
   // the other SC buffers while they are scored
-  constexpr int SC = chunks_per_barrier(NW);
+  constexpr int SC = chunks_per_barrier(NW, M::EB);
   // the lagging group (wave-uniform)
   const bool lag = NW == 8 && wv >= 4;
   f32x16 acc[FR];
@@ -184,12 +207,14 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
     const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
 #pragma unroll
     for (int g = 0; g < FR; ++g) acc[g] = f32x16{};
-    if constexpr (M::EB == 2) {
-      // bf16: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling groups
-      // below keep the compiler from pulling the reads back next to their use (it
-      // otherwise waits for the LDS every two k-steps).  (fp32 keeps the plain loop: with
-      // one-register operands the groups only lengthen live ranges and cause spills.)
+    if constexpr (M::EB != 4) {
+      // bf16 and fp8: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling
+      // groups below keep the compiler from pulling the reads back next to their use (it
+      // otherwise waits for the LDS every two k-steps).  An fp8 operand is two LDS reads.
+      // (fp32 keeps the plain loop: with one-register operands the groups only lengthen
+      // live ranges and cause spills.)
       constexpr int PD = 4;
+      constexpr int RD = M::EB == 1 ? 2 : 1;  // LDS reads per operand
       typename M::frag a[M::NK];
 #pragma unroll
       for (int kk = 0; kk < PD && kk < M::NK; ++kk) a[kk] = M::lds_k(myrow, swz, kk, hi);
@@ -199,10 +224,10 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
 #pragma unroll
         for (int g = 0; g < FR; ++g) acc[g] = M::mma(a[kk], qf[g][kk], acc[g]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, PD < M::NK ? PD : M::NK, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, RD * (PD < M::NK ? PD : M::NK), 0);  // DS reads
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
-        if (kk + PD < M::NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kk + PD < M::NK) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, FR, 0);                     // MFMAs
       }
     } else {
@@ -242,6 +267,18 @@ __device__ __forceinline__ BlockPos block_pos(int H, int n, int splits, int cps)
   return p;
 }
 
+// The bound theta of the selection (see theta_kernel): its ordered key keeps the top THETA_BITS
+// bits.  ThetaArgs: where pass 1 writes it itself (theta non-NULL) and, for the fp8 bound, the
+// norms its margin scales with.
+constexpr int THETA_BITS = 16;
+struct ThetaArgs {
+  float* theta = nullptr;
+  int k = 0;
+  const float* qn = nullptr;
+  const float* kmax = nullptr;
+  float eta = 0.f;
+};
+
 // Max over the 16 scores of one lane, or only over those of sub-keys < n.
 template <bool FULL>
 __device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, int hi, int r0, int r1) {
@@ -259,11 +296,12 @@ __device__ __forceinline__ float lane_max(const f32x16& a, int sub_base, int n, 
 template <typename DT, int DH, int GS, int NW, int FR>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, int splits, int cps,
-                                                       float* __restrict__ gmax, int32_t* __restrict__ zero_count) {
+                                                       float* __restrict__ gmax, int32_t* __restrict__ zero_count,
+                                                       ThetaArgs ta) {
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
   constexpr int SPAN = GS <= 2 ? 1 : (1 << (GS - 2)); // chunks per group when a group spans chunks
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW, Mma<DT, DH>::EB) * CHUNK * RB];
   const BlockPos bp = block_pos(H, n, splits, cps);
   const int pair = bp.pair;
   const int64_t tile = bp.tile;
@@ -284,7 +322,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
 #pragma unroll
   for (int g = 0; g < FR; ++g) {
     const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
-    live[g] = hi == 0 && t < T;
+    live[g] = t < T;  // both lanes of a row store its group maxima (the same values)
     const int64_t r2 = (t * H + h) * 2 + c;
     gm[g] = gmax + r2 * (int64_t)MAX_GROUPS;
     // with split sub-key ranges pass 2 counts every row's candidates with atomics: the
@@ -355,6 +393,40 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
     for (int i = 0; i < NB; ++i)
       if (i < nbuf) gm[g][done + i] = buf[g][NB - nbuf + i];
   }
+  // theta of every row of the block (sub-keys not split: the block has all its group maxima),
+  // instead of the theta kernel: the row's two lanes take 64 of its 128 slots each, 16-byte
+  // pieces of their own stores, and run the descent of theta_kernel with their counts summed
+  if (ta.theta) {
+    const int ngroups = (n + (8 << GS) - 1) >> (3 + GS);
+#pragma unroll
+    for (int g = 0; g < FR; ++g) {
+      uint32_t v[MAX_GROUPS / 2];
+#pragma unroll
+      for (int p = 0; p < MAX_GROUPS / 8; ++p) {  // piece 2 p + hi: groups 8 p + 4 hi .. + 3
+        const int g0 = 8 * p + 4 * hi;
+        const f32x4 x = live[g] && g0 < ngroups ? *(const f32x4*)(gm[g] + g0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * p + e] = live[g] && g0 + e < ngroups ? ord_score(x[e]) : 0u;
+      }
+      uint32_t prefix = 0;
+#pragma unroll
+      for (int bit = 31; bit >= 32 - THETA_BITS; --bit) {
+        const uint32_t cand = prefix | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_GROUPS / 2; ++j) cnt += v[j] >= cand ? 1 : 0;
+        cnt += __shfl_xor(cnt, 32, WAVE);
+        if (cnt >= ta.k) prefix = cand;
+      }
+      const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
+      if (hi == 0 && t < T) {
+        const int64_t r2 = (t * H + h) * 2 + c;
+        float th = ngroups < ta.k ? -__builtin_inff() : score_of_ord(prefix);
+        if (ta.qn) th -= ta.eta * ta.qn[r2] * ta.kmax[pair];
+        ta.theta[r2] = th;
+      }
+    }
+  }
 }
 
 // theta: per row a lower bound of the k-th largest of its group maxima (-inf if there are
@@ -366,9 +438,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
 // 54 to 34 us at 131,072 rows.
 // Keys strictly above a bound that is below the k-th group maximum already number at least
 // k, so pass 2's cap on keys equal to the bound drops none that matter.
-constexpr int THETA_BITS = 16;
+// With group maxima of fp8 scores (qn != NULL) the k-th largest is only an estimate: the bound
+// is lowered by eta * |q half| * max |sub-key| of the pair, a few standard deviations of the
+// fp8 rounding error of a score.  Pass 2 then still counts the exact scores at or above it, and
+// a row left with fewer than k is scored exhaustively, so the bound decides only the work.
 __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gmax, int64_t rows, int ngroups, int k,
-                                                    float* __restrict__ theta) {
+                                                    float* __restrict__ theta, const float* __restrict__ qn,
+                                                    const float* __restrict__ kmax, int pairs, float eta) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -387,7 +463,40 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
     const int cnt = __popcll(__ballot(v0 >= cand)) + __popcll(__ballot(v1 >= cand));
     if (cnt >= k) prefix = cand;
   }
-  if (lane == 0) theta[row] = score_of_ord(prefix);
+  if (lane == 0) theta[row] = qn ? score_of_ord(prefix) - eta * qn[row] * kmax[row % pairs] : score_of_ord(prefix);
+}
+
+// Candidate lists of up to SORTED keys are sorted after pass 2, one thread per list, so that
+// the combine merges the two lists of a row instead of ranking every candidate against every
+// other (one wave per row).
+constexpr int SORTED = 32;
+
+// Sort one candidate list of n <= SORTED keys in place, descending: a bitonic network in
+// registers (Batcher 1968; empty slots are key 0, which sorts last).
+__device__ __forceinline__ void sort_list(uint64_t* list, int n) {
+  uint64_t L[SORTED];
+#pragma unroll
+  for (int j = 0; j < SORTED; ++j) L[j] = j < n ? list[j] : 0ull;
+#pragma unroll
+  for (int size = 2; size <= SORTED; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < SORTED; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t a = L[i], b = L[j];
+          const bool swap = desc ? a < b : a > b;
+          L[i] = swap ? b : a;
+          L[j] = swap ? a : b;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < SORTED; ++j)
+    if (j < n) list[j] = L[j];
 }
 
 // Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
@@ -583,8 +692,9 @@ __device__ void exhaustive_row(const DT* __restrict__ qhat, const DT* __restrict
 }
 
 // Rows whose candidates overflowed (more than cs / 2 in either lane's half: structured
-// data with many sub-keys above the bound) are scored again exhaustively.  A persistent
-// grid scans the counts; with no overflow it only reads them.
+// data with many sub-keys above the bound), or, under an estimated bound, that hold fewer
+// than k, are scored again exhaustively.  A persistent grid scans the counts; with neither
+// it only reads them.
 template <typename DT, int DH, int LK>
 __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t rows2, int H, int n, int k, uint64_t* __restrict__ cand,
@@ -594,12 +704,50 @@ __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qh
   const int64_t waves = (int64_t)gridDim.x * 4;
   for (int64_t base = ((int64_t)blockIdx.x * 4 + wv) * 64; base < rows2; base += waves * 64) {
     const int64_t r = base + lane;
-    uint64_t over = __ballot(r < rows2 && (count[2 * r] > cs / 2 || count[2 * r + 1] > cs / 2));
+    uint64_t over = __ballot(r < rows2 && (count[2 * r] > cs / 2 || count[2 * r + 1] > cs / 2 ||
+                                           count[2 * r] + count[2 * r + 1] < k));
     while (over) {
       const int64_t r2 = base + __builtin_ctzll(over);
       over &= over - 1;
       exhaustive_row<DT, DH, LK>(qhat, khat, r2, H, n, k, cand, cs, count, qs[wv], lane);
     }
+  }
+}
+
+// The candidate lists sorted, one thread per list (list i = 2 * row + lane half): those holding
+// 2..SORTED keys; runs after the overflow pass (whose rewritten rows are already in order).  A
+// wave takes 32 consecutive rows (64 lists): their first SORTED slots move between memory and
+// LDS in 16-byte pieces, 16 lanes per list (coalesced), and each lane sorts its own list in LDS
+// (one list per lane read directly from memory took 41 us at 131,072 rows: 64 lanes on 64
+// different lines per load, the vector L1 thrashing).
+constexpr int SORT_LD = SORTED + 2;  // keys per list in LDS: 16-byte aligned rows, spread banks
+__global__ void __launch_bounds__(256) sort_lists_kernel(uint64_t* __restrict__ cand, int cs,
+                                                         const int32_t* __restrict__ count, int64_t lists) {
+  __shared__ __attribute__((aligned(16))) uint64_t ls[4][64 * SORT_LD];
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t first = ((int64_t)blockIdx.x * 4 + wv) * 64;  // the wave's first list
+  if (first >= lists) return;
+  uint64_t* lw = ls[wv];
+  auto list_at = [&](int q) { return cand + ((first + q) >> 1) * cs + ((first + q) & 1) * (cs / 2); };
+  // load: piece c = it * 64 + lane is 16-byte piece c % 16 of list c / 16
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int c = it * 64 + lane, q = c >> 4, pc = c & 15;
+    if (first + q < lists) *(u32x4*)(lw + q * SORT_LD + 2 * pc) = *(const u32x4*)(list_at(q) + 2 * pc);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int n = first + lane < lists ? count[first + lane] : 0;
+  if (n > 1 && n <= SORTED) sort_list(lw + lane * SORT_LD, n);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // store back the same pieces (unsorted lists come back unchanged)
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int c = it * 64 + lane, q = c >> 4, pc = c & 15;
+    if (first + q < lists) *(u32x4*)(list_at(q) + 2 * pc) = *(const u32x4*)(lw + q * SORT_LD + 2 * pc);
   }
 }
 
@@ -630,9 +778,16 @@ hipError_t launch_direct(const void* qhat, const void* khat, int64_t rows, int H
   return hipGetLastError();
 }
 
+// The fp8 bound pass, where built: bf16 workloads with 256-wide halves (a 32-sub-key fp8
+// chunk then splits evenly over 4 or 8 waves).
+template <typename DT, int DH>
+constexpr bool fp8_bound_built() {
+  return sizeof(DT) == 2 && DH == 256;
+}
+
 template <typename DT, int DH, int NW, int FR>
 hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax,
-                            float* theta, uint64_t* cand, int32_t* count, int cus, hipStream_t s) {
+                            float* theta, uint64_t* cand, int32_t* count, int cus, const Fp8Bound& fb, hipStream_t s) {
   const int64_t tiles = (T + 32 * FR * NW - 1) / (32 * FR * NW);
   int gshift = 0;
   while (((n + (8 << gshift) - 1) >> (3 + gshift)) > MAX_GROUPS) ++gshift;
@@ -660,9 +815,30 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   // passes from k + 32 groups (at most 128 are formed), where the bound still leaves about
   // 100-190 candidates per row against 256 slots
   if (ngroups < (k <= 32 ? 2 * k : k + 32)) return launch_direct<DT, DH>(qhat, khat, rows, H, n, k, cand, count, s);
-#define PKM_P1(G)                                                                                       \
-  pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, splits, cps, gmax, \
-                                                           splits > 1 ? count : nullptr)
+  const bool fp8 = fb.q8 != nullptr;
+  if (fp8 && !fp8_bound_built<DT, DH>()) return hipErrorInvalidValue;
+  // without split sub-key ranges pass 1 writes theta itself
+  ThetaArgs ta;
+  if (splits == 1) {
+    ta.theta = theta;
+    ta.k = k;
+    ta.qn = fp8 ? fb.qn : nullptr;
+    ta.kmax = fb.kmax;
+    ta.eta = FP8_BOUND_ETA;
+  }
+#define PKM_P1(G)                                                                                                 \
+  do {                                                                                                            \
+    if constexpr (fp8_bound_built<DT, DH>()) {                                                                    \
+      if (fp8) {                                                                                                  \
+        pass1_kernel<uint8_t, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const uint8_t*)fb.q8, (const uint8_t*)fb.k8, T, \
+                                                                      H, n, splits, cps, gmax,                    \
+                                                                      splits > 1 ? count : nullptr, ta);          \
+        break;                                                                                                    \
+      }                                                                                                           \
+    }                                                                                                             \
+    pass1_kernel<DT, DH, G, NW, FR><<<grid, 64 * NW, 0, s>>>((const DT*)qhat, (const DT*)khat, T, H, n, splits, cps,   \
+                                                             gmax, splits > 1 ? count : nullptr, ta);             \
+  } while (0)
   switch (gshift) {
     case 0: PKM_P1(0); break;
     case 1: PKM_P1(1); break;
@@ -675,8 +851,11 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   }
 #undef PKM_P1
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (splits > 1) {
+    theta_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(gmax, rows, ngroups, k, theta, fp8 ? fb.qn : nullptr,
+                                                                   fb.kmax, 2 * H, FP8_BOUND_ETA);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (splits > 1) {
     // 8-wave blocks of 64-token waves are taken only when every CU gets one, so they never
     // split (and their LDS leaves no room for the stashes)
@@ -696,6 +875,9 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   else
     overflow_kernel<DT, DH, MAX_K><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k,
                                                                       cand, cs, count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (k <= 32)  // the combine for k <= 32 merges sorted lists
+    sort_lists_kernel<<<dim3((unsigned)((2 * rows + 255) / 256)), 256, 0, s>>>(cand, cs, count, 2 * rows);  // 64 lists a wave
   return hipGetLastError();
 }
 
@@ -710,7 +892,7 @@ constexpr bool eight_waves_built() {
 
 template <typename DT, int DH>
 hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, int n, int k, float* gmax, float* theta,
-                         uint64_t* cand, int32_t* count, hipStream_t s) {
+                         uint64_t* cand, int32_t* count, const Fp8Bound& fb, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, c = 0;
@@ -720,10 +902,10 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
   }
   if constexpr (eight_waves_built<DT, DH>()) {
     if ((T + 511) / 512 * 2 * H >= cus)
-      return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
-    return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
+      return launch_passes_nw<DT, DH, 8, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, fb, s);
+    return launch_passes_nw<DT, DH, 8, 1>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, fb, s);
   } else {
-    return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, s);
+    return launch_passes_nw<DT, DH, 4, 2>(qhat, khat, T, H, n, k, gmax, theta, cand, count, cus, fb, s);
   }
 }
 
@@ -731,9 +913,9 @@ hipError_t launch_passes(const void* qhat, const void* khat, int64_t T, int H, i
 
 hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T, int H, int d_h, int n, int k,
                                    int dtype, float* gmax, float* theta, uint64_t* cand, int32_t* count,
-                                   hipStream_t s) {
+                                   const Fp8Bound& fb, hipStream_t s) {
   if (T == 0) return hipSuccess;
-#define PKM_PASSES(DT, DHV) return launch_passes<DT, DHV>(qhat, khat, T, H, n, k, gmax, theta, cand, count, s)
+#define PKM_PASSES(DT, DHV) return launch_passes<DT, DHV>(qhat, khat, T, H, n, k, gmax, theta, cand, count, fb, s)
   if (dtype == DT_BF16) {
     switch (d_h) {
       case 64: PKM_PASSES(uint16_t, 64);

@@ -54,6 +54,9 @@ def test_workspace_size_matches_layout(P):
     want = (a(H * dq * dm * 2) + a(H * 2 * n * dq // 2 * 2) + a(dv * dm * 2) + a(dm * dv * 2) + a(T * H * dq * 4) +
             a(T * H * dq * 2) + a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * 128 * 8) + a(T * H * 2 * 2 * 4) +
             2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 4) + a(T * dv * 2))
+    # the fp8 bound (bf16, 256-wide halves): e4m3 sub-keys, their norms, the largest per (head,
+    # half), e4m3 query halves and their norms
+    want += a(H * 2 * n * 256) + a(H * 2 * n * 4) + a(H * 2 * 4) + a(T * H * 2 * 256) + a(T * H * 2 * 4)
     assert P.pkm_workspace_size(c) == want
     # without the gate there is no W1/W2 copy and no y/g buffer
     assert P.pkm_workspace_size(_cfg(P, memory_plus=0)) < want
@@ -103,6 +106,8 @@ def test_workspace_of_padded_query_halves_and_wide_k(P, d_query, k):
     want = (a(H * d_query * dm * 2) + a(H * 2 * n * dhp * 2) + a(T * H * d_query * 4) + a(T * H * 2 * dhp * 2) +
             a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * cs * 8) + a(T * H * 2 * 2 * 4) +
             2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4))
+    if dhp == 256:   # the fp8 bound of bf16 workloads
+        want += a(H * 2 * n * 256) + a(H * 2 * n * 4) + a(H * 2 * 4) + a(T * H * 2 * 256) + a(T * H * 2 * 4)
     assert P.pkm_workspace_size(c) == want
 
 

@@ -751,6 +751,69 @@ def test_wide_combine_rounding_tie_takes_exhaustive_path():
     pk.close()
 
 
+@pytest.mark.parametrize("case", [
+    dict(n_sub=4096, H=4, T=700, d_q=512, k=32),      # 8-wave blocks of 32-token waves, 16M-key sub-keys
+    dict(n_sub=1024, H=64, T=520, d_q=512, k=64),     # 8-wave blocks of 64-token waves, k > 32
+    dict(n_sub=2048, H=4, T=150, d_q=400, k=16),      # split sub-key ranges, halves padded from 200 to 256
+])
+def test_fp8_bound_and_exact_bound_select_alike(case):
+    """The bound pass from fp8 scores (bf16, 256-wide halves) and the exact one from bf16
+    scores: both forwards match the oracle stage-wise, and they select the same lists (any
+    difference would be a near-tie the rule excuses)."""
+    import sparse_key_value_amd as P
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name=f"bounds_h{case['H']}_n{case['n_sub']}", d_model=128, d_v=128, **case)
+    say(f"fp8 and exact bounds {case}")
+    wl = _G().Workload(cfg, seed=17)
+    rows = None if cfg.T * cfg.H <= 4096 else _sample_tokens(cfg.T)
+    res = {}
+    for mode in ("exact", "auto"):
+        P.pkm_set_score_bound(wl.pkm.handle, mode)
+        res[mode] = run_debug(wl)
+        full_check(wl, res[mode], rows=rows)
+    diff = res["auto"]["idx"] != res["exact"]["idx"]
+    say(f"positions selected differently by the two bounds: {int(diff.sum())} of {diff.size}")
+    assert diff.mean() < 1e-3
+    wl.close()
+
+
+def test_fp8_bound_that_overshoots_falls_back_to_exhaustive_rows():
+    """Every sub-key element is 1.09375, which fp8 rounds up to 1.125: each fp8 score overstates
+    the exact one by about 8, far beyond the bound's margin (about 1.7 here), so no exact
+    score reaches the bound and every row holds fewer than k candidates.  Each row is then
+    scored exhaustively, and the lists equal the oracle's exactly (the scores are exact in
+    fp32: sums of multiples of 1/32)."""
+    import sparse_key_value_amd as P
+    n, dh, k, T = 256, 256, 8, 6
+    K = np.full((1, 2, n, dh), 1.09375, dtype=np.float32)
+    K[0, 0, :, 0] = np.arange(n) / 16.0                 # half 0: score rises with the index
+    K[0, 1, :, 0] = np.arange(n)[::-1] / 16.0           # half 1: falls with the index
+    kb = torch.from_numpy(K).to(torch.bfloat16).cuda()
+    assert torch.equal(kb.float().cpu(), torch.from_numpy(K))       # bf16-exact
+    q = np.ones((T, 1, 2, dh), dtype=np.float32)
+    q[1::2, 0, 1, :] = 0.5                                           # other scales of half 1
+    qb = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    wq = torch.zeros((64, 2 * dh), dtype=torch.bfloat16, device="cuda")
+    vals = torch.zeros((n * n, 8), dtype=torch.bfloat16, device="cuda")
+    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=2 * dh, n_sub=n, k=k, d_value=8, dtype="bf16", qk_norm=0,
+                            memory_plus=0, max_tokens=T, W_q=wq, subkeys=kb, values=vals)
+    q64 = q.astype(np.float64).reshape(T, 1, 2 * dh)
+    sel = O.select(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64), k)
+    assert sel["half_idx"][0, 0, 0].tolist() == list(range(n - 1, n - 1 - k, -1))
+    for mode in ("auto", "exact"):
+        P.pkm_set_score_bound(pk.handle, mode)
+        hi_ = torch.empty((T, 1, 2, k), dtype=torch.int32, device="cuda")
+        hs_ = torch.empty((T, 1, 2, k), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, 1, k), dtype=torch.int32, device="cuda")
+        sc = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+        w = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
+        P.pkm_select(pk.handle, qb, T, hi_, hs_, idx, sc, w)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"], err_msg=mode)
+        np.testing.assert_array_equal(hs_.cpu().numpy(), sel["half_score"].astype(np.float32), err_msg=mode)
+        np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"], err_msg=mode)
+    pk.close()
+
+
 @pytest.mark.parametrize("shape", [
     dict(n_sub=256, T=300),             # few sub-keys: every row scored exhaustively
     dict(n_sub=1100, T=600, H=64),      # the two MFMA passes in 8-wave blocks, theta, overflow scan
