@@ -59,6 +59,19 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t idx) {
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
 __device__ __forceinline__ float key_score(uint64_t k) { return score_of_ord((uint32_t)(k >> 32)); }
 
+// The other half of the wave (lane l ^ 32) on gfx950's v_permlane32_swap, a VALU op, rather
+// than ds_bpermute (an LDS round trip, whose wait also waits for every LDS read in flight).
+// swap32(x) = {r0, r1} with r0 = x in lanes 0-31 and lane l - 32's x in lanes 32-63, r1 = lane
+// l + 32's x in lanes 0-31 and x in lanes 32-63: every lane holds its own and its partner's.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int add_xor32(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(r[0] + r[1]);
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((uint32_t)v, m, WAVE);
   uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, WAVE);

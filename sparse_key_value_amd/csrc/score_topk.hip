@@ -22,11 +22,10 @@
 //      theta  picks per row the k-th largest group maximum, rounded down to its top 16
 //             bits: at least k sub-keys reach it, so it bounds the row's k-th best score
 //             from below (found bit by bit with wave ballots);
-//      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring
-//             above the bound, and of those scoring exactly the bound the first k each
-//             lane sees (lowest indices first), as 64-bit keys to the row's candidate
-//             list (cand_slots(k) slots, half per lane).  With random-like data and
-//             k = 32 about 37 of 4,096 per row.
+//      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring at
+//             or above the bound as a 64-bit key to the row's candidate list
+//             (cand_slots(k) slots, half per lane).  With random-like data and k = 32
+//             about 37 of 4,096 per row (48 with the fp8 bound's margin).
 //    A lane's count may exceed its half of the slots (structured data); that row is then
 //    scored exhaustively by the overflow kernel before the combine kernel reads it.
 //  * With fewer than 2k groups (k + 32 for k > 32: few sub-keys for the k asked for) the
@@ -131,9 +130,10 @@ __device__ __forceinline__ int sub_of(int sub_base, int r, int hi) { return sub_
 // chunk ch - 1 runs right after the barrier, beside the first group's MFMAs of chunk ch,
 // and its MFMAs of chunk ch beside the first group's selection), which keeps the matrix
 // core fed through both halves.  The accumulators live across the barrier for that.
-template <typename DT, int DH, int NW, int FR, typename F>
+template <typename DT, int DH, int NW, int FR, bool TWO, typename F>
 __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __restrict__ khat, int64_t T, int H, int n,
-                                      int pair, int64_t tile, int c0, int c1, uint8_t* ks, F&& on_tile) {
+                                      int pair, int64_t tile, int c0, int c1, uint8_t* ka, uint8_t* kb,
+                                      F&& on_tile) {
   using M = Mma<DT, DH>;
   constexpr int RB = DH * M::EB;          // bytes per sub-key row
   constexpr int U16 = RB / 16;            // 16-byte units per row
@@ -151,7 +151,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   }
 
   const uint8_t* kbase = (const uint8_t*)(khat + (size_t)pair * n * DH);
-  // Chunk ch goes to LDS buffer b by direct global->LDS loads: wave wv's i-th load fills
+  // Chunk ch goes to an LDS buffer by direct global->LDS loads: wave wv's i-th load fills
   // the 64 consecutive 16-byte units starting at unit (wv * DPW + i) * 64, and each lane
   // fetches the global unit that belongs at its LDS unit under the XOR swizzle.  Rows past
   // n_sub load row 0 instead (in bounds); their scores are masked by every consumer.
@@ -164,7 +164,7 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
   static_assert(DPW >= 1 && CHUNK * U16 % (64 * NW) == 0, "chunk must split evenly over the waves");
   const __amdgpu_buffer_rsrc_t krsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, n * RB, 0x00020000);  // raw, 32-bit dwords
-  auto fetch = [&](int ch, int buf) {
+  auto fetch = [&](int ch, uint8_t* dst) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int p = (wv * DPW + i) * 64 + lane;          // LDS unit this lane fills
@@ -176,72 +176,106 @@ __device__ __forceinline__ void sweep(const DT* __restrict__ qhat, const DT* __r
       // them, and every reload from scratch waited for all loads in flight
       const uint32_t off = (uint32_t)sub * RB + (uint32_t)col * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krsrc, (void __attribute__((address_space(3)))*)(ks + buf * CHUNK * RB + (wv * DPW + i) * 64 * 16), 16, off,
-          0, 0, 0);
+          krsrc, (void __attribute__((address_space(3)))*)(dst + (wv * DPW + i) * 64 * 16), 16, off, 0, 0, 0);
     }
   };
   const int swz = (lane & 31) % U16;
 
-  // The block sweeps chunks [c0, c1).  SC chunks per barrier: the chunk at position lc =
-  // ch - c0 lives in LDS buffer lc % (2 SC); the SC chunks after a barrier are loaded into
-  // the other SC buffers while they are scored
+  // The block sweeps chunks [c0, c1) in groups of SC chunks, one barrier per group.  The
+  // groups alternate between two LDS buffers (ka, kb: SC chunks each): a group is scored
+  // from one while the next group's chunks load into the other.  TWO: the buffers are two
+  // LDS arrays and the group's code is inlined once for each, so that the compiler knows
+  // that the MFMA operand reads cannot touch the buffer the loads in flight are filling;
+  // pass 2 needs it, where the compiler otherwise waited for those loads (and for the
+  // candidate stores, which share their counter) before every chunk.  Otherwise (pass 1,
+  // whose registers do not allow two copies) kb follows ka in one array and one loop
+  // indexes the 2 SC chunk buffers.
   constexpr int SC = chunks_per_barrier(NW, M::EB);
+  constexpr int CB = CHUNK * RB;  // bytes per chunk buffer
   // the lagging group (wave-uniform)
   const bool lag = NW == 8 && wv >= 4;
   f32x16 acc[FR];
-#pragma unroll
-  for (int j = 0; j < SC; ++j)
-    if (c0 + j < c1) fetch(c0 + j, j);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
-  __syncthreads();
-  for (int ch = c0; ch < c1; ++ch) {
-    const int lc = ch - c0;
-    const int buf = lc % (2 * SC);
-    // the other SC buffers were last read before the barrier that ended the previous group
-    if (lc % SC == 0) {
-#pragma unroll
-      for (int j = 0; j < SC; ++j)
-        if (ch + SC + j < c1) fetch(ch + SC + j, (lc + SC + j) % (2 * SC));
-    }
-    if (lag && lc > 0) on_tile(ch - 1, (const f32x16*)acc);
-    const uint8_t* myrow = ks + buf * CHUNK * RB + (lane & 31) * RB;
+  // bf16 and fp8: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling groups
+  // below keep the compiler from pulling the reads back next to their use (it otherwise
+  // waits for the LDS every two k-steps).  An fp8 operand is two LDS reads.  (Reading the
+  // next fp8 chunk's operands before the current chunk's selection was 5-10 us slower.)
+  // (fp32 keeps the plain loop: with one-register operands the groups only lengthen live
+  // ranges and cause spills.)
+  constexpr int PD = 4 < M::NK ? 4 : M::NK;
+  constexpr int RD = M::EB == 1 ? 2 : 1;  // LDS reads per operand
+  // the scores of the chunk at this lane's row `row`
+  auto score_chunk = [&](const uint8_t* row) {
 #pragma unroll
     for (int g = 0; g < FR; ++g) acc[g] = f32x16{};
     if constexpr (M::EB != 4) {
-      // bf16 and fp8: the LDS operands run PD k-steps ahead of the MFMAs; the scheduling
-      // groups below keep the compiler from pulling the reads back next to their use (it
-      // otherwise waits for the LDS every two k-steps).  An fp8 operand is two LDS reads.
-      // (fp32 keeps the plain loop: with one-register operands the groups only lengthen
-      // live ranges and cause spills.)
-      constexpr int PD = 4;
-      constexpr int RD = M::EB == 1 ? 2 : 1;  // LDS reads per operand
       typename M::frag a[M::NK];
 #pragma unroll
-      for (int kk = 0; kk < PD && kk < M::NK; ++kk) a[kk] = M::lds_k(myrow, swz, kk, hi);
+      for (int kk = 0; kk < PD; ++kk) a[kk] = M::lds_k(row, swz, kk, hi);
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
-        if (kk + PD < M::NK) a[kk + PD] = M::lds_k(myrow, swz, kk + PD, hi);
+        if (kk + PD < M::NK) a[kk + PD] = M::lds_k(row, swz, kk + PD, hi);
 #pragma unroll
         for (int g = 0; g < FR; ++g) acc[g] = M::mma(a[kk], qf[g][kk], acc[g]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, RD * (PD < M::NK ? PD : M::NK), 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, RD * PD, 0);  // DS reads
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
         if (kk + PD < M::NK) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FR, 0);                     // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, FR, 0);     // MFMAs
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < M::NK; ++kk) {
-        const typename M::frag a = M::lds_k(myrow, swz, kk, hi);
+        const typename M::frag b = M::lds_k(row, swz, kk, hi);
 #pragma unroll
-        for (int g = 0; g < FR; ++g) acc[g] = M::mma(a, qf[g][kk], acc[g]);
+        for (int g = 0; g < FR; ++g) acc[g] = M::mma(b, qf[g][kk], acc[g]);
       }
     }
-    if (!lag) on_tile(ch, (const f32x16*)acc);
-    if (lc % SC == SC - 1 || ch + 1 == c1) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+#pragma unroll
+  for (int j = 0; j < SC; ++j)
+    if (c0 + j < c1) fetch(c0 + j, ka + j * CB);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
+  __syncthreads();
+  if constexpr (TWO) {
+    auto group = [&](int g0, const uint8_t* cur, uint8_t* nxt) {
+#pragma unroll
+      for (int j = 0; j < SC; ++j)
+        if (g0 + SC + j < c1) fetch(g0 + SC + j, nxt + j * CB);
+      const uint8_t* rows = cur + (lane & 31) * RB;  // this lane's row of chunk 0 of the group
+      for (int j = 0; j < SC && g0 + j < c1; ++j) {
+        const int ch = g0 + j;
+        if (lag && ch > c0) on_tile(ch - 1, (const f32x16*)acc);
+        score_chunk(rows + j * CB);
+        if (!lag) on_tile(ch, (const f32x16*)acc);
+      }
+      // this group's reads are done and the next group's chunks have landed
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
+    };
+    for (int g0 = c0; g0 < c1; g0 += 2 * SC) {
+      group(g0, ka, kb);
+      if (g0 + SC < c1) group(g0 + SC, kb, ka);
+    }
+  } else {
+    // the chunk at position lc = ch - c0 lives in buffer lc % (2 SC) of ka (kb = ka + SC CB)
+    const uint8_t* rows = ka + (lane & 31) * RB;
+    for (int ch = c0; ch < c1; ++ch) {
+      const int lc = ch - c0;
+      const int buf = lc % (2 * SC);
+      // the other SC buffers were last read before the barrier that ended the previous group
+      if (lc % SC == 0) {
+#pragma unroll
+        for (int j = 0; j < SC; ++j)
+          if (ch + SC + j < c1) fetch(ch + SC + j, ka + ((lc + SC + j) % (2 * SC)) * CB);
+      }
+      if (lag && lc > 0) on_tile(ch - 1, (const f32x16*)acc);
+      score_chunk(rows + buf * CB);
+      if (!lag) on_tile(ch, (const f32x16*)acc);
+      if (lc % SC == SC - 1 || ch + 1 == c1) {  // the group's last chunk
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
     }
   }
   if (lag) on_tile(c1 - 1, (const f32x16*)acc);
@@ -301,7 +335,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   constexpr int RB = DH * Mma<DT, DH>::EB;
   constexpr int GPC = GS <= 2 ? (4 >> GS) : 1;        // groups finished per chunk (or per span)
   constexpr int SPAN = GS <= 2 ? 1 : (1 << (GS - 2)); // chunks per group when a group spans chunks
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW, Mma<DT, DH>::EB) * CHUNK * RB];
+  constexpr int KB = chunks_per_barrier(NW, Mma<DT, DH>::EB) * CHUNK * RB;  // bytes per buffer
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * KB];
   const BlockPos bp = block_pos(H, n, splits, cps);
   const int pair = bp.pair;
   const int64_t tile = bp.tile;
@@ -351,7 +386,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
       nbuf = 0;
     }
   };
-  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR, false>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, ks + KB, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     float mg[FR][GPC];
 #pragma unroll
@@ -362,7 +397,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
         constexpr int RW = GS <= 2 ? (4 << GS) : 16;
         const float m = full ? lane_max<true>(acc[g], ch * CHUNK, n, hi, j * RW, j * RW + RW)
                              : lane_max<false>(acc[g], ch * CHUNK, n, hi, j * RW, j * RW + RW);
-        mg[g][j] = fmaxf(m, __shfl_xor(m, 32, WAVE));
+        mg[g][j] = max_xor32(m);
       }
     }
     if (GS <= 2) {
@@ -395,29 +430,55 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
   }
   // theta of every row of the block (sub-keys not split: the block has all its group maxima),
   // instead of the theta kernel: the row's two lanes take 64 of its 128 slots each, 16-byte
-  // pieces of their own stores, and run the descent of theta_kernel with their counts summed
+  // pieces of their own stores, and run the descent of theta_kernel with their counts summed.
+  // Every group maximum of a row lies in [vmin, vmax], so theta shares their leading bits:
+  // the descent starts at the highest bit where the two differ (the wave's highest, found
+  // with five ballots, so that the steps stay uniform; a row whose bit is already settled
+  // keeps its prefix at that step).  That skips the sign and most exponent bits, about a
+  // third of the steps, with the result of the full descent.
   if (ta.theta) {
     const int ngroups = (n + (8 << GS) - 1) >> (3 + GS);
 #pragma unroll
     for (int g = 0; g < FR; ++g) {
       uint32_t v[MAX_GROUPS / 2];
+      uint32_t vmin = 0xFFFFFFFFu, vmax = 0u;
 #pragma unroll
       for (int p = 0; p < MAX_GROUPS / 8; ++p) {  // piece 2 p + hi: groups 8 p + 4 hi .. + 3
         const int g0 = 8 * p + 4 * hi;
         const f32x4 x = live[g] && g0 < ngroups ? *(const f32x4*)(gm[g] + g0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * p + e] = live[g] && g0 + e < ngroups ? ord_score(x[e]) : 0u;
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = live[g] && g0 + e < ngroups;
+          const uint32_t o = ord_score(x[e]);
+          v[4 * p + e] = ok ? o : 0u;
+          vmin = ok && o < vmin ? o : vmin;
+          vmax = ok && o > vmax ? o : vmax;
+        }
       }
-      uint32_t prefix = 0;
+      {  // the row's two lanes
+        const auto a = __builtin_amdgcn_permlane32_swap(vmin, vmin, false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(vmax, vmax, false, false);
+        vmin = a[0] < a[1] ? a[0] : a[1];
+        vmax = b[0] > b[1] ? b[0] : b[1];
+      }
+      const uint32_t d = vmin ^ vmax;
+      const int hb = d ? 31 - __builtin_clz(d) : 0;
+      uint32_t prefix = vmax & ~((2u << hb) - 1u);  // the bits above hb (none for hb = 31)
+      int top = 0;
+#pragma unroll
+      for (int b5 = 4; b5 >= 0; --b5)
+        if (__ballot(hb >= (top | (1 << b5)))) top |= 1 << b5;
 #pragma unroll
       for (int bit = 31; bit >= 32 - THETA_BITS; --bit) {
+        if (bit > top) continue;
         const uint32_t cand = prefix | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < MAX_GROUPS / 2; ++j) cnt += v[j] >= cand ? 1 : 0;
-        cnt += __shfl_xor(cnt, 32, WAVE);
+        cnt = add_xor32(cnt);
         if (cnt >= ta.k) prefix = cand;
       }
+      prefix &= ~((1u << (32 - THETA_BITS)) - 1u);
       const int64_t t = tile * (32 * FR * NW) + wv * (32 * FR) + g * 32 + (lane & 31);
       if (hi == 0 && t < T) {
         const int64_t r2 = (t * H + h) * 2 + c;
@@ -499,9 +560,9 @@ __device__ __forceinline__ void sort_list(uint64_t* list, int n) {
     if (j < n) list[j] = L[j];
 }
 
-// Pass 2: write the candidates of every row (keys above theta, and up to k per lane at
-// theta).  Each of a token's two lanes owns `half` of the row's 2 * half slots and counts
-// its own candidates.
+// Pass 2: write the candidates of every row (keys at or above theta; with split sub-key
+// ranges only the first k per lane of those equal to theta).  Each of a token's two lanes
+// owns `half` of the row's 2 * half slots and counts its own candidates.
 template <typename DT, int DH, int NW, int FR, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __restrict__ qhat, const DT* __restrict__ khat,
                                                        int64_t T, int H, int n, int k, int splits, int cps,
@@ -520,7 +581,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
   constexpr int STASH_FIT = (160 * 1024 / (8 / NW) - LDS_USED) / (FR * NW * 64 * 8);
   constexpr int STASH = SPLIT ? (STASH_FIT < 16 ? STASH_FIT : 16) : 1;
   static_assert(STASH >= 1, "no LDS left for the candidate stash");
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2 * chunks_per_barrier(NW) * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ka[chunks_per_barrier(NW) * CHUNK * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t kb[chunks_per_barrier(NW) * CHUNK * RB];
   __shared__ __attribute__((aligned(16))) float stage[NW * 64 * SROW];
   __shared__ uint64_t stash[SPLIT ? STASH * FR * NW * 64 : 1];
   const BlockPos bp = block_pos(H, n, splits, cps);
@@ -556,7 +618,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
     for (int i = 0; i < nst; ++i)
       if (base + i < half) d[base + i] = stash_at(g, i);
   };
-  sweep<DT, DH, NW, FR>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ks, [&](int ch, const f32x16* acc) {
+  sweep<DT, DH, NW, FR, true>(qhat, khat, T, H, n, pair, tile, bp.c0, bp.c1, ka, kb, [&](int ch, const f32x16* acc) {
     const bool full = (ch + 1) * CHUNK <= n;
     // bit 16 g + r: score r of token fragment g reaches the bound.  The sign bits of the
     // differences are shifted in with v_alignbit: two VALU ops per score and no lane
@@ -588,34 +650,54 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass2_kernel(const DT* __rest
         for (int j = 0; j < 4; ++j)
           *(f32x4*)(my + 16 * g + 4 * j) = f32x4{acc[g][4 * j], acc[g][4 * j + 1], acc[g][4 * j + 2], acc[g][4 * j + 3]};
     }
-    while (m) {
-      const int b = __builtin_ctz(m);  // fragment 0 first, ascending positions: the order of a scan
-      m &= m - 1;
-      const int g = b >> 4, r = b & 15;
-      const float s = my[b];
-      const int sub = sub_of(ch * CHUNK, r, hi);
-      int cn = g ? cnt[FR - 1] : cnt[0];
-      int e = g ? eq[FR - 1] : eq[0];
-      bool take = true;
-      if (s == (g ? thr[FR - 1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
-      if (take) {
-        if constexpr (SPLIT) {  // split sub-key ranges share the row's lane-half list
+    if constexpr (SPLIT) {  // split sub-key ranges share the row's lane-half list
+      while (m) {
+        const int b = __builtin_ctz(m);  // fragment 0 first, ascending positions: the order of a scan
+        m &= m - 1;
+        const int g = b >> 4, r = b & 15;
+        const float s = my[b];
+        const int sub = sub_of(ch * CHUNK, r, hi);
+        int cn = g ? cnt[FR - 1] : cnt[0];
+        int e = g ? eq[FR - 1] : eq[0];
+        bool take = true;
+        if (s == (g ? thr[FR - 1] : thr[0])) take = e++ < k;  // exact ties with the bound: the first k suffice
+        if (take) {
           if (cn == STASH) {
             publish(g, cn);
             cn = 0;
           }
           stash_at(g, cn) = make_key(s, (uint32_t)sub);
-        } else if (cn < half) {
-          (g ? dst[FR - 1] : dst[0])[cn] = make_key(s, (uint32_t)sub);
+          ++cn;
         }
-        ++cn;
+        if (g) {
+          cnt[FR - 1] = cn;
+          eq[FR - 1] = e;
+        } else {
+          cnt[0] = cn;
+          eq[0] = e;
+        }
       }
-      if (g) {
-        cnt[FR - 1] = cn;
-        eq[FR - 1] = e;
-      } else {
-        cnt[0] = cn;
-        eq[0] = e;
+    } else {
+      // The score of the lane's next hit is read from LDS before the current hit's key is
+      // built, so that part of the read's latency overlaps that work.  The rounds have no
+      // branches: a full list takes further keys in its last slot
+      // (the row then goes to the overflow pass, which rewrites its list), and keys equal to
+      // the bound are all taken (capping them only spares the overflow pass on structured
+      // data, and cost a compare and two branches a round).
+      int b = m ? __builtin_ctz(m) : 0;  // fragment 0 first, ascending positions: the order of a scan
+      float s = my[b];
+      while (m) {
+        const int bh = b;
+        const float sh = s;
+        m &= m - 1;
+        b = m ? __builtin_ctz(m) : 0;
+        s = my[b];
+        const int g = bh >> 4, r = bh & 15;
+        const uint64_t key = make_key(sh, (uint32_t)sub_of(ch * CHUNK, r, hi));
+        const int cn = g ? cnt[FR - 1] : cnt[0];
+        (g ? dst[FR - 1] : dst[0])[cn < half ? cn : half - 1] = key;
+        cnt[0] += g ? 0 : 1;
+        if constexpr (FR == 2) cnt[1] += g;
       }
     }
   });
