@@ -72,9 +72,39 @@ __device__ __forceinline__ int add_xor32(int x) {
   return (int)(r[0] + r[1]);
 }
 
+// x of lane l ^ s for s = 1, 2, 4, ..., 32 (a constant once the caller's loop is unrolled), on
+// the VALU rather than through ds_bpermute: DPP quad permutes for 1 and 2, a row half-mirror
+// (l ^ 7) or row mirror (l ^ 15) followed by a quad reversal (l ^ 3) or half-mirror for 4 and
+// 8, and v_permlane16_swap / v_permlane32_swap for 16 and 32 (each returns a lane's own value
+// and its partner's, in an order set by the lane's bit s).
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int s) {
+  constexpr int QXOR1 = 0xB1, QXOR2 = 0x4E, QREV = 0x1B, ROW_MIRROR = 0x140, ROW_HALF_MIRROR = 0x141;
+  switch (s) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, QXOR1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, QXOR2, 0xF, 0xF, false);
+    case 4: {
+      const int t = __builtin_amdgcn_mov_dpp((int)x, ROW_HALF_MIRROR, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_mov_dpp(t, QREV, 0xF, 0xF, false);
+    }
+    case 8: {
+      const int t = __builtin_amdgcn_mov_dpp((int)x, ROW_MIRROR, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_mov_dpp(t, ROW_HALF_MIRROR, 0xF, 0xF, false);
+    }
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      return (__lane_id() & 16) ? r[0] : r[1];
+    }
+    case 32: {
+      const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      return (__lane_id() & 32) ? r[0] : r[1];
+    }
+    default: return (uint32_t)__shfl_xor((int)x, s, WAVE);
+  }
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m, WAVE);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, WAVE);
+  const uint32_t lo = xor_lane_u32((uint32_t)v, m);
+  const uint32_t hi = xor_lane_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
@@ -120,7 +150,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
-  for (int m = 1; m < WAVE; m <<= 1) v += __shfl_xor(v, m, WAVE);
+  for (int m = 1; m < WAVE; m <<= 1) v += __uint_as_float(xor_lane_u32(__float_as_uint(v), m));
   return v;
 }
 
