@@ -38,7 +38,9 @@ struct Stair {
   uint8_t rect_col[32];   // ceil(k / (a + 1)) - 1: rows 0..a x columns 0..rect_col[a] hold >= k cells
 };
 
-// Sort 64 keys held one per lane in descending order (lane 0 ends with the largest).
+// Sort 64 keys held one per lane in descending order (lane 0 ends with the largest).  A
+// compare-exchange keeps x when (x > o) matches the side's keep-the-larger flag, else takes o:
+// one 64-bit compare and two selects (building both the max and the min took six).
 __device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
 #pragma unroll
   for (int size = 2; size <= 64; size <<= 1) {
@@ -46,7 +48,7 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const uint64_t o = shfl_xor_u64(x, stride);
       const bool take_max = ((lane & size) == 0) == ((lane & stride) == 0);
-      x = take_max ? (x > o ? x : o) : (x > o ? o : x);
+      x = (x > o) == take_max ? x : o;
     }
   }
   return x;
@@ -61,17 +63,18 @@ __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lan
       if (stride == 1) {
         // within the lane: elements 2l and 2l+1; block direction from bit `size` of e = 2l
         const bool desc = ((2 * lane) & size) == 0;
-        const uint64_t mx = x0 > x1 ? x0 : x1, mn = x0 > x1 ? x1 : x0;
-        x0 = desc ? mx : mn;
-        x1 = desc ? mn : mx;
+        const bool keep = (x0 > x1) == desc;  // x0 already on its side
+        const uint64_t t = x0;
+        x0 = keep ? x0 : x1;
+        x1 = keep ? x1 : t;
       } else {
         const int lx = stride >> 1;  // partner lane: e ^ stride = 2 * (lane ^ lx) + slot
         const uint64_t o0 = shfl_xor_u64(x0, lx), o1 = shfl_xor_u64(x1, lx);
         const bool desc = ((2 * lane) & size) == 0;
         const bool lower = (lane & lx) == 0;
         const bool take_max = desc == lower;
-        x0 = take_max ? (x0 > o0 ? x0 : o0) : (x0 > o0 ? o0 : x0);
-        x1 = take_max ? (x1 > o1 ? x1 : o1) : (x1 > o1 ? o1 : x1);
+        x0 = (x0 > o0) == take_max ? x0 : o0;
+        x1 = (x1 > o1) == take_max ? x1 : o1;
       }
     }
   }

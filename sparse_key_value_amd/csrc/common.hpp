@@ -127,13 +127,9 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
   for (int size = 2; size <= WAVE; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t other = shfl_xor_u64(key, stride);
-      bool desc_block = (lane & size) == 0;
-      bool lower = (lane & stride) == 0;
-      bool take_max = (desc_block == lower);
-      uint64_t mx = key > other ? key : other;
-      uint64_t mn = key > other ? other : key;
-      key = take_max ? mx : mn;
+      const uint64_t other = shfl_xor_u64(key, stride);
+      const bool take_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      key = (key > other) == take_max ? key : other;  // one compare, two selects
     }
   }
   return key;
