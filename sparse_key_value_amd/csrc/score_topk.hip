@@ -529,8 +529,9 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
 
 // Candidate lists of up to SORTED keys are sorted after pass 2, one thread per list, so that
 // the combine merges the two lists of a row instead of ranking every candidate against every
-// other (one wave per row).
+// other (one wave per row); batches under SORT_MIN_ROWS rows skip it (see the launch).
 constexpr int SORTED = 32;
+constexpr int64_t SORT_MIN_ROWS = 32768;  // rows (T x H x 2) from which the lists are sorted
 
 // Sort one candidate list of n <= SORTED keys in place, descending: a bitonic network in
 // registers (Batcher 1968; empty slots are key 0, which sorts last).
@@ -958,7 +959,11 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
     overflow_kernel<DT, DH, MAX_K><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k,
                                                                       cand, cs, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (k <= 32)  // the combine for k <= 32 merges sorted lists
+  // the combine for k <= 32 merges sorted lists and ranks unsorted ones; sorting pays from about
+  // 32,768 rows (T x H x 2) on: below that its ~12 us of load and sort latency exceeds what the
+  // merge saves (256 tokens x 4 heads: sort 12.8 + combine 8.4 us against a ranking combine of
+  // 8.7; at 4,096 tokens both 37-38 us; at 16,384 tokens 43 + 74 against about 137)
+  if (k <= 32 && rows >= SORT_MIN_ROWS)
     sort_lists_kernel<<<dim3((unsigned)((2 * rows + 255) / 256)), 256, 0, s>>>(cand, cs, count, 2 * rows);  // 64 lists a wave
   return hipGetLastError();
 }
