@@ -47,7 +47,8 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const uint64_t o = shfl_xor_u64(x, stride);
-      const bool take_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      // keep the larger where bit `size` and bit `stride` of the lane agree (a constant lane mask)
+      const bool take_max = lane_in(~(lanes_bit_clear(size) ^ lanes_bit_clear(stride)));
       x = (x > o) == take_max ? x : o;
     }
   }
@@ -62,7 +63,7 @@ __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lan
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride == 1) {
         // within the lane: elements 2l and 2l+1; block direction from bit `size` of e = 2l
-        const bool desc = ((2 * lane) & size) == 0;
+        const bool desc = lane_in(lanes_bit_clear(size >> 1));  // bit `size` of element 2 lane clear
         const bool keep = (x0 > x1) == desc;  // x0 already on its side
         const uint64_t t = x0;
         x0 = keep ? x0 : x1;
@@ -70,9 +71,8 @@ __device__ __forceinline__ void sort128_desc(uint64_t& x0, uint64_t& x1, int lan
       } else {
         const int lx = stride >> 1;  // partner lane: e ^ stride = 2 * (lane ^ lx) + slot
         const uint64_t o0 = shfl_xor_u64(x0, lx), o1 = shfl_xor_u64(x1, lx);
-        const bool desc = ((2 * lane) & size) == 0;
-        const bool lower = (lane & lx) == 0;
-        const bool take_max = desc == lower;
+        // keep the larger where bit `size` of element 2 lane and bit lx of the lane agree
+        const bool take_max = lane_in(~(lanes_bit_clear(size >> 1) ^ lanes_bit_clear(lx)));
         x0 = (x0 > o0) == take_max ? x0 : o0;
         x1 = (x1 > o1) == take_max ? x1 : o1;
       }

@@ -107,6 +107,15 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t hi = xor_lane_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
+// The lanes of a wave whose bit s (a power of two) is clear, as a 64-bit lane mask; and a
+// lane's bit of a wave-uniform mask, read from the mask itself (no per-lane arithmetic: the
+// select that uses it takes the mask as its condition).
+__device__ __forceinline__ constexpr uint64_t lanes_bit_clear(int s) {
+  return s == 1 ? 0x5555555555555555ull : s == 2 ? 0x3333333333333333ull : s == 4 ? 0x0F0F0F0F0F0F0F0Full
+       : s == 8 ? 0x00FF00FF00FF00FFull : s == 16 ? 0x0000FFFF0000FFFFull : s == 32 ? 0x00000000FFFFFFFFull : ~0ull;
+}
+__device__ __forceinline__ bool lane_in(uint64_t mask) { return __builtin_amdgcn_inverse_ballot_w64(mask); }
+
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   uint32_t lo = __shfl((uint32_t)v, src, WAVE);
   uint32_t hi = __shfl((uint32_t)(v >> 32), src, WAVE);
@@ -128,7 +137,8 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key, int lane) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const uint64_t other = shfl_xor_u64(key, stride);
-      const bool take_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      // keep the larger where bit `size` and bit `stride` of the lane agree
+      const bool take_max = lane_in(~(lanes_bit_clear(size) ^ lanes_bit_clear(stride)));
       key = (key > other) == take_max ? key : other;  // one compare, two selects
     }
   }
