@@ -101,7 +101,12 @@ typedef struct pkm_handle pkm_handle; /* opaque */
  *   idx        [T, H, k]     int32    final flat indices a*n_sub + b, best first
  *   score      [T, H, k]     fp32     final scores
  *   w          [T, H, k]     fp32     softmax weights
- *   y          [T, d_value]  fp32     gathered values before the gate          */
+ *   y          [T, d_value]  fp32     gathered values before the gate
+ *   theta      [T, H, 2]     fp32     the per-half selection bound of the two scoring passes
+ *                                     (unspecified when every row is scored exhaustively:
+ *                                     fewer than 2k groups of sub-keys, k + 32 for k > 32)
+ *   counts     [T, H, 2, 2]  int32    candidates per lane half after the overflow pass
+ *                                     (same condition)                                    */
 typedef struct {
   void* qhat;
   int32_t* half_idx;
@@ -110,6 +115,8 @@ typedef struct {
   float* score;
   float* w;
   float* y;
+  float* theta;
+  int32_t* counts;
 } pkm_debug_ptrs;
 
 /* Bytes of device workspace a handle with this config needs (0 if the config is

@@ -40,7 +40,8 @@ class pkm_config(ctypes.Structure):
 
 
 class pkm_debug_ptrs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("qhat", "half_idx", "half_score", "idx", "score", "w", "y")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("qhat", "half_idx", "half_score", "idx", "score", "w", "y", "theta",
+                                               "counts")]
 
 
 class engram_config(ctypes.Structure):

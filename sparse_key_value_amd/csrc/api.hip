@@ -222,6 +222,9 @@ int run_forward(pkm_handle* h, const void* x, int64_t T, void* out, const pkm_de
     if (dbg->idx) PKM_HIP(hipMemcpyAsync(dbg->idx, idx, nsel * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->score) PKM_HIP(hipMemcpyAsync(dbg->score, h->at(L.sc), nsel * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->w) PKM_HIP(hipMemcpyAsync(dbg->w, w, nsel * 4, hipMemcpyDeviceToDevice, s));
+    const size_t rows = (size_t)T * H * 2;
+    if (dbg->theta) PKM_HIP(hipMemcpyAsync(dbg->theta, h->at(L.theta), rows * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->counts) PKM_HIP(hipMemcpyAsync(dbg->counts, h->at(L.count), rows * 2 * 4, hipMemcpyDeviceToDevice, s));
   }
   return PKM_OK;
 }

@@ -814,6 +814,95 @@ def test_fp8_bound_that_overshoots_falls_back_to_exhaustive_rows():
     pk.close()
 
 
+def _ord_key(x):
+    """float32 -> the kernels' ordered 32-bit key (a larger float has a larger key; -0 as +0)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    b[b == 0x80000000] = 0
+    return np.where((b & 0x80000000) != 0, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def _of_ord_key(o):
+    o = np.asarray(o, dtype=np.uint32)
+    return np.where((o & 0x80000000) != 0, o & np.uint32(0x7FFFFFFF), ~o).astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(n_sub=1100, T=600, H=64),      # 8-wave blocks, sub-keys not split: the bound in pass 1's tail
+    dict(n_sub=1024, T=300, H=2),       # a small batch: split sub-key ranges, the bound from theta_kernel
+])
+def test_selection_bound_is_the_kth_group_maximum(shape):
+    """The bound the two scoring passes select against ("Memory Layers at Scale" digest, product-key
+    search: only the sub-keys that can be among a half's k best need be kept).  With the exact
+    bound it is the k-th largest of the row's group maxima rounded down to the top 16 bits of its
+    ordered key, so at least k sub-keys reach it, and the candidate counts are the scores at or
+    above it; with the fp8 bound it is that value for fp8 scores less a margin of
+    0.006 |q_c| max|K_c|.  Per (token, head, half), from the GPU's own q-hat and K-hat bytes in
+    float64.  The results never depend on the bound (exact counts catch one set too high), so
+    this is what pins pass 1's group maxima, their cross-lane maxima and the bit descent."""
+    import sparse_key_value_amd as P
+    G = _G()
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name="bound", d_v=64, d_model=256, memory_plus=False, **shape)
+    say(f"selection bound {shape}")
+    wl = G.Workload(cfg, seed=31)
+    T, H, k, n, dh = wl.T, cfg.H, cfg.k, cfg.n_sub, cfg.d_h
+    assert cfg.dtype == "bf16" and cfg.qk_norm and dh == 256        # the fp8 bound is built here
+    gs = 0
+    while -(-n // (8 << gs)) > 128:
+        gs += 1
+    gsz = 8 << gs
+    ng = -(-n // gsz)
+    assert ng >= 2 * k                                                # the two passes, not exhaustive rows
+    kh = torch.empty((H, 2, n, dh), dtype=torch.bfloat16, device="cuda")
+    P.pkm_copy_normalized_subkeys(wl.pkm.handle, kh)
+    K = O.to_f64(G.to_host(kh), "bf16")
+    got = {}
+    for mode in ("exact", "auto"):
+        P.pkm_set_score_bound(wl.pkm.handle, mode)
+        qh = torch.empty((T, H, 2, dh), dtype=torch.bfloat16, device="cuda")
+        th = torch.empty((T, H, 2), dtype=torch.float32, device="cuda")
+        ct = torch.empty((T, H, 2, 2), dtype=torch.int32, device="cuda")
+        out = torch.empty((T, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+        P.pkm_forward_debug(wl.pkm.handle, wl.dev["x"], T, out, {"qhat": qh, "theta": th, "counts": ct})
+        torch.cuda.synchronize()
+        got[mode] = (G.to_host(qh), th.cpu().numpy(), ct.cpu().numpy())
+    assert np.array_equal(got["exact"][0], got["auto"][0])
+    Q = O.to_f64(got["exact"][0], "bf16")
+    th_x, ct_x = got["exact"][1], got["exact"][2]
+    th_8 = got["auto"][1]
+    n_near = n_rewritten = 0
+    far = []
+    for h in range(H):
+        for c in range(2):
+            s = Q[:, h, c] @ K[h, c].T                                    # [T, n] exact scores
+            gm = np.full((T, ng * gsz), -np.inf)
+            gm[:, :n] = s
+            gm = gm.reshape(T, ng, gsz).max(axis=2)
+            kth = -np.sort(-gm, axis=1)[:, k - 1]
+            tol = 1e-3 * np.maximum(1.0, np.abs(kth))                     # fp32 sums against float64
+            window = np.abs(kth) * 2.0 ** -7 + tol                        # rounded down to 16 bits
+            t = th_x[:, h, c].astype(np.float64)
+            assert np.all(t <= kth + tol) and np.all(t >= kth - window), (h, c)
+            # the GPU's bound is the float64 k-th group maximum, truncated, up to the fp32 sums
+            want = _of_ord_key(_ord_key(kth.astype(np.float32)) & np.uint32(0xFFFF0000)).astype(np.float64)
+            assert np.mean(np.abs(t - want) <= tol) > 0.99, (h, c)
+            cnt = (s >= t[:, None]).sum(axis=1)
+            near = (np.abs(s - t[:, None]) <= tol[:, None]).sum(axis=1)
+            c0, c1 = ct_x[:, h, c, 0], ct_x[:, h, c, 1]
+            rewritten = (c0 == k) & (c1 == 0) & (cnt != k)                # rows the overflow pass redid
+            ok = rewritten | (np.abs(c0 + c1 - cnt) <= near)
+            assert ok.all() and np.all((c0 + c1)[~rewritten] >= k), (h, c)
+            n_near += int((near > 0).sum())
+            n_rewritten += int(rewritten.sum())
+            # the fp8 estimate: near the k-th maximum less the margin
+            margin = 0.006 * np.linalg.norm(Q[:, h, c], axis=1) * np.linalg.norm(K[h, c], axis=1).max()
+            dev = np.abs(th_8[:, h, c] - (kth - margin))
+            assert np.all(dev <= 2 * margin + window), (h, c, float(dev.max()), float(margin.max()))
+            far.append(np.mean(dev > margin))
+    say(f"  rows with a score within the fp32 tolerance of the bound: {n_near}; rewritten rows: {n_rewritten}; "
+        f"fp8 bound off by more than its margin: {max(far):.3%} of rows at worst")
+    assert max(far) < 0.05
+
+
 @pytest.mark.parametrize("shape", [
     dict(n_sub=256, T=300),             # few sub-keys: every row scored exhaustively
     dict(n_sub=1100, T=600, H=64),      # the two MFMA passes in 8-wave blocks, theta, overflow scan
