@@ -9,25 +9,29 @@
 //
 // Design for gfx950:
 //  * The scores are a dense contraction (tokens x sub-keys x d_h) on the matrix cores:
-//    v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2f32 (fp32), computing
-//    S^T = Khat * Qhat^T so that each lane's 16 accumulators belong to ONE token.  A wave
-//    owns 64 tokens (two 32-token MFMA columns), so every 16-byte LDS operand read feeds
-//    two MFMAs.  A block is 4 or 8 waves = 256 or 512 tokens of one (h, c); 32-sub-key
-//    chunks reach a double-buffered, XOR-swizzled LDS tile shared by the block's waves by
-//    direct buffer->LDS loads, the next chunk's while the current one is scored.  Pass 2
-//    also keeps a small per-lane row of scores in LDS for its appends.
+//    v_mfma_f32_32x32x16_bf16 (bf16), v_mfma_f32_32x32x2f32 (fp32) or, for the fp8 bound
+//    pass, v_mfma_scale_f32_32x32x64_f8f6f4, computing S^T = Khat * Qhat^T so that each
+//    lane's 16 accumulators belong to ONE token.  A wave owns 64 tokens (two 32-token MFMA
+//    columns), so every 16-byte LDS operand read feeds two MFMAs.  A block is 4 or 8 waves
+//    = 256 or 512 tokens of one (h, c); 32-sub-key chunks reach a double-buffered,
+//    XOR-swizzled LDS tile shared by the block's waves by direct buffer->LDS loads, the
+//    next chunks while the current ones are scored.  Pass 2 also keeps a small per-lane row
+//    of scores in LDS for its appends.
 //  * The scores are never written out; selection takes two passes:
 //      pass 1 writes, per row, the maximum score of every group of G consecutive
-//             sub-keys (G in {8, 16, 32, 64, ...}, the smallest giving <= 128 groups);
-//      theta  picks per row the k-th largest group maximum, rounded down to its top 16
-//             bits: at least k sub-keys reach it, so it bounds the row's k-th best score
-//             from below (found bit by bit with wave ballots);
-//      pass 2 recomputes the same scores (bitwise) and writes every sub-key scoring at
-//             or above the bound as a 64-bit key to the row's candidate list
-//             (cand_slots(k) slots, half per lane).  With random-like data and k = 32
-//             about 37 of 4,096 per row (48 with the fp8 bound's margin).
-//    A lane's count may exceed its half of the slots (structured data); that row is then
-//    scored exhaustively by the overflow kernel before the combine kernel reads it.
+//             sub-keys (G in {8, 16, 32, 64, ...}, the smallest giving <= 128 groups),
+//             then theta in its tail: the k-th largest group maximum, rounded down to its
+//             top 16 bits: at least k sub-keys reach it, so it bounds the row's k-th best
+//             score from below (with split sub-key ranges theta_kernel forms it instead).
+//             With the fp8 bound the maxima are of fp8 scores and theta is lowered by a
+//             margin: an estimate, which the counts of pass 2 check;
+//      pass 2 recomputes the scores exactly and writes every sub-key scoring at or above
+//             the bound as a 64-bit key to the row's candidate list (cand_slots(k) slots,
+//             half per lane).  With random-like data and k = 32 about 37 of 4,096 per row
+//             (48 with the fp8 bound's margin).
+//    A lane's count may exceed its half of the slots (structured data), or the two halves
+//    hold fewer than k (an fp8 estimate set too high); that row is then scored exhaustively
+//    by the overflow kernel before the combine kernel reads it.
 //  * With fewer than 2k groups (k + 32 for k > 32: few sub-keys for the k asked for) the
 //    bound prunes little and most rows would overflow: every row is then scored
 //    exhaustively, one wave per row, instead of the two passes.
@@ -498,7 +502,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) pass1_kernel(const DT* __rest
 // scalar unit (popcounts, adds and compares per bit): 16 bits instead of 32 took it from
 // 54 to 34 us at 131,072 rows.
 // Keys strictly above a bound that is below the k-th group maximum already number at least
-// k, so pass 2's cap on keys equal to the bound drops none that matter.
+// k, so the cap on keys equal to the bound (pass 2 over split sub-key ranges) drops none that
+// matter.
 // With group maxima of fp8 scores (qn != NULL) the k-th largest is only an estimate: the bound
 // is lowered by eta * |q half| * max |sub-key| of the pair, a few standard deviations of the
 // fp8 rounding error of a score.  Pass 2 then still counts the exact scores at or above it, and
