@@ -10,10 +10,11 @@
 // of the two fp32 half scores.
 //
 // One wave per (token, head).  First the two per-half lists: each half's candidates
-// (at most cand_slots(k) keys from the scoring kernel, a superset of its top-k, in two lists)
-// are merged when both lists are sorted (the scoring sorts lists of up to 32 keys), else
-// ranked by comparing every key with every other (v_readlane broadcasts), and the k best
-// are written, in order, to LDS (and to the per-half outputs when asked for).  Both lists are
+// (at most cand_slots(k) keys from the scoring kernel, a superset of its top-k, in two
+// unsorted lists) are, when both lists hold at most 32 keys, sorted one list per 32-lane half
+// by a bitonic network and merged, else ranked by comparing every key with every other
+// (v_readlane broadcasts); the k best are written, in order, to LDS (and to the per-half
+// outputs when asked for).  Both lists are
 // then sorted, so the pair of positions (i, j) is beaten by every (i', j') with i' <= i,
 // j' <= j; in exact arithmetic only the "staircase" (i + 1)(j + 1) <= k can reach the
 // top-k (119 pairs for k = 32 instead of 1,024).  Staircase cells below a lower bound of
@@ -49,6 +50,22 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t x, int lane) {
       const uint64_t o = shfl_xor_u64(x, stride);
       // keep the larger where bit `size` and bit `stride` of the lane agree (a constant lane mask)
       const bool take_max = lane_in(~(lanes_bit_clear(size) ^ lanes_bit_clear(stride)));
+      x = (x > o) == take_max ? x : o;
+    }
+  }
+  return x;
+}
+
+// Sort the keys of each 32-lane half of the wave (one per lane) in descending order, the
+// two halves independently (lanes 0 and 32 end with their half's largest): the bitonic network
+// of sort64_desc up to blocks of 32, whose last merge runs descending in both halves.
+__device__ __forceinline__ uint64_t sort32x2_desc(uint64_t x) {
+#pragma unroll
+  for (int size = 2; size <= 32; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(x, stride);
+      const bool take_max = lane_in(~(lanes_bit_clear(size < 32 ? size : 64) ^ lanes_bit_clear(stride)));
       x = (x > o) == take_max ? x : o;
     }
   }
@@ -101,38 +118,33 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint64_t* __restrict
     const int64_t r2 = row * 2 + c;
     const int na = count[2 * r2], nb = count[2 * r2 + 1];  // <= 64 after the overflow pass
     const uint64_t* cr = cand + r2 * 128;
-    // Both lists sorted (the scoring sorts lists of up to 32 keys; the exhaustive rows write
-    // theirs in order): lanes 0-31 hold list 0, lanes 32-63 list 1, and a key's rank is its
+    // Lists of up to 32 keys: lanes 0-31 hold list 0 and lanes 32-63 list 1, each half sorted
+    // by a bitonic network (empty slots are key 0 and sort last); a key's rank is then its
     // position in its own list plus the number of the other list's keys above it (a binary
     // search; the keys are distinct).
-    bool merged = false;
     if (na <= 32 && nb <= 32) {  // wave-uniform
       const int own = lane & 31, side = lane >> 5;
       const int n_own = side ? nb : na, n_oth = side ? na : nb;
-      const uint64_t x = own < n_own ? cr[64 * side + own] : 0ull;
-      const uint64_t nx = shfl_u64(x, lane + 1);  // the next key of the own list, when own + 1 < n_own
-      if (__ballot(own + 1 < n_own && !(x > nx)) == 0) {
-        merged = true;
-        surv[wv][lane] = x;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        const uint64_t* oth = surv[wv] + 32 * (1 - side);
-        int lo = 0, hi = n_oth;
+      const uint64_t x = sort32x2_desc(own < n_own ? cr[64 * side + own] : 0ull);
+      surv[wv][lane] = x;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      const uint64_t* oth = surv[wv] + 32 * (1 - side);
+      int lo = 0, hi = n_oth;
 #pragma unroll
-        for (int it = 0; it < 6; ++it) {  // n_oth <= 32
-          if (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (oth[mid] > x) lo = mid + 1;
-            else hi = mid;
-          }
+      for (int it = 0; it < 6; ++it) {  // n_oth <= 32
+        if (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (oth[mid] > x) lo = mid + 1;
+          else hi = mid;
         }
-        const int rank = own + lo;
-        if (own < n_own && rank < k) lists[wv][c][rank] = x;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
+      const int rank = own + lo;
+      if (own < n_own && rank < k) lists[wv][c][rank] = x;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      continue;
     }
-    if (merged) continue;
     const uint64_t x0 = lane < na ? cr[lane] : 0ull;
     const uint64_t x1 = lane < nb ? cr[64 + lane] : 0ull;
     // rank = the number of candidates with a larger key; two broadcasts per step so that

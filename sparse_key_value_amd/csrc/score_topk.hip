@@ -532,40 +532,6 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ gm
   if (lane == 0) theta[row] = qn ? score_of_ord(prefix) - eta * qn[row] * kmax[row % pairs] : score_of_ord(prefix);
 }
 
-// Candidate lists of up to SORTED keys are sorted after pass 2, one thread per list, so that
-// the combine merges the two lists of a row instead of ranking every candidate against every
-// other (one wave per row); batches under SORT_MIN_ROWS rows skip it (see the launch).
-constexpr int SORTED = 32;
-constexpr int64_t SORT_MIN_ROWS = 32768;  // rows (T x H x 2) from which the lists are sorted
-
-// Sort one candidate list of n <= SORTED keys in place, descending: a bitonic network in
-// registers (Batcher 1968; empty slots are key 0, which sorts last).
-__device__ __forceinline__ void sort_list(uint64_t* list, int n) {
-  uint64_t L[SORTED];
-#pragma unroll
-  for (int j = 0; j < SORTED; ++j) L[j] = j < n ? list[j] : 0ull;
-#pragma unroll
-  for (int size = 2; size <= SORTED; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-#pragma unroll
-      for (int i = 0; i < SORTED; ++i) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool desc = (i & size) == 0;
-          const uint64_t a = L[i], b = L[j];
-          const bool swap = desc ? a < b : a > b;
-          L[i] = swap ? b : a;
-          L[j] = swap ? a : b;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < SORTED; ++j)
-    if (j < n) list[j] = L[j];
-}
-
 // Pass 2: write the candidates of every row (keys at or above theta; with split sub-key
 // ranges only the first k per lane of those equal to theta).  Each of a token's two lanes
 // owns `half` of the row's 2 * half slots and counts its own candidates.
@@ -802,43 +768,6 @@ __global__ void __launch_bounds__(256) overflow_kernel(const DT* __restrict__ qh
   }
 }
 
-// The candidate lists sorted, one thread per list (list i = 2 * row + lane half): those holding
-// 2..SORTED keys; runs after the overflow pass (whose rewritten rows are already in order).  A
-// wave takes 32 consecutive rows (64 lists): their first SORTED slots move between memory and
-// LDS in 16-byte pieces, 16 lanes per list (coalesced), and each lane sorts its own list in LDS
-// (one list per lane read directly from memory took 41 us at 131,072 rows: 64 lanes on 64
-// different lines per load, the vector L1 thrashing).
-constexpr int SORT_LD = SORTED + 2;  // keys per list in LDS: 16-byte aligned rows, spread banks
-__global__ void __launch_bounds__(256) sort_lists_kernel(uint64_t* __restrict__ cand, int cs,
-                                                         const int32_t* __restrict__ count, int64_t lists) {
-  __shared__ __attribute__((aligned(16))) uint64_t ls[4][64 * SORT_LD];
-  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t first = ((int64_t)blockIdx.x * 4 + wv) * 64;  // the wave's first list
-  if (first >= lists) return;
-  uint64_t* lw = ls[wv];
-  auto list_at = [&](int q) { return cand + ((first + q) >> 1) * cs + ((first + q) & 1) * (cs / 2); };
-  // load: piece c = it * 64 + lane is 16-byte piece c % 16 of list c / 16
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int c = it * 64 + lane, q = c >> 4, pc = c & 15;
-    if (first + q < lists) *(u32x4*)(lw + q * SORT_LD + 2 * pc) = *(const u32x4*)(list_at(q) + 2 * pc);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int n = first + lane < lists ? count[first + lane] : 0;
-  if (n > 1 && n <= SORTED) sort_list(lw + lane * SORT_LD, n);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // store back the same pieces (unsorted lists come back unchanged)
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int c = it * 64 + lane, q = c >> 4, pc = c & 15;
-    if (first + q < lists) *(u32x4*)(list_at(q) + 2 * pc) = *(const u32x4*)(lw + q * SORT_LD + 2 * pc);
-  }
-}
-
 // Few sub-keys per row (fewer than 2k groups, so the group-maximum bound prunes little and
 // most rows would overflow): every row exhaustively, one wave per row.
 template <typename DT, int DH, int LK>
@@ -963,13 +892,6 @@ hipError_t launch_passes_nw(const void* qhat, const void* khat, int64_t T, int H
   else
     overflow_kernel<DT, DH, MAX_K><<<dim3((unsigned)ob), 256, 0, s>>>((const DT*)qhat, (const DT*)khat, rows, H, n, k,
                                                                       cand, cs, count);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // the combine for k <= 32 merges sorted lists and ranks unsorted ones; sorting pays from about
-  // 32,768 rows (T x H x 2) on: below that its ~12 us of load and sort latency exceeds what the
-  // merge saves (256 tokens x 4 heads: sort 12.8 + combine 8.4 us against a ranking combine of
-  // 8.7; at 4,096 tokens both 37-38 us; at 16,384 tokens 43 + 74 against about 137)
-  if (k <= 32 && rows >= SORT_MIN_ROWS)
-    sort_lists_kernel<<<dim3((unsigned)((2 * rows + 255) / 256)), 256, 0, s>>>(cand, cs, count, 2 * rows);  // 64 lists a wave
   return hipGetLastError();
 }
 
