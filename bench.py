@@ -865,6 +865,26 @@ def main():
     achieved = alg_b / (g_ms * 1e-3) / 1e9
     log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items() if v is not None))
 
+    rr_ms = None
+    if not host:
+        # the same rows read with the gather's lane layout and no arithmetic (XOR only): the
+        # read rate of this random-row pattern, the gather's own ceiling
+        sel = torch.empty((T, cfg.H * cfg.k), dtype=torch.int32, device="cuda")
+        P.pkm_forward(h, x, T, out, idx_out=sel, stream=stream)
+        rr_out = torch.empty((T, cfg.d_v * cfg.elem_bytes), dtype=torch.uint8, device="cuda")
+        SD.row_read(wl.values, sel, rr_out)
+        rr = []
+        for _ in range(3):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            SD.row_read(wl.values, sel, rr_out)
+            ev1.record()
+            torch.cuda.synchronize()
+            rr.append(ev0.elapsed_time(ev1))
+        rr_ms = sorted(rr)[1]
+        del sel, rr_out
+        log(f"row read of the forward's rows (no arithmetic): {rr_ms:.3f} ms against the gather's {g_ms:.3f} ms")
+
     cpu = None
     if not a.no_cpu_baseline and not host:
         cpu = cpu_baseline(wl, cfg, a.cpu_seconds)
@@ -900,6 +920,9 @@ def main():
         "gather_value_frac_hbm": rows_b / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stream_read_GBps": stream_gbps,
         "gather_frac_of_stream_read": achieved / stream_gbps if stream_gbps else None,
+        "row_read_ms": rr_ms,
+        "row_read_value_GBps": rows_b / (rr_ms * 1e-3) / 1e9 if rr_ms else None,
+        "gather_time_over_row_read": g_ms / rr_ms if rr_ms else None,
         "stages_ms": stages,
         "stages_note": f"from {n_bd} forwards after the timed steps with every stage's events recorded (the events "
                        "slow a forward by about 2%; the timed steps record the gather's alone)",

@@ -14,6 +14,9 @@
 //    streaming-read ceiling of the HBM).
 //  * synth_copy: a plain 16-byte copy kernel of known size, used to calibrate the
 //    HBM byte counters.
+//  * synth_row_read: reads the rows a list of bags names, with the lane layout of a
+//    weighted bag gather (one 16-byte column slice per lane, 16 rows in flight), and
+//    only XORs them: the read rate of those random rows with no arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,6 +80,36 @@ __global__ void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ s
     dst[i] = __builtin_nontemporal_load(src + i);
 }
 
+// Bag b's rows idx[b * bag ..][0, bag): lane slice `col` of each, XORed, one 16-byte store per lane
+// and bag into out[b * row_vecs + col]; indices outside [0, n_rows) read row 0.
+__global__ void __launch_bounds__(256) row_read_kernel(const uint8_t* __restrict__ table, int64_t n_rows,
+                                                       int row_vecs, int tpr, int bpb,
+                                                       const int32_t* __restrict__ idx, int64_t n_bags, int bag,
+                                                       u32x4* __restrict__ out) {
+  const int g = threadIdx.x / tpr;
+  const int col = blockIdx.y * tpr + (threadIdx.x - g * tpr);
+  if (g >= bpb || col >= row_vecs) return;
+  const size_t rb = (size_t)row_vecs * 16;
+  auto slice = [&](int32_t r) {
+    r = (uint64_t)(int64_t)r < (uint64_t)n_rows ? r : 0;
+    return __builtin_nontemporal_load((const u32x4*)(table + (size_t)r * rb) + col);
+  };
+  for (int64_t b = (int64_t)blockIdx.x * bpb + g; b < n_bags; b += (int64_t)gridDim.x * bpb) {
+    const int32_t* bi = idx + b * bag;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int j = 0;
+    for (; j + 16 <= bag; j += 16) {
+      u32x4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = slice(bi[j + u]);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc ^= v[u];
+    }
+    for (; j < bag; ++j) acc ^= slice(bi[j]);
+    __builtin_nontemporal_store(acc, out + b * row_vecs + col);
+  }
+}
+
 extern "C" {
 
 // Fill rows [row0, row0 + n_rows) of a [*, d_v] table at `table` (device pointer to row 0)
@@ -107,6 +140,23 @@ int synth_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t gr
 int synth_copy(void* dst, const void* src, int64_t bytes, int32_t grid, void* stream) {
   if (!dst || !src || bytes < 16 || grid < 1) return (int)hipErrorInvalidValue;
   copy_kernel<<<grid, 256, 0, (hipStream_t)stream>>>((u32x4*)dst, (const u32x4*)src, bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// out: n_bags x row_bytes bytes.  row_bytes: a multiple of 16.
+int synth_row_read(const void* table, int64_t n_rows, int64_t row_bytes, const int32_t* idx, int64_t n_bags,
+                   int32_t bag, void* out, void* stream) {
+  if (!table || !idx || !out || n_rows < 1 || row_bytes < 16 || row_bytes % 16 != 0 || n_bags < 0 || bag < 1)
+    return (int)hipErrorInvalidValue;
+  if (n_bags == 0) return 0;
+  const int row_vecs = (int)(row_bytes / 16);
+  const int tpr = row_vecs < 256 ? row_vecs : 256, bpb = 256 / tpr;
+  const int64_t cols = (row_vecs + tpr - 1) / tpr;
+  if (cols > 65535) return (int)hipErrorInvalidValue;
+  const int64_t groups = (n_bags + bpb - 1) / bpb, cap = ((int64_t)1 << 22) / cols;
+  const dim3 grid((unsigned)(groups < cap ? groups : (cap > 0 ? cap : 1)), (unsigned)cols);
+  row_read_kernel<<<grid, bpb * tpr, 0, (hipStream_t)stream>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx,
+                                                              n_bags, bag, (u32x4*)out);
   return (int)hipGetLastError();
 }
 

@@ -15,7 +15,8 @@ _lib.synth_fill_values.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64,
 _lib.synth_fill_table.argtypes = [_vp, _i64, _i64, _i32, _i32, ctypes.c_uint64, ctypes.c_uint32, _vp]
 _lib.synth_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
 _lib.synth_copy.argtypes = [_vp, _vp, _i64, _i32, _vp]
-for _f in (_lib.synth_fill_values, _lib.synth_fill_table, _lib.synth_stream_read, _lib.synth_copy):
+_lib.synth_row_read.argtypes = [_vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp]
+for _f in (_lib.synth_fill_values, _lib.synth_fill_table, _lib.synth_stream_read, _lib.synth_copy, _lib.synth_row_read):
     _f.restype = ctypes.c_int
 
 
@@ -60,3 +61,18 @@ def copy(dst, src, grid: int = 2048) -> None:
     rc = _lib.synth_copy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), grid, _stream())
     if rc:
         raise RuntimeError(f"synth_copy failed: hip error {rc}")
+
+
+def row_read(table, idx, out) -> None:
+    """Read the rows of ``table`` ([N, *] on the GPU) that the bags of ``idx`` ([n_bags, bag]
+    int32) name, with a weighted bag gather's lane layout and no arithmetic but an XOR:
+    out[b] (``table.shape[1:]`` bytes per bag) = the XOR of the bag's rows, bytewise.
+    Indices outside [0, N) read row 0."""
+    import torch
+    assert idx.dtype == torch.int32 and idx.dim() == 2 and idx.is_contiguous() and table.is_contiguous()
+    row_bytes = table[0].numel() * table.element_size()
+    assert out.is_contiguous() and out.numel() * out.element_size() == idx.shape[0] * row_bytes
+    rc = _lib.synth_row_read(table.data_ptr(), table.shape[0], row_bytes, idx.data_ptr(), idx.shape[0], idx.shape[1],
+                             out.data_ptr(), _stream())
+    if rc:
+        raise RuntimeError(f"synth_row_read failed: hip error {rc}")
