@@ -28,9 +28,11 @@ design notes of the repository):
 * order: score descending, then index ascending (the lowest index wins a tie);
   -0.0 compares equal to +0.0.
 * softmax over each head's final k scores, no temperature.
-* bf16 workloads: the normalised query and sub-keys are rounded to bf16 before
-  scoring, and y * silu(x W1) is rounded to bf16 before W2; all other
-  arithmetic here is float64 on the exact stored values.
+* bf16 workloads: the projections q = x W_q and z = x W1 are stored in bf16 (the
+  type a bf16 product returns) before the norm and the gate read them; the
+  normalised query and sub-keys are rounded to bf16 before scoring, and
+  y * silu(z) is rounded to bf16 before W2; all other arithmetic here is float64
+  on the exact stored values.
 
 Arrays of stored bf16 values are uint16 bit patterns; float32 storage is
 float32.
@@ -171,9 +173,11 @@ def silu(z: np.ndarray) -> np.ndarray:
 def memory_plus(y: np.ndarray, x: np.ndarray, W1: np.ndarray, W2: np.ndarray, dtype: str) -> np.ndarray:
     """Memory+ output (digest, Memory+ block): out = (y * silu(x W1)) W2, row-major form.
 
-    For bf16 workloads the gated product is stored as bf16 before W2.
+    For bf16 workloads z = x W1 and the gated product are each stored as bf16 before
+    they are used.
     """
-    g = round_stored(y * silu(x @ W1), dtype)
+    z = round_stored(x @ W1, dtype)
+    g = round_stored(y * silu(z), dtype)
     return g @ W2
 
 
@@ -182,8 +186,9 @@ def memory_plus(y: np.ndarray, x: np.ndarray, W1: np.ndarray, W2: np.ndarray, dt
 
 
 def normalized_query(x, W_q, H, d_q, qk_norm: bool, eps: float, dtype: str):
-    """q -> optional RMSNorm over d_q -> rounding to the scoring precision -> halves."""
-    q = project_query(x, W_q, H, d_q)
+    """q stored in dtype -> optional RMSNorm over d_q -> rounding to the scoring precision
+    -> halves."""
+    q = round_stored(project_query(x, W_q, H, d_q), dtype)
     if qk_norm:
         q = rmsnorm(q, eps)
     q = round_stored(q, dtype)

@@ -5,8 +5,8 @@
 // memory bandwidth, not FLOPs).  In the forward a bag is one token's H*k selected
 // rows with their softmax weights (core idea: weighted sum of the top-k values).
 // With the Memory+ gate (digest, Memory+ block) the kernel also applies the gate's
-// elementwise part, g = y * silu(z) with z = x W1 computed beforehand, and writes g in
-// the table's type instead of y in fp32: the fp32 y never reaches HBM.  Writes mixed
+// elementwise part, g = y * silu(z) with z = x W1 computed beforehand (in the stored type),
+// and writes g in the table's type instead of y in fp32: the fp32 y never reaches HBM.  Writes mixed
 // into this read stream cost far more than their bytes (128 MiB of fp32 y slowed the
 // 8.6 GB gather by about 16% on MI355X), while reading z costs about its bytes.
 //
@@ -42,33 +42,33 @@ struct VecTraits<4> {  // fp32: 4 elements per 16 bytes
   }
 };
 
-template <int EB, int UNROLL, bool GATE>
+template <int EB, int UNROLL, int ZB>
 __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
                                            const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
-                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z,
+                                           int bag, void* __restrict__ y, int y_f32, const void* __restrict__ z,
                                            int64_t z_ld);
 
 // Block = BAGS_PER_BLOCK groups of TPR lanes; group g handles bags blockIdx.x*BPB+g,
 // then + gridDim.x*BPB, ... (one block per group of bags up to a grid cap), and the
 // 16-byte column slices [blockIdx.y*TPR, blockIdx.y*TPR + TPR) of their rows.
-template <int EB, int UNROLL, bool UNIFORM, bool GATE>
+template <int EB, int UNROLL, bool UNIFORM, int ZB>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, int64_t n_rows,
                                                      int row_vecs, int tpr, int bags_per_block,
                                                      const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                      int64_t n_bags, int bag, void* __restrict__ y, int y_f32,
-                                                     const float* __restrict__ z, int64_t z_ld) {
+                                                     const void* __restrict__ z, int64_t z_ld) {
   int g = threadIdx.x / tpr;
   if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
   const int col = blockIdx.y * tpr + (threadIdx.x - g * tpr);  // 16-byte slice index in the row
   if (g >= bags_per_block || col >= row_vecs) return;
   for (int64_t b = (int64_t)blockIdx.x * bags_per_block + g; b < n_bags; b += (int64_t)gridDim.x * bags_per_block)
-    gather_bag<EB, UNROLL, GATE>(table, n_rows, row_vecs, col, idx, w, b, bag, y, y_f32, z, z_ld);
+    gather_bag<EB, UNROLL, ZB>(table, n_rows, row_vecs, col, idx, w, b, bag, y, y_f32, z, z_ld);
 }
 
-template <int EB, int UNROLL, bool GATE>
+template <int EB, int UNROLL, int ZB>
 __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, int64_t n_rows, int row_vecs, int col,
                                            const int32_t* __restrict__ idx, const float* __restrict__ w, int64_t b,
-                                           int bag, void* __restrict__ y, int y_f32, const float* __restrict__ z,
+                                           int bag, void* __restrict__ y, int y_f32, const void* __restrict__ z,
                                            int64_t z_ld) {
   using VT = VecTraits<EB>;
   constexpr int E = VT::E;
@@ -107,13 +107,24 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
 
   const int64_t dim = (int64_t)row_vecs * E;
   const int64_t o = b * dim + (int64_t)col * E;
-  if constexpr (GATE) {
-    // g = y * silu(z), stored in the table's type
+  if constexpr (ZB != 0) {
+    // g = y * silu(z), stored in the table's type; z in fp32 (ZB = 4) or bf16 (ZB = 2, with bf16
+    // values: the lane's 8 elements of z in one 16-byte load)
+    if constexpr (ZB == 4) {
 #pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const f32x4 zz = __builtin_nontemporal_load((const f32x4*)(z + b * z_ld + (int64_t)col * E + e));
+      for (int e = 0; e < E; e += 4) {
+        const f32x4 zz = __builtin_nontemporal_load((const f32x4*)((const float*)z + b * z_ld + (int64_t)col * E + e));
 #pragma unroll
-      for (int x = 0; x < 4; ++x) acc[e + x] = acc[e + x] * silu_f32(zz[x]);
+        for (int x = 0; x < 4; ++x) acc[e + x] = acc[e + x] * silu_f32(zz[x]);
+      }
+    } else {
+      static_assert(ZB == 2 && EB == 2, "a bf16 z goes with bf16 values");
+      const u32x4 zz = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)z + b * z_ld + (int64_t)col * E));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        acc[2 * x] = acc[2 * x] * silu_f32(bf16_lo(zz[x]));
+        acc[2 * x + 1] = acc[2 * x + 1] * silu_f32(bf16_hi(zz[x]));
+      }
     }
     if constexpr (EB == 2) {
       u32x4 pk;
@@ -147,7 +158,7 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
 
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s,
-                         const float* z, int64_t z_ld) {
+                         const void* z, int64_t z_ld, int z_bf16) {
   if (n_bags == 0) return hipSuccess;
   // one block per group of bags; a grid of at most 2^22 blocks (of <= 256 lanes: far below
   // the 2^32 work-items of one dispatch) loops over larger bag counts
@@ -164,19 +175,22 @@ hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, 
   dim3 grid((unsigned)bx, (unsigned)cols);
   const int y_f32 = (!y_dtype_is_table || dtype == DT_F32) ? 1 : 0;
   const bool uniform = (tpr % 64) == 0;
-#define PKM_GATHER(EBV, UNI, GT)                                                                              \
-  gather_kernel<EBV, 16, UNI, GT><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, \
-                                                           w, n_bags, bag, y, y_f32, z, z_ld)
-  if (z) {
+#define PKM_GATHER(EBV, UNI, ZBV)                                                                             \
+  gather_kernel<EBV, 16, UNI, ZBV><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, \
+                                                            w, n_bags, bag, y, y_f32, z, z_ld)
+  if (z && z_bf16) {
+    if (eb != 2) return hipErrorInvalidValue;  // a bf16 z comes with bf16 values
+    if (uniform) PKM_GATHER(2, true, 2); else PKM_GATHER(2, false, 2);
+  } else if (z) {
     if (eb == 2) {
-      if (uniform) PKM_GATHER(2, true, true); else PKM_GATHER(2, false, true);
+      if (uniform) PKM_GATHER(2, true, 4); else PKM_GATHER(2, false, 4);
     } else {
-      if (uniform) PKM_GATHER(4, true, true); else PKM_GATHER(4, false, true);
+      if (uniform) PKM_GATHER(4, true, 4); else PKM_GATHER(4, false, 4);
     }
   } else if (eb == 2) {
-    if (uniform) PKM_GATHER(2, true, false); else PKM_GATHER(2, false, false);
+    if (uniform) PKM_GATHER(2, true, 0); else PKM_GATHER(2, false, 0);
   } else {
-    if (uniform) PKM_GATHER(4, true, false); else PKM_GATHER(4, false, false);
+    if (uniform) PKM_GATHER(4, true, 0); else PKM_GATHER(4, false, 0);
   }
 #undef PKM_GATHER
   return hipGetLastError();

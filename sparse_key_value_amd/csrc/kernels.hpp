@@ -70,11 +70,11 @@ hipError_t launch_score_candidates(const void* qhat, const void* khat, int64_t T
 hipError_t launch_combine(const uint64_t* cand, const int32_t* count, int64_t T, int H, int n, int k,
                           int32_t* half_idx, float* half_score, int32_t* idx, float* score, float* w, hipStream_t s);
 // Weighted EmbeddingBag: y[b] = sum_j w[b,j] table[idx[b,j]]; y fp32 or dtype.  With z
-// (fp32, row b at z + b * z_ld, dim elements) it writes g[b] = y[b] * silu(z[b]) in dtype
-// instead.
+// (row b at z + b * z_ld, dim elements; fp32, or bf16 if z_bf16 with a bf16 table) it writes
+// g[b] = y[b] * silu(z[b]) in dtype instead.
 hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, const int32_t* idx,
                          const float* w, int64_t n_bags, int bag, void* y, int y_dtype_is_table, hipStream_t s,
-                         const float* z = nullptr, int64_t z_ld = 0);
+                         const void* z = nullptr, int64_t z_ld = 0, int z_bf16 = 0);
 
 hipError_t launch_convert_f32(const float* in, void* out, int64_t n, int dtype, hipStream_t s);
 

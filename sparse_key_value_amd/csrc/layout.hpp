@@ -91,7 +91,7 @@ inline Layout make_layout(const pkm_config* c) {
   if (c->memory_plus) L.w1T = L.wqT + H * dq * dm * eb;
   L.khat = take(H * 2 * n * dhp * eb);
   if (c->memory_plus) L.w2T = take(dm * dv * eb);
-  L.q = take(T * (size_t)L.qz_cols * 4);
+  L.q = take(T * (size_t)L.qz_cols * eb);
   L.qhat = take(T * H * 2 * dhp * eb);
   L.gmax = take(T * H * 2 * 128 * 4);   // MAX_GROUPS group maxima per row
   L.theta = take(T * H * 2 * 4);

@@ -58,9 +58,10 @@ __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, size_t i, floa
 // (r % per_tok) * width in the input (in_ld elements per token).  The output row is the
 // input row cut into segments of `seg` elements, each stored in `seg_ld` >= seg elements
 // followed by zeros (seg_ld = seg: rows back to back, nothing padded); output row r starts at
-// r * (width / seg) * seg_ld.  VEC: fp32 input read four elements (16 bytes) per lane at a
-// time, unpadded output only.  Q8 (VEC with 256-wide segments): also the fp8 copy of the output
-// row (q8, same layout, one byte per element) and the fp32 norm of every segment (qn).
+// r * (width / seg) * seg_ld.  VEC: the input read four elements (16 bytes of fp32, 8 of bf16)
+// per lane at a time, unpadded output only.  Q8 (VEC with 256-wide segments): also the fp8 copy
+// of the output row (q8, same layout, one byte per element) and the fp32 norm of every segment
+// (qn).
 template <typename TI, typename TO, bool VEC, bool Q8 = false>
 __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in, TO* __restrict__ out,
                                                       int64_t rows, int width, int per_tok, int64_t in_ld, int norm,
@@ -82,7 +83,12 @@ __global__ void __launch_bounds__(256) rownorm_kernel(const TI* __restrict__ in,
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       if (i < nv) {
-        v[i] = *(const f32x4*)((const float*)src + i * 256 + lane * 4);
+        if constexpr (sizeof(TI) == 4) {
+          v[i] = *(const f32x4*)((const float*)src + i * 256 + lane * 4);
+        } else {
+          const uint2 p = *(const uint2*)((const uint16_t*)src + i * 256 + lane * 4);
+          v[i] = f32x4{bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)};
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss += v[i][e] * v[i][e];
       }
@@ -134,20 +140,24 @@ hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtyp
   if (in_ld == 0) in_ld = (int64_t)per_tok * width;
   if (seg == 0) seg = seg_ld = width;
   dim3 grid((unsigned)((rows + 3) / 4));
-  const bool vec = in_is_f32 && width % 256 == 0 && width <= 1024 && in_ld % 4 == 0 && ((uintptr_t)in & 15) == 0 &&
-                   seg == seg_ld;
+  const bool vec = width % 256 == 0 && width <= 1024 && in_ld % 4 == 0 &&
+                   ((uintptr_t)in & (in_is_f32 ? 15 : 7)) == 0 && seg == seg_ld;
 #define PKM_RN(TI, TO, V)                                                                                          \
   rownorm_kernel<TI, TO, V><<<grid, 256, 0, s>>>((const TI*)in, (TO*)out, rows, width, per_tok, in_ld, norm, eps, seg, \
                                                  seg_ld)
-  if (q8) {  // fp8 copy and segment norms with the bf16 rows: 256-wide segments, fp32 input
-    if (!vec || seg != 256 || out_dtype != DT_BF16 || !in_is_f32) {
+  if (q8) {  // fp8 copy and segment norms with the bf16 rows: 256-wide segments
+    if (!vec || seg != 256 || out_dtype != DT_BF16) {
       const hipError_t e =
           launch_rownorm(in, in_is_f32, out, out_dtype, rows, width, norm, eps, s, per_tok, in_ld, seg, seg_ld);
       if (e != hipSuccess) return e;
       return launch_fp8_rows(out, q8, qn, rows * (width / seg), seg_ld, nullptr, 1, s);
     }
-    rownorm_kernel<float, uint16_t, true, true><<<grid, 256, 0, s>>>((const float*)in, (uint16_t*)out, rows, width,
-                                                                     per_tok, in_ld, norm, eps, seg, seg_ld, q8, qn);
+    if (in_is_f32)
+      rownorm_kernel<float, uint16_t, true, true><<<grid, 256, 0, s>>>((const float*)in, (uint16_t*)out, rows, width,
+                                                                       per_tok, in_ld, norm, eps, seg, seg_ld, q8, qn);
+    else
+      rownorm_kernel<uint16_t, uint16_t, true, true><<<grid, 256, 0, s>>>(
+          (const uint16_t*)in, (uint16_t*)out, rows, width, per_tok, in_ld, norm, eps, seg, seg_ld, q8, qn);
     return hipGetLastError();
   }
   if (in_is_f32) {
@@ -157,8 +167,11 @@ hipError_t launch_rownorm(const void* in, int in_is_f32, void* out, int out_dtyp
       if (vec) PKM_RN(float, float, true); else PKM_RN(float, float, false);
     }
   } else {
-    if (out_dtype == DT_BF16) PKM_RN(uint16_t, uint16_t, false);
-    else PKM_RN(uint16_t, float, false);
+    if (out_dtype == DT_BF16) {
+      if (vec) PKM_RN(uint16_t, uint16_t, true); else PKM_RN(uint16_t, uint16_t, false);
+    } else {
+      PKM_RN(uint16_t, float, false);
+    }
   }
 #undef PKM_RN
   return hipGetLastError();

@@ -51,9 +51,10 @@ def test_workspace_size_matches_layout(P):
     c = _cfg(P)
     a = lambda v: (v + 255) // 256 * 256
     T, H, dq, dm, dv, n, k = 16384, 4, 512, 2048, 2048, 4096, 32
-    want = (a(H * dq * dm * 2) + a(H * 2 * n * dq // 2 * 2) + a(dv * dm * 2) + a(dm * dv * 2) + a(T * H * dq * 4) +
+    # the projection's output [T, H dq + dv] (q, then z) is stored in bf16
+    want = (a(H * dq * dm * 2) + a(H * 2 * n * dq // 2 * 2) + a(dv * dm * 2) + a(dm * dv * 2) + a(T * H * dq * 2) +
             a(T * H * dq * 2) + a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * 128 * 8) + a(T * H * 2 * 2 * 4) +
-            2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 4) + a(T * dv * 2))
+            2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4) + a(T * dv * 2) + a(T * dv * 2))
     # the fp8 bound (bf16, 256-wide halves): e4m3 sub-keys, their norms, the largest per (head,
     # half), e4m3 query halves and their norms
     want += a(H * 2 * n * 256) + a(H * 2 * n * 4) + a(H * 2 * 4) + a(T * H * 2 * 256) + a(T * H * 2 * 4)
@@ -103,7 +104,7 @@ def test_workspace_of_padded_query_halves_and_wide_k(P, d_query, k):
     d_h = d_query // 2
     dhp = 64 if d_h <= 64 else (128 if d_h <= 128 else 256)
     cs = 128 if k <= 32 else 256
-    want = (a(H * d_query * dm * 2) + a(H * 2 * n * dhp * 2) + a(T * H * d_query * 4) + a(T * H * 2 * dhp * 2) +
+    want = (a(H * d_query * dm * 2) + a(H * 2 * n * dhp * 2) + a(T * H * d_query * 2) + a(T * H * 2 * dhp * 2) +
             a(T * H * 2 * 128 * 4) + a(T * H * 2 * 4) + a(T * H * 2 * cs * 8) + a(T * H * 2 * 2 * 4) +
             2 * a(T * H * 2 * k * 4) + 3 * a(T * H * k * 4))
     if dhp == 256:   # the fp8 bound of bf16 workloads

@@ -98,6 +98,51 @@ def test_hand_two_head_forward():
     np.testing.assert_allclose(c["expect_y"], [s(0.5) + s(1.5), s(-0.5) + 2 * s(-1.5)], rtol=1e-15)
 
 
+def _projections_equal_when_stored(d, seed):
+    """x [1, 2] and two weight matrices whose exact products x W differ (by 2^-11, alternating in
+    sign) but round to the same bf16 values a (bf16-exact, in [1, 2), where half an ulp is 2^-8)."""
+    rng = np.random.default_rng(seed)
+    a = O.bf16_bits_to_f64(O.f64_to_bf16_bits(rng.uniform(1.0, 2.0, d)))
+    s = np.where(np.arange(d) % 2 == 0, 1.0, -1.0) * 2.0 ** -12
+    x = np.array([[1.0, 1.0]])
+    Wa, Wb = np.stack([a, s]), np.stack([a, -s])
+    assert not np.array_equal(x @ Wa, x @ Wb)
+    assert np.array_equal(O.f64_to_bf16_bits(x @ Wa), O.f64_to_bf16_bits(a[None]))
+    assert np.array_equal(O.f64_to_bf16_bits(x @ Wb), O.f64_to_bf16_bits(a[None]))
+    return x, Wa, Wb
+
+
+def test_bf16_query_is_normalised_from_its_stored_projection():
+    """bf16 workloads store q = x W_q in bf16 before the qk-norm reads it (the type a bf16
+    product returns): two projections that store the same bf16 values give the same q-hat,
+    bit for bit.  The case is one where normalising the exact products would not (so a
+    missing or misplaced rounding fails here)."""
+    d = 64
+    x, Wa, Wb = _projections_equal_when_stored(d, seed=10)
+    qa = np.concatenate(O.normalized_query(x, Wa, 1, d, True, 0.0, "bf16"), axis=-1)
+    qb = np.concatenate(O.normalized_query(x, Wb, 1, d, True, 0.0, "bf16"), axis=-1)
+    np.testing.assert_array_equal(qa, qb)
+    ea, eb = (O.round_stored(O.rmsnorm(x @ W, 0.0), "bf16") for W in (Wa, Wb))
+    assert (ea != eb).sum() >= 3
+    # fp32 workloads keep the exact product
+    fa = np.concatenate(O.normalized_query(x, Wa, 1, d, True, 0.0, "f32"), axis=-1)
+    fb = np.concatenate(O.normalized_query(x, Wb, 1, d, True, 0.0, "f32"), axis=-1)
+    assert not np.array_equal(fa, fb)
+
+
+def test_bf16_gate_reads_its_stored_projection():
+    """The same for z = x W1 of the Memory+ gate: equal stored z, equal output; the exact
+    products would give different gated rows."""
+    d = 64
+    x, Wa, Wb = _projections_equal_when_stored(d, seed=10)
+    y = np.ones((1, d))
+    oa = O.memory_plus(y, x, Wa, np.eye(d), "bf16")
+    ob = O.memory_plus(y, x, Wb, np.eye(d), "bf16")
+    np.testing.assert_array_equal(oa, ob)
+    ga, gb = (O.round_stored(y * O.silu(x @ W), "bf16") for W in (Wa, Wb))
+    assert (ga != gb).sum() >= 3
+
+
 def test_hand_memory_plus():
     c = GOLD["memory_plus_case"]
     out = O.memory_plus(np.array(c["y"], float), np.array(c["x"], float), np.array(c["W1"], float),
@@ -365,15 +410,32 @@ def _rmsnorm_eps_outside(v, eps):
     return v / (np.sqrt(np.mean(v * v, axis=-1, keepdims=True)) + eps)
 
 
+def _normalized_query_from_exact_product(x, W_q, H, d_q, qk_norm, eps, dtype):
+    """Slip: the norm reads the exact product instead of the stored q."""
+    q = O.project_query(x, W_q, H, d_q)
+    q = O.rmsnorm(q, eps) if qk_norm else q
+    return O.split_halves(O.round_stored(q, dtype))
+
+
+def _memory_plus_from_exact_product(y, x, W1, W2, dtype):
+    """Slip: the gate reads the exact x W1 instead of the stored z."""
+    return O.round_stored(y * O.silu(x @ W1), dtype) @ W2
+
+
 @pytest.mark.parametrize("slip,target,pin", [
     ("head_split_transposed", "project_query", test_hand_two_head_forward),
     ("eps_outside_the_root", "rmsnorm", test_hand_rmsnorm_eps_inside_the_root),
+    ("query_norm_of_the_exact_product", "normalized_query", test_bf16_query_is_normalised_from_its_stored_projection),
+    ("gate_of_the_exact_product", "memory_plus", test_bf16_gate_reads_its_stored_projection),
 ])
 def test_pins_catch_planted_oracle_slips(monkeypatch, slip, target, pin):
-    """A wrong head split, or eps outside the square root, planted in the oracle's own step,
-    fails the hand-worked pin of that step."""
+    """A wrong head split, eps outside the square root, or a norm or gate that reads the exact
+    product instead of the stored one, planted in the oracle's own step, fails the pin of
+    that step."""
     pin()   # the true oracle passes
     monkeypatch.setattr(O, target, {"project_query": _project_query_interleaved,
-                                    "rmsnorm": _rmsnorm_eps_outside}[target])
+                                    "rmsnorm": _rmsnorm_eps_outside,
+                                    "normalized_query": _normalized_query_from_exact_product,
+                                    "memory_plus": _memory_plus_from_exact_product}[target])
     with pytest.raises(AssertionError):
         pin()
