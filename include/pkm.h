@@ -16,7 +16,7 @@
  *    and is bound by memory bandwidth.
  *
  * What pkm_forward computes for every token t (row-major, per head h < H):
- *   q        = x[t] W_q[:, h*d_q : (h+1)*d_q]                         (fp32 accumulate)
+ *   q        = x[t] W_q[:, h*d_q : (h+1)*d_q]           (fp32 accumulate, stored in dtype)
  *   qhat     = RMSNorm(q) if qk_norm else q, over all d_q; stored in dtype
  *   s_c[i]   = <qhat[c*d_h : (c+1)*d_h], Khat[h, c, i]>, c in {0, 1}, i < n_sub
  *              where Khat = RMSNorm(subkeys) per row if qk_norm (folded at create)
@@ -25,9 +25,10 @@
  *   idx, sc  = top-k cells under (score desc, flat index asc)
  *   w        = softmax(sc)                                             (per head)
  *   y[t]     = sum over h, j of w[h, j] * V[idx[h, j]]                 (fp32 accumulate)
- *   out[t]   = memory_plus ? (y * silu(x[t] W1)) W2 : y                (stored in dtype)
- * With dtype = BF16, qhat, Khat and y * silu(x W1) are rounded to bf16
- * (round-to-nearest-even); scores, softmax and y are fp32.
+ *   out[t]   = memory_plus ? (y * silu(z)) W2 : y, z = x[t] W1 (stored in dtype)
+ * With dtype = BF16, q, z, qhat, Khat and y * silu(z) are rounded to bf16
+ * (round-to-nearest-even): a bf16 product returns q and z in bf16, and the norm and
+ * the gate read those stored values; scores, softmax and y are fp32.
  *
  * Conventions for every call below:
  *  - Pointers to tensors are DEVICE pointers, row-major, owned by the caller

@@ -1,7 +1,8 @@
 // Dense GEMMs of the forward: the query projection q = x W_q, and the two Memory+
 // products ("Memory Layers at Scale" digest, Memory+ block: out = (y * silu(x W1)) W2):
-// z = x W1 in fp32 (the gate's elementwise part y * silu(z) is fused into the gather,
-// which writes g) and out = g W2.
+// z = x W1 (the gate's elementwise part y * silu(z) is fused into the gather, which writes
+// g) and out = g W2.  The bf16 products store their result in bf16 (the projection's q
+// and z too: 15-20% faster than fp32 output at 16,384 x 4,096 x 2,048).
 //
 // C[M, N] = A[M, K] * Bt[N, K]^T: both operands are K-contiguous (the weights are
 // transposed once at create), fp32 accumulation.
