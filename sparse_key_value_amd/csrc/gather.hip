@@ -109,17 +109,32 @@ __device__ __forceinline__ void gather_bag(const uint8_t* __restrict__ table, in
   const int64_t o = b * dim + (int64_t)col * E;
   if constexpr (ZB != 0) {
     // g = y * silu(z), stored in the table's type; z in fp32 (ZB = 4) or bf16 (ZB = 2, with bf16
-    // values: the lane's 8 elements of z in one 16-byte load)
-    if constexpr (ZB == 4) {
+    // values): the lane's E elements of z in 16-byte loads when every z row is 16-byte aligned,
+    // else (ZB < 0) in 4-byte loads (z rows are always 4-byte aligned)
+    if constexpr (ZB == 4 || ZB == -4) {
+      const float* zr = (const float*)z + b * z_ld + (int64_t)col * E;
 #pragma unroll
       for (int e = 0; e < E; e += 4) {
-        const f32x4 zz = __builtin_nontemporal_load((const f32x4*)((const float*)z + b * z_ld + (int64_t)col * E + e));
+        f32x4 zz;
+        if constexpr (ZB == 4) {
+          zz = __builtin_nontemporal_load((const f32x4*)(zr + e));
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) zz[x] = __builtin_nontemporal_load(zr + e + x);
+        }
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc[e + x] = acc[e + x] * silu_f32(zz[x]);
       }
     } else {
-      static_assert(ZB == 2 && EB == 2, "a bf16 z goes with bf16 values");
-      const u32x4 zz = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)z + b * z_ld + (int64_t)col * E));
+      static_assert((ZB == 2 || ZB == -2) && EB == 2, "a bf16 z goes with bf16 values");
+      const uint16_t* zr = (const uint16_t*)z + b * z_ld + (int64_t)col * E;
+      u32x4 zz;
+      if constexpr (ZB == 2) {
+        zz = __builtin_nontemporal_load((const u32x4*)zr);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) zz[x] = __builtin_nontemporal_load((const uint32_t*)zr + x);
+      }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         acc[2 * x] = acc[2 * x] * silu_f32(bf16_lo(zz[x]));
@@ -178,14 +193,31 @@ hipError_t launch_gather(const void* table, int64_t n_rows, int dim, int dtype, 
 #define PKM_GATHER(EBV, UNI, ZBV)                                                                             \
   gather_kernel<EBV, 16, UNI, ZBV><<<grid, threads, 0, s>>>((const uint8_t*)table, n_rows, row_vecs, tpr, bpb, idx, \
                                                             w, n_bags, bag, y, y_f32, z, z_ld)
+  // z rows whose start is not 16-byte aligned (a query width or head count that leaves the z
+  // columns, or the row pitch, off a 16-byte multiple) take 4-byte loads
+  const int zb = z_bf16 ? 2 : 4;
+  const bool z16 = z && ((uintptr_t)z & 15) == 0 && (z_ld * zb) % 16 == 0;
+  if (z && (((uintptr_t)z & 3) != 0 || (z_ld * zb) % 4 != 0)) return hipErrorInvalidValue;
   if (z && z_bf16) {
     if (eb != 2) return hipErrorInvalidValue;  // a bf16 z comes with bf16 values
-    if (uniform) PKM_GATHER(2, true, 2); else PKM_GATHER(2, false, 2);
+    if (z16) {
+      if (uniform) PKM_GATHER(2, true, 2); else PKM_GATHER(2, false, 2);
+    } else {
+      if (uniform) PKM_GATHER(2, true, -2); else PKM_GATHER(2, false, -2);
+    }
   } else if (z) {
     if (eb == 2) {
-      if (uniform) PKM_GATHER(2, true, 4); else PKM_GATHER(2, false, 4);
+      if (z16) {
+        if (uniform) PKM_GATHER(2, true, 4); else PKM_GATHER(2, false, 4);
+      } else {
+        if (uniform) PKM_GATHER(2, true, -4); else PKM_GATHER(2, false, -4);
+      }
     } else {
-      if (uniform) PKM_GATHER(4, true, 4); else PKM_GATHER(4, false, 4);
+      if (z16) {
+        if (uniform) PKM_GATHER(4, true, 4); else PKM_GATHER(4, false, 4);
+      } else {
+        if (uniform) PKM_GATHER(4, true, -4); else PKM_GATHER(4, false, -4);
+      }
     }
   } else if (eb == 2) {
     if (uniform) PKM_GATHER(2, true, 0); else PKM_GATHER(2, false, 0);

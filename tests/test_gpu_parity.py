@@ -298,6 +298,12 @@ def test_edge_shapes(case, dt):
     # 256-wide sub-keys (the 16M-key kernels) with a partial last chunk of sub-keys
     dict(name="dh256_partial_chunk", dtype="bf16", qk_norm=True, n_sub=77, k=8, H=2, d_q=512, d_model=128, d_v=64,
          T=70),
+    # gated, with z rows off 16-byte alignment (the gate reads z in 4-byte loads): bf16 z at
+    # byte 12 of a 140-byte row, fp32 z at byte 24 of a 56-byte row
+    dict(name="bf16_gate_z_unaligned", dtype="bf16", qk_norm=True, memory_plus=True, n_sub=96, k=8, H=1, d_q=6,
+         d_model=64, d_v=64, T=50),
+    dict(name="f32_gate_z_unaligned", dtype="f32", qk_norm=True, memory_plus=True, n_sub=96, k=8, H=3, d_q=2,
+         d_model=64, d_v=8, T=50),
 ])
 def test_flag_combinations(case):
     case = dict(case)
