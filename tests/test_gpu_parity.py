@@ -506,6 +506,17 @@ def test_full_size_as_benchmarked(name):
     wl = _G().Workload(cfg)
     say(f"{name}: forward T={cfg.T}")
     o = run_debug(wl)
+    # the entry point the benchmark times (no debug outputs) returns the debug forward's
+    # results bit for bit, so the oracle checks below hold for it too
+    import sparse_key_value_amd as P
+    plain = (torch.empty((cfg.T, cfg.d_out), dtype=_G().TORCH_DT[cfg.dtype], device="cuda"),
+             torch.empty((cfg.T, cfg.H, cfg.k), dtype=torch.int32, device="cuda"),
+             torch.empty((cfg.T, cfg.H, cfg.k), dtype=torch.float32, device="cuda"))
+    P.pkm_forward(wl.pkm.handle, wl.dev["x"], cfg.T, *plain)
+    torch.cuda.synchronize()
+    for key, t in zip(("out", "idx", "w"), plain):
+        np.testing.assert_array_equal(_G().to_host(t), o[key], err_msg=f"{name}: plain forward {key}")
+    del plain
     # properties over every token
     assert (o["idx"] >= 0).all() and (o["idx"] < cfg.N).all()
     np.testing.assert_allclose(o["w"].sum(axis=-1), 1.0, atol=1e-5)
