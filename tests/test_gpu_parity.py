@@ -237,11 +237,13 @@ def test_tiny_fp32_ragged_token_counts(T):
     wl.close()
 
 
-@pytest.mark.parametrize("name,T", [("memplus_16m_bf16", 200), ("memplus_64m_bf16", 77)])
+@pytest.mark.parametrize("name,T", [("memplus_16m_bf16", 200), ("memplus_64m_bf16", 77),
+                                    ("memplus_16m_bf16", 1), ("memplus_64m_bf16", 1)])
 def test_small_batches_split_the_sub_keys(name, T):
-    """A batch far smaller than the chip (200 and 77 tokens over 4,096 and 8,192 sub-keys):
-    every block sweeps one range of the sub-keys and the ranges share each row's candidate
-    list through atomic counts."""
+    """A batch far smaller than the chip (200 and 77 tokens over 4,096 and 8,192 sub-keys, and a
+    single token, whose one valid lane per wave fragment meets every split): every block sweeps
+    one range of the sub-keys and the ranges share each row's candidate list through atomic
+    counts."""
     cfg = CONFIGS[name].with_(T=T)
     say(f"{name} T={T}: sub-key splits")
     wl = _G().Workload(cfg, T=T)
