@@ -8,14 +8,20 @@
 // transposed once at create), fp32 accumulation.
 //  * bf16: these are plain GEMMs (no fused epilogue), so they go to hipBLASLt, which on
 //    MI355X runs the 16384 x 2048 x 2048 shapes at 1.0-1.35 PFLOP/s against 0.8 for the
-//    hand-written MFMA tiles this file held before.  Plans (descriptors, layouts and the
-//    heuristic's first algorithm, no workspace) are made once per device and shape and
-//    kept for the process; the heuristic query is host work of about 0.1 s per new shape.
+//    hand-written MFMA tiles this file held before.  The algorithm (the heuristic's first,
+//    no workspace) is chosen once per device, (N, K, output type) and power-of-two bucket of
+//    M, by a heuristic query for the bucket's largest M: the query is host work of about
+//    0.1 s, so a batch size seen for the first time costs it only when its bucket is new, and
+//    the number of queries stays bounded (at most 25 buckets per shape).  A plan for an exact
+//    M (its layouts and the bucket's algorithm, checked to support that M, else the
+//    heuristic's choice for it) is kept in a small cache, least recently used first out.
 //    All candidate algorithms for these shapes were checked to be bitwise deterministic.
 //  * fp32: a plain SIMT tile (64 x 64 x 16, 4 x 4 per thread) for the fp32 workloads.
+#include <hipblaslt/hipblaslt-ext.hpp>
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
+#include <memory>
 #include <mutex>
 #include <tuple>
 
@@ -78,16 +84,70 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 // hipBLASLt is column-major: C[M, N] row-major is the column-major N x M matrix
 // Bt^T(op T on the column-major K x N view of Bt) times A (the column-major K x M view of A).
 struct LtPlan {
+  LtPlan() = default;
+  LtPlan(const LtPlan&) = delete;
+  LtPlan& operator=(const LtPlan&) = delete;
   hipblasLtMatmulDesc_t op = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
   hipblasLtMatmulAlgo_t algo;
+  ~LtPlan() {
+    if (lc) hipblasLtMatrixLayoutDestroy(lc);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
 };
 
-std::mutex g_lt_mu;
-std::map<int, hipblasLtHandle_t> g_lt;                                  // per device
-std::map<std::tuple<int, int64_t, int, int, int>, LtPlan> g_plans;      // (device, M, N, K, out fp32)
+// (device, M, N, K, out fp32); the algorithm cache's M is the bucket's largest M
+typedef std::tuple<int, int64_t, int, int, int> PlanKey;
+constexpr size_t MAX_PLANS = 64;
 
-hipError_t lt_plan(int dev, int64_t M, int N, int K, bool out_f32, hipblasLtHandle_t* h, const LtPlan** plan) {
+// The caches live until the process ends and are never destroyed (like the hipBLASLt
+// handles): at exit, a destructor calling into hipBLASLt could run after its own teardown.
+// Evicted plans are destroyed while the process runs, once no launch holds them.
+std::mutex g_lt_mu;
+auto& g_lt = *new std::map<int, hipblasLtHandle_t>;                       // per device
+auto& g_algos = *new std::map<PlanKey, hipblasLtMatmulAlgo_t>;            // per bucket of M
+auto& g_plans = *new std::map<PlanKey, std::pair<std::shared_ptr<const LtPlan>, uint64_t>>;  // exact M, last use
+uint64_t g_tick = 0;
+
+// descriptors of C[M, N] = A[M, K] Bt[N, K]^T with bf16 operands; false on failure
+bool make_descs(LtPlan& P, int64_t M, int N, int K, bool out_f32) {
+  bool ok = hipblasLtMatmulDescCreate(&P.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+  const hipblasOperation_t tA = HIPBLAS_OP_T, tB = HIPBLAS_OP_N;
+  ok = ok && hipblasLtMatmulDescSetAttribute(P.op, HIPBLASLT_MATMUL_DESC_TRANSA, &tA, sizeof tA) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatmulDescSetAttribute(P.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tB, sizeof tB) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&P.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&P.lb, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&P.lc, out_f32 ? HIP_R_32F : HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS;
+  return ok;
+}
+
+// the heuristic's first algorithm (no workspace) for the plan's shape; false if none
+bool heuristic_algo(hipblasLtHandle_t h, const LtPlan& P, hipblasLtMatmulAlgo_t* algo) {
+  hipblasLtMatmulPreference_t pref = nullptr;
+  bool ok = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+  const uint64_t no_ws = 0;
+  ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws,
+                                                   sizeof no_ws) == HIPBLAS_STATUS_SUCCESS;
+  hipblasLtMatmulHeuristicResult_t res[1];
+  int got = 0;
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, P.op, P.la, P.lb, P.lc, P.lc, pref, 1, res, &got) ==
+                 HIPBLAS_STATUS_SUCCESS && got > 0;
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (ok) *algo = res[0].algo;
+  return ok;
+}
+
+// the largest M of M's bucket: the next power of two (M >= 1)
+int64_t bucket_top(int64_t M) {
+  int64_t b = 1;
+  while (b < M) b <<= 1;
+  return b;
+}
+
+hipError_t lt_plan(int dev, int64_t M, int N, int K, bool out_f32, hipblasLtHandle_t* h,
+                   std::shared_ptr<const LtPlan>* plan) {
   std::lock_guard<std::mutex> lock(g_lt_mu);
   auto hit = g_lt.find(dev);
   if (hit == g_lt.end()) {
@@ -96,38 +156,40 @@ hipError_t lt_plan(int dev, int64_t M, int N, int K, bool out_f32, hipblasLtHand
     hit = g_lt.emplace(dev, lt).first;
   }
   *h = hit->second;
-  const auto key = std::make_tuple(dev, M, N, K, out_f32 ? 1 : 0);
+  const PlanKey key = std::make_tuple(dev, M, N, K, out_f32 ? 1 : 0);
   auto p = g_plans.find(key);
-  if (p == g_plans.end()) {
-    LtPlan P;
-    bool ok = hipblasLtMatmulDescCreate(&P.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
-    const hipblasOperation_t tA = HIPBLAS_OP_T, tB = HIPBLAS_OP_N;
-    ok = ok && hipblasLtMatmulDescSetAttribute(P.op, HIPBLASLT_MATMUL_DESC_TRANSA, &tA, sizeof tA) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatmulDescSetAttribute(P.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tB, sizeof tB) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&P.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&P.lb, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS;
-    ok = ok && hipblasLtMatrixLayoutCreate(&P.lc, out_f32 ? HIP_R_32F : HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
-    const uint64_t no_ws = 0;
-    ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws,
-                                                     sizeof no_ws) == HIPBLAS_STATUS_SUCCESS;
-    hipblasLtMatmulHeuristicResult_t res[1];
-    int got = 0;
-    ok = ok && hipblasLtMatmulAlgoGetHeuristic(*h, P.op, P.la, P.lb, P.lc, P.lc, pref, 1, res, &got) ==
-                   HIPBLAS_STATUS_SUCCESS && got > 0;
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (!ok) {
-      if (P.lc) hipblasLtMatrixLayoutDestroy(P.lc);
-      if (P.lb) hipblasLtMatrixLayoutDestroy(P.lb);
-      if (P.la) hipblasLtMatrixLayoutDestroy(P.la);
-      if (P.op) hipblasLtMatmulDescDestroy(P.op);
-      return hipErrorNotSupported;
-    }
-    P.algo = res[0].algo;
-    p = g_plans.emplace(key, P).first;
+  if (p != g_plans.end()) {
+    p->second.second = ++g_tick;
+    *plan = p->second.first;
+    return hipSuccess;
   }
-  *plan = &p->second;
+  // the bucket's algorithm, from a heuristic query for the bucket's largest M
+  const PlanKey bkey = std::make_tuple(dev, bucket_top(M), N, K, out_f32 ? 1 : 0);
+  auto a = g_algos.find(bkey);
+  if (a == g_algos.end()) {
+    LtPlan B;
+    hipblasLtMatmulAlgo_t algo;
+    if (!make_descs(B, bucket_top(M), N, K, out_f32) || !heuristic_algo(*h, B, &algo)) return hipErrorNotSupported;
+    a = g_algos.emplace(bkey, algo).first;
+  }
+  auto P = std::make_shared<LtPlan>();
+  if (!make_descs(*P, M, N, K, out_f32)) return hipErrorNotSupported;
+  P->algo = a->second;
+  size_t ws = 0;
+  const float alpha = 1.0f, beta = 0.0f;
+  if (hipblaslt_ext::matmulIsAlgoSupported(*h, P->op, &alpha, P->la, P->lb, &beta, P->lc, P->lc, P->algo, ws) !=
+          HIPBLAS_STATUS_SUCCESS || ws != 0) {
+    // the bucket's choice does not take this M (or would need a workspace): the heuristic's for it
+    if (!heuristic_algo(*h, *P, &P->algo)) return hipErrorNotSupported;
+  }
+  if (g_plans.size() >= MAX_PLANS) {  // evict the least recently used; launches holding it keep it alive
+    auto old = g_plans.begin();
+    for (auto it = g_plans.begin(); it != g_plans.end(); ++it)
+      if (it->second.second < old->second.second) old = it;
+    g_plans.erase(old);
+  }
+  g_plans.emplace(key, std::make_pair(std::shared_ptr<const LtPlan>(P), ++g_tick));
+  *plan = P;
   return hipSuccess;
 }
 
@@ -141,7 +203,7 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N,
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     hipblasLtHandle_t h;
-    const LtPlan* P;
+    std::shared_ptr<const LtPlan> P;
     if ((e = lt_plan(dev, M, N, K, epi == EPI_STORE_F32, &h, &P)) != hipSuccess) return e;
     const float alpha = 1.0f, beta = 0.0f;
     if (hipblasLtMatmul(h, P->op, &alpha, Bt, P->la, A, P->lb, &beta, C, P->lc, C, P->lc, &P->algo, nullptr, 0, s) !=
