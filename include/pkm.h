@@ -35,10 +35,12 @@
  *    (typically PyTorch tensors) and must stay valid while in use.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work and returns without waiting for the GPU;
- *    the forward allocates nothing and performs no host sync, so a forward
- *    (default single-stream mode, GEMM plans made by an earlier call of the same
- *    shape) can be captured in a HIP graph and replayed.  Its results are
- *    ordered on `stream`: work enqueued on `stream` afterwards sees them.
+ *    the forward allocates nothing and performs no host sync, so a forward can
+ *    be captured in a HIP graph and replayed once an earlier call with the same
+ *    number of tokens has made its GEMM plans (bf16: host work only; the first
+ *    call whose token count falls in a new power-of-two bucket also runs one
+ *    hipBLASLt heuristic query, about 0.1 s).  Its results are ordered on
+ *    `stream`: work enqueued on `stream` afterwards sees them.
  *  - A handle belongs to the device that is current at pkm_create.
  *  - Return value: PKM_OK (0) or a negative PKM_E* code; on error, the message
  *    is available from pkm_last_error() (thread-local) and nothing was enqueued
