@@ -15,6 +15,8 @@
 //    the number of queries stays bounded (at most 25 buckets per shape).  A plan for an exact
 //    M (its layouts and the bucket's algorithm, checked to support that M, else the
 //    heuristic's choice for it) is kept in a small cache, least recently used first out.
+//    Host threads share the handle, the caches and the plans under one lock, which is also held
+//    while a product is enqueued.
 //    All candidate algorithms for these shapes were checked to be bitwise deterministic.
 //  * fp32: a plain SIMT tile (64 x 64 x 16, 4 x 4 per thread) for the fp32 workloads.
 #include <hipblaslt/hipblaslt-ext.hpp>
@@ -206,10 +208,12 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N,
     std::shared_ptr<const LtPlan> P;
     if ((e = lt_plan(dev, M, N, K, epi == EPI_STORE_F32, &h, &P)) != hipSuccess) return e;
     const float alpha = 1.0f, beta = 0.0f;
-    if (hipblasLtMatmul(h, P->op, &alpha, Bt, P->la, A, P->lb, &beta, C, P->lc, C, P->lc, &P->algo, nullptr, 0, s) !=
-        HIPBLAS_STATUS_SUCCESS)
-      return hipErrorLaunchFailure;
-    return hipSuccess;
+    hipblasStatus_t st;
+    {  // host threads share one hipBLASLt handle per device: its calls (enqueue only) are serialised
+      std::lock_guard<std::mutex> lock(g_lt_mu);
+      st = hipblasLtMatmul(h, P->op, &alpha, Bt, P->la, A, P->lb, &beta, C, P->lc, C, P->lc, &P->algo, nullptr, 0, s);
+    }
+    return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
   } else {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     const float* a = (const float*)A;

@@ -464,6 +464,52 @@ def test_many_batch_sizes_rebuild_their_gemm_plans_alike():
     wl.close()
 
 
+def test_concurrent_forwards_share_the_gemm_plans():
+    """Two host threads, each with its own handle and stream, run forwards over 70 batch sizes
+    at once (both bf16 products per forward): they share the library's GEMM plans, whose
+    cache evicts entries while the other thread may be launching with them.  Every result
+    equals the same forward run alone afterwards, bit for bit."""
+    import threading
+
+    import sparse_key_value_amd as P
+    cfg = CONFIGS["pkm_1m_bf16"].with_(n_sub=256, T=96, d_v=256, memory_plus=True, d_model=256)
+    say("concurrent forwards over batch sizes")
+    wls = [_G().Workload(cfg, seed=s) for s in (21, 22)]
+    sizes = [list(range(1, 71)), list(range(96, 26, -1))]
+
+    def fwd(wl, T, stream):
+        out = torch.empty((T, cfg.d_out), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((T, cfg.H, cfg.k), dtype=torch.int32, device="cuda")
+        P.pkm_forward(wl.pkm.handle, wl.dev["x"], T, out, idx, None, stream=stream)
+        stream.synchronize()
+        return out.view(torch.int16).cpu().numpy(), idx.cpu().numpy()
+
+    got = [{}, {}]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            for T in sizes[i]:
+                got[i][T] = fwd(wls[i], T, s)
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    s = torch.cuda.Stream()
+    for i in range(2):
+        for T in sizes[i]:
+            for a, b in zip(got[i][T], fwd(wls[i], T, s)):
+                np.testing.assert_array_equal(a, b)
+    for wl in wls:
+        wl.close()
+
+
 def test_forward_on_a_side_stream_follows_its_inputs():
     """The forward enqueues every kernel (hipBLASLt's included) on the caller's stream: on a
     side stream whose input is written late by earlier work on that same stream, the result
