@@ -41,7 +41,9 @@
  *    call whose token count falls in a new power-of-two bucket also runs one
  *    hipBLASLt heuristic query, about 0.1 s).  Its results are ordered on
  *    `stream`: work enqueued on `stream` afterwards sees them.
- *  - A handle belongs to the device that is current at pkm_create.
+ *  - A handle belongs to the device that is current at pkm_create.  One call at
+ *    a time may use a handle; different handles may be used by different host
+ *    threads at once (the library's shared GEMM plans are guarded by a lock).
  *  - Return value: PKM_OK (0) or a negative PKM_E* code; on error, the message
  *    is available from pkm_last_error() (thread-local) and nothing was enqueued
  *    unless the code is PKM_EHIP.  Nothing aborts and no C++ exception leaves
