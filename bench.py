@@ -112,6 +112,32 @@ def counter_traffic(counters_file=COUNTERS_FILE):
         return None
 
 
+def source_digest():
+    """sha256 (first 16 hex digits) over the library's kernel and header sources, in path order:
+    names the code a bench line measured (the GPU run has no git metadata)."""
+    h = hashlib.sha256()
+    for d in ("sparse_key_value_amd/csrc", "include"):
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            if name.endswith((".hip", ".hpp", ".h")):
+                h.update(f"{d}/{name}\0".encode())
+                h.update(open(os.path.join(ROOT, d, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def environment(a):
+    """Seed, software stack and device of a bench line."""
+    env = {"seed": a.seed, "source_sha16": source_digest(), "torch": None, "hip": None, "device": None, "arch": None}
+    try:
+        import torch
+        env["torch"], env["hip"] = torch.__version__, torch.version.hip
+        if torch.cuda.is_available():
+            p = torch.cuda.get_device_properties(0)
+            env["device"], env["arch"] = p.name, getattr(p, "gcnArchName", None)
+    except Exception as ex:  # the line still prints without it
+        log(f"environment: {ex}")
+    return env
+
+
 def cpu_baseline(wl, cfg, target_s, max_tokens=None):
     """Time the oracle on the first S tokens of the same workload on the host cores."""
     import numpy as np
@@ -329,6 +355,7 @@ def bench_engram(a):
         "unique_rows": uniq,
         "unique_row_bytes": uniq * cfg.head_dim * eb if uniq is not None else None,
         "stream_read_GBps": stream_gbps,
+        "env": environment(a),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -426,6 +453,7 @@ def bench_engram_host(a):
                      "frac": achieved / HOST_LINK_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": link_b,
                      "avg_launch_ms": pf_ms},
         "prefetch_ms": pf_ms, "staged_gate_ms": gate_ms,
+        "env": environment(a),
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -542,6 +570,7 @@ def bench_backward(a):
         "dw_alone": {"kernel": "bag_dw_kernel (dw + ds, no update)", "ms": dw_ms, "algorithmic_bytes": dw_bytes,
                      "GBps": dw_bytes / (dw_ms * 1e-3) / 1e9,
                      "frac_hbm": dw_bytes / (dw_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "env": environment(a),
         "cpu_baseline": None if a.no_cpu_baseline else backward_cpu_baseline(a, cfg, wl, idx, w, dy),
     }
     print(json.dumps(res), flush=True)
@@ -591,6 +620,7 @@ def bench_uniform(a):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "traffic": None, "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": ms},
         "value_rows_GBps": rows_b / (ms * 1e-3) / 1e9,
+        "env": environment(a),
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -654,6 +684,7 @@ def bench_shard(a):
                      "frac": alg_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
                      "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": ms},
         "value_rows_GBps": rows_b / (ms * 1e-3) / 1e9,
+        "env": environment(a),
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -738,6 +769,7 @@ def bench_ma(a):
                      "algorithmic_bytes_per_launch": alg_b, "avg_launch_ms": launch_ms,
                      "table_MiB_vs_llc_MiB": [cfg.vocab * cfg.d_v * eb / 2**20, 256]},
         "unique_ids": uniq,
+        "env": environment(a),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -865,7 +897,7 @@ def main():
     achieved = alg_b / (g_ms * 1e-3) / 1e9
     log("stages (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in stages.items() if v is not None))
 
-    rr_ms = None
+    rr_ms = uniq = None
     if not host:
         # the same rows read with the gather's lane layout and no arithmetic (XOR only): the
         # read rate of this random-row pattern, the gather's own ceiling
@@ -882,6 +914,7 @@ def main():
             torch.cuda.synchronize()
             rr.append(ev0.elapsed_time(ev1))
         rr_ms = sorted(rr)[1]
+        uniq = int(torch.unique(sel).numel())
         del sel, rr_out
         log(f"row read of the forward's rows (no arithmetic): {rr_ms:.3f} ms against the gather's {g_ms:.3f} ms")
 
@@ -923,10 +956,14 @@ def main():
         "row_read_ms": rr_ms,
         "row_read_value_GBps": rows_b / (rr_ms * 1e-3) / 1e9 if rr_ms else None,
         "gather_time_over_row_read": g_ms / rr_ms if rr_ms else None,
+        # distinct rows among the T * H * k selected (a row picked twice is read twice)
+        "unique_rows": uniq,
+        "unique_row_GBps": uniq * cfg.d_v * cfg.elem_bytes / (g_ms * 1e-3) / 1e9 if uniq else None,
         "stages_ms": stages,
         "stages_note": f"from {n_bd} forwards after the timed steps with every stage's events recorded (the events "
                        "slow a forward by about 2%; the timed steps record the gather's alone)",
         **stage_rates(cfg, T, stages),
+        "env": environment(a),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -60,3 +60,21 @@ def test_stage_flops_are_charged_to_the_stage_that_runs_them():
     r1 = bench.stage_rates(c1, c1.T, {"project": 0.05, "score": 0.1, "gate": None})
     assert r1["gate_TFLOPs"] is None and r1["project_TFLOPs"] > 0
     assert bench.stage_rates(c1, c1.T, {"score": float("nan")})["score_mfma_frac"] is None
+
+
+def test_environment_names_the_seed_stack_and_sources():
+    """Every bench line carries its seed, torch/HIP versions, device and a digest of the library's
+    sources; on a host without a GPU the device fields are None and the line still prints."""
+    sys.path.insert(0, ROOT)
+    import types
+
+    import bench
+
+    env = bench.environment(types.SimpleNamespace(seed=7))
+    assert env["seed"] == 7
+    assert len(env["source_sha16"]) == 16 and int(env["source_sha16"], 16) >= 0
+    assert env["source_sha16"] == bench.source_digest()      # deterministic
+    assert isinstance(env["torch"], str)
+    import torch
+    if not torch.cuda.is_available():
+        assert env["device"] is None and env["arch"] is None
