@@ -570,16 +570,18 @@ def _benchmark_block_rows(T, n_random=272, seed=1):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["memplus_16m_bf16", "memplus_64m_bf16", "pkm_1m_bf16"])
-def test_full_size_as_benchmarked(name):
+@pytest.mark.parametrize("name,seed", [("memplus_16m_bf16", 0), ("memplus_64m_bf16", 0), ("pkm_1m_bf16", 0),
+                                       ("memplus_16m_bf16", 1)])
+def test_full_size_as_benchmarked(name, seed):
     """The headline, the largest and the 1M-key workload at full size, run exactly as the
-    benchmark runs them.  Properties on every token; the oracle on 1,024 tokens of the 16M- and
-    64M-key batches (a whole 512-token scoring block, the end of the last block and random
-    tokens), and stage-wise on all 8,192 tokens of the 1M-key batch (which takes the 32-token
-    waves of the scoring passes) with end to end on a sample."""
+    benchmark runs them (the headline also on a second seed: other inputs, weights and table).
+    Properties on every token; the oracle on 1,024 tokens of the 16M- and 64M-key batches (a
+    whole 512-token scoring block, the end of the last block and random tokens), and stage-wise
+    on all 8,192 tokens of the 1M-key batch (which takes the 32-token waves of the scoring
+    passes) with end to end on a sample."""
     cfg = CONFIGS[name]
-    say(f"{name}: filling {cfg.N} x {cfg.d_v} value table on the GPU")
-    wl = _G().Workload(cfg)
+    say(f"{name} seed {seed}: filling {cfg.N} x {cfg.d_v} value table on the GPU")
+    wl = _G().Workload(cfg, seed=seed)
     say(f"{name}: forward T={cfg.T}")
     o = run_debug(wl)
     # the entry point the benchmark times (no debug outputs) returns the debug forward's
@@ -600,7 +602,7 @@ def test_full_size_as_benchmarked(name):
     if cfg.T <= 8192:
         rows, e2e = None, _sample_rows(cfg.T)
     else:
-        rows, e2e = _benchmark_block_rows(cfg.T), None
+        rows, e2e = _benchmark_block_rows(cfg.T, seed=1 + seed), None
     say(f"{name}: oracle stage-wise on {cfg.T if rows is None else len(rows)} tokens")
     full_check(wl, o, rows=rows, e2e_rows=e2e)
     wl.close()
