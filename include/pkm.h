@@ -71,12 +71,12 @@ enum {
 typedef enum { PKM_F32 = 0, PKM_BF16 = 1 } pkm_dtype;
 
 typedef struct {
-  int32_t d_model;      /* width of x; a multiple of 32 for bf16 (4 for fp32) */
+  int32_t d_model;      /* width of x, <= 65536; a multiple of 32 for bf16 (4 for fp32) */
   int32_t n_heads;      /* 1 <= H <= 64 */
   int32_t d_query;      /* per-head query width d_q: even, 2..512 (larger: PKM_EUNSUPPORTED) */
   int32_t n_sub;        /* sub-keys per half; the table has N = n_sub^2 < 2^31 rows */
   int32_t k;            /* per-half and final top-k, 1 <= k <= min(n_sub, 64) */
-  int32_t d_value;      /* value width; d_value * sizeof(dtype) a multiple of 16 (bf16 Memory+: of 64) */
+  int32_t d_value;      /* value width, <= 65536; d_value * sizeof(dtype) a multiple of 16 (bf16 Memory+: of 64) */
   int32_t dtype;        /* pkm_dtype of x, W_q, subkeys, values, W1, W2 and out */
   int32_t qk_norm;      /* 0 or 1: RMSNorm of the query (before the split) and of sub-key rows */
   int32_t memory_plus;  /* 0: out = y [T, d_value]; 1: gated out [T, d_model] */

@@ -39,8 +39,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
   __shared__ float Bs[16][64 + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * 64;
-  const int n0 = blockIdx.x * 64;
+  // token tiles on the grid's x dimension (2^31 - 1 blocks; y holds at most 65,536)
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += 16) {
     // 64 rows x 16 k of each operand: 1024 elements, 4 per thread
@@ -215,7 +216,7 @@ hipError_t launch_gemm(const void* A, const void* Bt, void* C, int64_t M, int N,
     }
     return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
   } else {
-    dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64));
     const float* a = (const float*)A;
     const float* b = (const float*)Bt;
     gemm_f32_kernel<<<grid, 256, 0, s>>>(a, b, (float*)C, M, N, K);

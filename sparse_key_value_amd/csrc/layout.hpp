@@ -39,6 +39,9 @@ inline std::string check_config(const pkm_config* c) {
   if (c->dtype == PKM_BF16 && c->d_model % 32 != 0) return "d_model must be a multiple of 32 for bf16 (GEMM K-tile)";
   if (c->dtype == PKM_BF16 && c->memory_plus && c->d_value % 32 != 0)
     return "d_value must be a multiple of 32 for the bf16 Memory+ gate (GEMM K-tile)";
+  // the weight transposes at create tile d_model and d_value on a launch grid's y dimension,
+  // which holds at most 65,536 blocks (of 32 rows each here: any width up to 65,536 fits)
+  if (c->d_model > 65536) return "d_model must be <= 65536";
   if (c->n_heads < 1 || c->n_heads > 64) return "n_heads must be in [1, 64]";
   if (c->d_query <= 0 || c->d_query % 2 != 0) return "d_query must be positive and even";
   if (c->n_sub < 1) return "n_sub must be >= 1";
@@ -46,6 +49,7 @@ inline std::string check_config(const pkm_config* c) {
   if (c->k < 1 || c->k > 64 || c->k > c->n_sub) return "k must satisfy 1 <= k <= min(n_sub, 64)";
   if (c->d_value <= 0 || ((int64_t)c->d_value * eb) % 16 != 0)
     return "d_value * sizeof(dtype) must be a positive multiple of 16";
+  if (c->d_value > 65536) return "d_value must be <= 65536";
   if (c->qk_norm != 0 && c->qk_norm != 1) return "qk_norm must be 0 or 1";
   if (c->memory_plus != 0 && c->memory_plus != 1) return "memory_plus must be 0 or 1";
   if (!(c->norm_eps >= 0.0f) || c->norm_eps > 1.0f) return "norm_eps must be in [0, 1]";

@@ -76,6 +76,8 @@ def test_workspace_size_matches_layout(P):
     (dict(k=64, n_sub=63), "k must"),
     (dict(k=9, n_sub=8), "k must"),
     (dict(d_value=12), "d_value"),
+    (dict(d_model=65536 + 32), "d_model must be <= 65536"),     # weight transposes: grid y of 32-row tiles
+    (dict(d_value=65536 + 32), "d_value must be <= 65536"),
     (dict(qk_norm=2), "qk_norm"),
     (dict(max_tokens=0), "max_tokens"),
     (dict(max_tokens=1 << 25), "max_tokens"),

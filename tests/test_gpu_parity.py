@@ -237,6 +237,30 @@ def test_tiny_fp32_ragged_token_counts(T):
     wl.close()
 
 
+@pytest.mark.timeout(600)
+def test_fp32_batch_with_more_token_tiles_than_a_grid_row():
+    """An fp32 gated batch of 65,537 * 64 tokens: its two fp32 GEMMs have one more 64-token tile
+    than a launch grid's y dimension holds (65,536), so the tiles run along x.  Narrow widths keep
+    it small; properties on every token, the oracle on the first and last tiles and random tokens."""
+    T = 65537 * 64
+    cfg = CONFIGS["tiny_fp32_65k"].with_(name="fp32_4m_tokens", T=T, d_model=16, H=1, d_q=8, n_sub=16, k=4,
+                                         d_v=16, qk_norm=True, memory_plus=True)
+    say(f"fp32 T={T}")
+    wl = _G().Workload(cfg)
+    o = run_debug(wl)
+    assert o["idx"].shape == (T, 1, 4) and o["out"].shape == (T, 16)
+    assert (o["idx"] >= 0).all() and (o["idx"] < cfg.N).all()
+    np.testing.assert_allclose(o["w"].sum(axis=-1), 1.0, atol=1e-5)
+    check_order_valid(o["idx"], o["score"], "final lists (all tokens)")
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), rng.choice(T, 128, replace=False)]))
+    full_check(wl, o, rows=rows)
+    wl.close()
+    del wl, o
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,T", [("memplus_16m_bf16", 200), ("memplus_64m_bf16", 77),
                                     ("memplus_16m_bf16", 1), ("memplus_64m_bf16", 1)])
 def test_small_batches_split_the_sub_keys(name, T):
