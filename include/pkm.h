@@ -176,8 +176,8 @@ int pkm_copy_normalized_subkeys(pkm_handle* h, void* dst, void* stream);
 /* Weighted EmbeddingBag in sum mode over a table of n_rows x dim (dtype):
  *   y[b, :] = sum over j < bag_size of w[b, j] * table[idx[b, j], :]     (fp32)
  * idx [n_bags, bag_size] int32, w [n_bags, bag_size] fp32, y [n_bags, dim] fp32.
- * Indices outside [0, n_rows) contribute nothing.  dim * sizeof(dtype) must be
- * a multiple of 16 and the table 16-byte aligned; the table may be device memory or
+ * Indices outside [0, n_rows) contribute nothing.  dim <= 2^24, dim * sizeof(dtype) a
+ * multiple of 16 and the table 16-byte aligned; the table may be device memory or
  * pinned host memory (as `values` of pkm_create).  n_bags = 0 enqueues nothing. */
 int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dtype,
                       const int32_t* idx, const float* w, int64_t n_bags, int32_t bag_size, float* y,

@@ -360,6 +360,9 @@ int pkm_embedding_bag(const void* table, int64_t n_rows, int32_t dim, int32_t dt
   if (dtype != PKM_F32 && dtype != PKM_BF16) return fail(PKM_EINVAL, "dtype must be PKM_F32 or PKM_BF16");
   const int eb = dtype == PKM_BF16 ? 2 : 4;
   if (dim <= 0 || ((int64_t)dim * eb) % 16 != 0) return fail(PKM_EINVAL, "dim * sizeof(dtype) must be a positive multiple of 16");
+  // a row's 16-byte slices go to blocks of 256 lanes along the launch grid's y dimension (at most
+  // 65,536 blocks): 2^24 elements need at most 16,384
+  if (dim > (1 << 24)) return fail(PKM_EINVAL, "dim must be <= 2^24");
   if (n_rows < 1) return fail(PKM_EINVAL, "n_rows must be >= 1");
   if (n_bags < 0 || n_bags > ((int64_t)1 << 31) - 1) return fail(PKM_EINVAL, "n_bags must be in [0, 2^31)");
   if (bag_size < 1) return fail(PKM_EINVAL, "bag_size must be >= 1");

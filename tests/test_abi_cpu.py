@@ -153,6 +153,8 @@ def test_other_entry_points_reject_bad_arguments(P):
     assert eb(256, 10, 12, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL   # 12 bf16 = 24 bytes per row
     assert eb(256, 10, 16, 3, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL   # bad dtype
     assert eb(256, 0, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL    # no rows
+    assert eb(256, 10, (1 << 24) + 8, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL  # wider than 2^24
+    assert "2^24" in P.pkm_last_error()
     assert eb(256, 10, 16, 1, 256, 256, 4, 0, 256, None) == P.PKM_EINVAL   # empty bags
     assert eb(None, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL  # NULL table
     assert eb(8, 10, 16, 1, 256, 256, 4, 4, 256, None) == P.PKM_EINVAL     # misaligned table
