@@ -244,17 +244,21 @@ hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int width, 
 
 namespace pkm {
 
+// A grid of at most 2^20 blocks loops over the n elements (n can pass the 2^32 work-items of
+// one launch: T * d_value).
 __global__ void __launch_bounds__(256) convert_f32_kernel(const float* __restrict__ in, uint16_t* __restrict__ out,
                                                           int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = f32_to_bf16(in[i]);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = f32_to_bf16(in[i]);
 }
 
 // fp32 -> dtype (bf16 rounding, or a plain copy for fp32).
 hipError_t launch_convert_f32(const float* in, void* out, int64_t n, int dtype, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (dtype == DT_F32) return hipMemcpyAsync(out, in, (size_t)n * 4, hipMemcpyDeviceToDevice, s);
-  convert_f32_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(in, (uint16_t*)out, n);
+  const int64_t blocks = (n + 255) / 256;
+  convert_f32_kernel<<<dim3((unsigned)(blocks < ((int64_t)1 << 20) ? blocks : ((int64_t)1 << 20))), 256, 0, s>>>(
+      in, (uint16_t*)out, n);
   return hipGetLastError();
 }
 
