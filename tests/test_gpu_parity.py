@@ -261,6 +261,30 @@ def test_fp32_batch_with_more_token_tiles_than_a_grid_row():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
+def test_largest_accepted_batch_of_selection_rows():
+    """max_tokens * n_heads = 2^24, the most the boundary accepts: 2^22 tokens of 4 heads, so the
+    selection runs over 2^25 (token, head, half) rows (2^31 work-items in the one-wave-per-row
+    launches) and the combine over 2^24.  Narrow widths keep it small (54 GiB of workspace);
+    properties on every token, the oracle on the first and last scoring blocks and random tokens."""
+    T = 1 << 22
+    cfg = CONFIGS["pkm_1m_bf16"].with_(name="bf16_max_rows", T=T, d_model=32, H=4, d_q=8, n_sub=64, k=4, d_v=16)
+    say(f"bf16 T={T} H=4: 2^25 selection rows")
+    wl = _G().Workload(cfg)
+    o = run_debug(wl)
+    assert o["idx"].shape == (T, 4, 4)
+    assert (o["idx"] >= 0).all() and (o["idx"] < cfg.N).all()
+    np.testing.assert_allclose(o["w"].sum(axis=-1), 1.0, atol=1e-5)
+    check_order_valid(o["idx"], o["score"], "final lists (all tokens)")
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(512), np.arange(T - 512, T), rng.choice(T, 256, replace=False)]))
+    full_check(wl, o, rows=rows)
+    wl.close()
+    del wl, o
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,T", [("memplus_16m_bf16", 200), ("memplus_64m_bf16", 77),
                                     ("memplus_16m_bf16", 1), ("memplus_64m_bf16", 1)])
 def test_small_batches_split_the_sub_keys(name, T):
