@@ -22,6 +22,23 @@ from ._lib import (  # noqa: F401
 )
 
 
+def _check_tensor(name, t, shape, dtype, host_ok=False, device=True):
+    """A contiguous torch tensor of exactly `shape` and `dtype`, on a GPU (or, with host_ok, in
+    pinned host memory; device=False: any device); ValueError otherwise."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if device and not (t.is_cuda or (host_ok and t.is_pinned())):
+        raise ValueError(f"{name} must be on the GPU" + (" or in pinned host memory" if host_ok else ""))
+
+
 class ProductKeyMemory:
     """Owns a handle and its workspace (a torch uint8 tensor on the current device).
 
@@ -39,6 +56,18 @@ class ProductKeyMemory:
 
         self.cfg = make_config(d_model, n_heads, d_query, n_sub, k, d_value, dtype, qk_norm, memory_plus, max_tokens,
                                norm_eps)
+        self.dtype = {"f32": torch.float32, "bf16": torch.bfloat16}.get(dtype) or (
+            torch.bfloat16 if dtype == PKM_BF16 else torch.float32)
+        # the C ABI takes bare pointers: shapes, types and layouts are checked here, so that no
+        # kernel reads past the end of a tensor
+        want = [("W_q", W_q, (d_model, n_heads * d_query), False),
+                ("subkeys", subkeys, (n_heads, 2, n_sub, d_query // 2), False),
+                ("values", values, (n_sub * n_sub, d_value), True)]
+        if memory_plus:
+            want += [("W1", W1, (d_model, d_value), False), ("W2", W2, (d_value, d_model), False)]
+        for device in (False, True):  # every shape, type and layout first, then where they live
+            for name, t, shape, host_ok in want:
+                _check_tensor(name, t, shape, self.dtype, host_ok=host_ok, device=device)
         self.ws_bytes = pkm_workspace_size(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=W_q.device)
         self._keep = (W_q, subkeys, values, W1, W2)
@@ -51,9 +80,16 @@ class ProductKeyMemory:
     def forward(self, x, out=None, idx_out=None, w_out=None, stream=None):
         import torch
 
-        T = x.shape[0]
+        T = x.shape[0] if getattr(x, "dim", lambda: 0)() == 2 else -1
+        _check_tensor("x", x, (T, self.cfg.d_model), self.dtype)
         if out is None:
             out = torch.empty((T, self.out_width), dtype=x.dtype, device=x.device)
+        _check_tensor("out", out, (T, self.out_width), self.dtype)
+        sel = (T, self.cfg.n_heads, self.cfg.k)
+        if idx_out is not None:
+            _check_tensor("idx_out", idx_out, sel, torch.int32)
+        if w_out is not None:
+            _check_tensor("w_out", w_out, sel, torch.float32)
         pkm_forward(self.handle, x, T, out, idx_out, w_out, stream)
         return out
 

@@ -272,3 +272,31 @@ def test_bag_backward_argument_errors_before_any_device_call(P):
     hdr = open(os.path.join(ROOT, "include", "bag_backward.h")).read()
     m = re.search(r"#define PKM_BAG_BACKWARD_NOALLOC_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
     assert m and int(m.group(1)) << int(m.group(2)) == P.PKM_BAG_BACKWARD_NOALLOC_BYTES
+
+
+def test_python_class_checks_tensor_shapes_before_any_call(P):
+    """The C ABI takes bare pointers, so ProductKeyMemory checks every tensor's shape, type,
+    layout and device before a kernel could read past the end of one."""
+    import torch
+
+    bf = torch.bfloat16
+    good = dict(W_q=torch.zeros(64, 2 * 16, dtype=bf), subkeys=torch.zeros(2, 2, 8, 8, dtype=bf),
+                values=torch.zeros(64, 32, dtype=bf), W1=torch.zeros(64, 32, dtype=bf), W2=torch.zeros(32, 64, dtype=bf))
+    cfg = dict(d_model=64, n_heads=2, d_query=16, n_sub=8, k=4, d_value=32, dtype="bf16", qk_norm=1, memory_plus=1,
+               max_tokens=16)
+    cases = [("W_q", torch.zeros(64, 16, dtype=bf), "shape"),
+             ("subkeys", torch.zeros(2, 2, 8, 8, dtype=torch.float32), "dtype"),
+             ("values", torch.zeros(32, 64, dtype=bf).t(), "contiguous"),
+             ("W2", torch.zeros(32, 32, dtype=bf), "shape"),
+             ("W1", None, "torch tensor")]
+    for name, t, needle in cases:
+        kw = dict(good, **{name: t})
+        with pytest.raises(ValueError) as e:
+            P.ProductKeyMemory(**cfg, **kw)
+        assert name in str(e.value) and needle in str(e.value)
+    with pytest.raises(ValueError) as e:   # right shapes, but host memory that is not pinned
+        P.ProductKeyMemory(**cfg, **good)
+    assert "W_q must be on the GPU" in str(e.value)
+    from sparse_key_value_amd import _check_tensor
+    with pytest.raises(ValueError, match="x has shape"):
+        _check_tensor("x", torch.zeros(5, 32, dtype=bf), (5, 64), bf)

@@ -812,22 +812,25 @@ def test_largest_sub_key_lists():
     q = (rng.integers(-8, 9, size=(T, 1, 2, dh)) / 8.0).astype(np.float32)
     say(f"largest sub-key lists: n_sub={n}")
     wq = torch.zeros((64, 2 * dh), dtype=torch.float32, device="cuda")
-    vals = torch.zeros((16, 4), dtype=torch.float32, device="cuda")   # never read by pkm_select
-    pk = P.ProductKeyMemory(d_model=64, n_heads=1, d_query=2 * dh, n_sub=n, k=k, d_value=4, dtype="f32", qk_norm=0,
-                            memory_plus=0, max_tokens=T, W_q=wq, subkeys=torch.from_numpy(K).cuda(), values=vals)
+    # pkm_select never reads the value table: the handle is made through the C ABI over a small
+    # stand-in (ProductKeyMemory, made for forwards, insists on the whole 1.6e9-row table)
+    vals = torch.zeros((16, 4), dtype=torch.float32, device="cuda")
+    cfg = P.make_config(64, 1, 2 * dh, n, k, 4, "f32", 0, 0, T)
+    ws = torch.empty(P.pkm_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    handle = P.pkm_create(cfg, wq, torch.from_numpy(K).cuda(), vals, None, None, ws, ws.numel())
     hi_ = torch.empty((T, 1, 2, k), dtype=torch.int32, device="cuda")
     hs_ = torch.empty((T, 1, 2, k), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, 1, k), dtype=torch.int32, device="cuda")
     sc = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
     w = torch.empty((T, 1, k), dtype=torch.float32, device="cuda")
-    P.pkm_select(pk.handle, torch.from_numpy(q).cuda(), T, hi_, hs_, idx, sc, w)
+    P.pkm_select(handle, torch.from_numpy(q).cuda(), T, hi_, hs_, idx, sc, w)
     torch.cuda.synchronize()
     q64 = q.astype(np.float64).reshape(T, 1, 2 * dh)
     sel = O.select(q64[..., :dh], q64[..., dh:], K[:, 0].astype(np.float64), K[:, 1].astype(np.float64), k)
     np.testing.assert_array_equal(hi_.cpu().numpy(), sel["half_idx"])
     np.testing.assert_array_equal(idx.cpu().numpy(), sel["idx"])
     np.testing.assert_array_equal(sc.cpu().numpy(), sel["score"].astype(np.float32))
-    pk.close()
+    P.pkm_destroy(handle)
 
 
 @pytest.mark.parametrize("case", [
